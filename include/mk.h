@@ -1,0 +1,172 @@
+/*
+ * mk.h -- C ABI of the persistent-megakernel batch-1 decoder for AMD MI355X (gfx950).
+ *
+ * The library runs the autoregressive decode step of a Qwen3-style decoder (the
+ * talker of a streaming TTS model) as ONE persistent kernel that loops over decode
+ * steps inside the kernel, instead of launching one kernel per operation:
+ *   - dev.to, "Porting a 1,200-line persistent CUDA megakernel to Qwen3-TTS",
+ *     section "The idea: one kernel that never exits": a decode step is embedding
+ *     lookup, attention, MLP, norms and sampling; the persistent kernel owns the GPU
+ *     and loops over steps itself.
+ *   - same article, "Porting it to Qwen3-TTS-1.7B": untied embeddings (the LM head
+ *     reads its own matrix) and multi-section rotary embeddings.
+ *   - theaicatchup, "I made a single CUDA kernel speak", section "Why Does a Single
+ *     Kernel Even Matter for TTS?": the talker body equals Qwen3-0.6B; its inputs are
+ *     sums of 17 embeddings, handed over through a sentinel: an id >= 0 is a table
+ *     lookup, an id < 0 means "take the precomputed row".
+ *   - same article, "So, What's the Catch with These Megakernels?": rotary
+ *     frequency tables are built on the host.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named d_* are DEVICE pointers (e.g. from torch tensors on the GPU);
+ *     h_* are host pointers.  The library borrows them for the stream-ordered
+ *     duration of the call and never frees them.
+ *   - Matrices are row-major [out][in] (the HF layout).  bf16 tensors are raw
+ *     16-bit patterns; f32 tensors are IEEE float.
+ *   - Every call is asynchronous on the handle's stream unless stated otherwise.
+ *     Argument errors are detected on the host before anything is launched and
+ *     returned as a negative code; faults found on the device (an id outside the
+ *     vocabulary, a wait that timed out) are latched in a device error word and
+ *     reported by the next mk_status().
+ *   - A handle is bound to one device and one stream and is not thread-safe.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------- */
+#define MK_OK               0
+#define MK_ERR_ARG         -1   /* null pointer, bad size, bad cfg field            */
+#define MK_ERR_UNSUPPORTED -2   /* cfg is valid but no kernel body is built for it  */
+#define MK_ERR_OOM         -3   /* device or pinned allocation failed               */
+#define MK_ERR_CAPACITY    -4   /* position + n would exceed cfg.max_seq            */
+#define MK_ERR_COOP        -5   /* one workgroup per CU cannot be made co-resident  */
+#define MK_ERR_HIP         -6   /* a HIP runtime call failed                        */
+#define MK_ERR_DEVICE      -7   /* device error word: bad id or bad position        */
+#define MK_ERR_TIMEOUT     -8   /* device error word: a cross-workgroup wait timed out */
+#define MK_ERR_STATE       -9   /* call order: e.g. feedback decode with no previous id */
+
+/* ---- dtypes ----------------------------------------------------------------- */
+#define MK_F32  0
+#define MK_BF16 1
+
+/* Model configuration.  Body shapes with a compiled kernel:
+ *   hidden 256,  head_dim 64,  16/8 -> 4/2 heads, intermediate 768,  f32 weights  (tiny)
+ *   hidden 1024, head_dim 128, 16 q / 8 kv heads, intermediate 3072, bf16 weights (Qwen3-0.6B body)
+ *   hidden 2048, head_dim 128, 16 q / 8 kv heads, intermediate 6144, bf16 weights (1.7B-scale talker)
+ * n_layers, vocab (< 2^18), max_seq, tied, rms_eps, rope_theta and the rotary
+ * sections are free.  sections[0..n_sections) are counts of rotary PAIRS, contiguous
+ * from pair 0, summing to head_dim/2; section k turns with position stream k
+ * ({head_dim/2} with n_sections = 1 is ordinary RoPE). */
+typedef struct mk_cfg {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  int32_t tied;          /* 1: the LM head reads the input embedding matrix          */
+  int32_t weight_dtype;  /* MK_F32 | MK_BF16 (every weight tensor, gains included)   */
+  int32_t kv_dtype;      /* MK_F32 | MK_BF16: KV cache storage; bf16 rounds to nearest even */
+  float   rms_eps, rope_theta;
+  int32_t n_sections, sections[3];
+  int32_t max_seq;       /* KV capacity in positions                                 */
+} mk_cfg;
+
+/* Weights, all device pointers, HF layout.  Per-layer entries are HOST arrays of
+ * n_layers device pointers.  Shapes: embed [vocab][hidden]; lm_head [vocab][hidden]
+ * (NULL when tied); final_norm, in_norm, post_norm [hidden]; wq [n_q*d][hidden];
+ * wk, wv [n_kv*d][hidden]; q_norm, k_norm [d]; wo [hidden][n_q*d];
+ * w_gate, w_up [intermediate][hidden]; w_down [hidden][intermediate].
+ * mk_create copies everything into a library-owned arena; the caller may free its
+ * tensors once mk_create has returned (it synchronizes the stream). */
+typedef struct mk_weights {
+  const void *embed, *lm_head, *final_norm;
+  const void *const *in_norm, *const *wq, *const *wk, *const *wv, *const *q_norm, *const *k_norm,
+             *const *wo, *const *post_norm, *const *w_gate, *const *w_up, *const *w_down;
+} mk_weights;
+
+typedef struct mk_handle mk_handle;
+
+/* Validate cfg, allocate the arena, KV cache, exchange buffers and the pinned
+ * progress word, pack the weights, build the rotary cos/sin table (computed in
+ * double, stored as float) and check that one workgroup per CU fits co-resident.
+ * stream: a hipStream_t (NULL = the null stream).  Synchronous.
+ * Returns MK_OK and *out, or a negative code with *out = NULL. */
+int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** out);
+
+/* Run n prompt positions starting at the current position (0 after create/reset,
+ * n_pos after mk_load_kv) position by position through the same persistent kernel;
+ * the LM head runs only at the last one and its greedy id (ties: lowest index) is
+ * written to d_out_first[0] (device int32) and kept as the feedback id.
+ *   d_ids  [n] int32: >= 0 reads embed[id]; < 0 reads row t of d_rows.
+ *   d_rows [n][hidden] float32, may be NULL when no id is negative.
+ *   d_pos3 [n][3] int32 rotary position streams, or NULL: every stream = position.
+ * MK_ERR_CAPACITY if position + n > max_seq. */
+int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
+               int32_t n, int32_t* d_out_first);
+
+/* The hot path: n_steps decode steps in ONE launch.  Step s runs at position
+ * position+s and reads
+ *   d_ids == NULL : the id picked by the previous step (step 0: by the last prefill
+ *                   or decode call; MK_ERR_STATE if there is none);
+ *   d_ids[s] >= 0 : embed[d_ids[s]];
+ *   d_ids[s] <  0 : row s of d_embed_buf ([n_steps][hidden] float32).
+ * d_pos3 as in mk_prefill.  d_out_ids [n_steps] int32 receives the greedy ids
+ * (ties: lowest index).  The pinned progress word advances after every step. */
+int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
+              const int32_t* d_pos3, int32_t* d_out_ids);
+
+/* Install n_pos already-rotated cache positions and set the position to n_pos.
+ * d_kv: device [n_layers][2][n_kv][n_pos][head_dim] in cfg.kv_dtype (K then V). */
+int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos);
+
+/* Rewind to position 0 and forget the feedback id (the cache is not cleared: it is
+ * only read at positions that have been written since). */
+int mk_reset(mk_handle* h);
+
+/* Current position (positions written so far).  Host only, no sync. */
+int mk_position(mk_handle* h, int32_t* pos);
+
+/* Debug outputs of the following prefill/decode calls (NULL turns each off):
+ *   d_hidden [n][n_layers+1][hidden] float32: the residual stream entering layer 0
+ *            and leaving every layer, for each position the call runs;
+ *   d_trace  [n][grid][2] uint64: per position and workgroup, the 100 MHz ticks spent
+ *            waiting for other workgroups and the ticks of the whole position. */
+int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
+
+/* Ids published so far by the most recently enqueued prefill/decode call (0 until
+ * its first id), read from pinned host memory without synchronizing: the basis of
+ * time-to-first-chunk.  A prefill publishes one id. */
+int mk_progress(mk_handle* h, int64_t* steps_done);
+
+/* Synchronize the stream and report the device error word (MK_OK when clean).
+ * The word is cleared by the read. */
+int mk_status(mk_handle* h);
+
+/* Number of workgroups of the persistent grid (one per CU). */
+int mk_grid_size(mk_handle* h, int32_t* n);
+
+/* Talker input rows on the device: row t = sum over c of codebooks[c][ids[t][c]]
+ * (c = 0..n_codebooks-1) plus text[ids[t][n_codebooks]], widened to float32 and
+ * added one row at a time in that order (the theaicatchup article, "Why Does a
+ * Single Kernel Even Matter for TTS?": inputs are sums of 16 codebook embeddings
+ * and a text embedding).
+ *   d_codebooks [n_codebooks][codebook_size][hidden], d_text [text_vocab][hidden],
+ *   both in dtype (MK_F32 | MK_BF16); d_ids [n][n_codebooks+1] int32;
+ *   d_rows [n][hidden] float32 (output).  An id outside its table reads row 0 of
+ *   that table and adds one to d_bad[0] (device int32) when d_bad is not NULL.
+ *   Stream-ordered on `stream` (a hipStream_t, NULL = null stream). */
+int mk_embed_sum(const void* d_codebooks, int32_t n_codebooks, int32_t codebook_size,
+                 const void* d_text, int32_t text_vocab, int32_t hidden, int32_t dtype,
+                 const int32_t* d_ids, int32_t n, float* d_rows, int32_t* d_bad, void* stream);
+
+const char* mk_strerror(int code);
+
+/* Free everything the handle owns.  Synchronizes its stream.  NULL is a no-op. */
+void mk_destroy(mk_handle* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

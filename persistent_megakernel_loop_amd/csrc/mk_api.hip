@@ -1,0 +1,480 @@
+// Host side of the C ABI declared in include/mk.h: validation, the weight arena,
+// the KV cache, exchange buffers, the rotary table and the launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mk.h"
+#include "mk_internal.h"
+
+using mk::LayerLayout;
+using mk::Params;
+
+struct mk_handle {
+  int body = -1;
+  mk_cfg cfg{};
+  hipStream_t stream = nullptr;
+  int device = 0;
+  int wb = 2;  // bytes per weight
+  int kvb = 2; // bytes per cache entry
+  // arena
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0;
+  LayerLayout lay{};
+  uint8_t* embed = nullptr;
+  uint8_t* lm_head = nullptr;
+  float* final_norm = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  // cache and exchange
+  void* kcache = nullptr;
+  void* vcache = nullptr;
+  unsigned long long* xbuf = nullptr;
+  size_t xbuf_words = 0;
+  unsigned long long *xq, *xatt, *xop, *xxa, *xm, *xdp, *xxb, *xarg;
+  uint32_t* ctl = nullptr;  // [0] err, [1] abort, [2] last id
+  // pinned
+  unsigned long long* progress = nullptr;
+  int32_t* pinned_ids = nullptr;
+  int32_t pinned_cap = 0;
+  // state
+  int32_t pos = 0;
+  bool have_last = false;
+  uint32_t tag = 1;
+  uint32_t lm_seq = 1;
+  uint32_t call_seq = 0;
+  float* dbg_hidden = nullptr;
+  unsigned long long* dbg_trace = nullptr;
+};
+
+namespace {
+
+struct BodyShape { int body, H, D, NQ, NKV, I, wdt; };
+const BodyShape kBodies[] = {
+    {mk::BODY_TINY, 256, 64, 4, 2, 768, MK_F32},
+    {mk::BODY_Q06, 1024, 128, 16, 8, 3072, MK_BF16},
+    {mk::BODY_Q17, 2048, 128, 16, 8, 6144, MK_BF16},
+};
+
+#define HIPCK(x)                          \
+  do {                                    \
+    if ((x) != hipSuccess) return MK_ERR_HIP; \
+  } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int validate_cfg(const mk_cfg* c) {
+  if (!c) return MK_ERR_ARG;
+  if (c->n_layers <= 0 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0 || c->vocab <= 0 || c->max_seq <= 0)
+    return MK_ERR_ARG;
+  if (c->n_q_heads % c->n_kv_heads) return MK_ERR_ARG;
+  if (c->head_dim % 2) return MK_ERR_ARG;
+  if (c->weight_dtype != MK_F32 && c->weight_dtype != MK_BF16) return MK_ERR_ARG;
+  if (c->kv_dtype != MK_F32 && c->kv_dtype != MK_BF16) return MK_ERR_ARG;
+  if (c->n_sections < 1 || c->n_sections > 3) return MK_ERR_ARG;
+  int sum = 0;
+  for (int k = 0; k < c->n_sections; ++k) {
+    if (c->sections[k] <= 0) return MK_ERR_ARG;
+    sum += c->sections[k];
+  }
+  if (sum != c->head_dim / 2) return MK_ERR_ARG;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return MK_ERR_ARG;
+  if (c->vocab >= (1 << 18)) return MK_ERR_UNSUPPORTED;
+  if ((long long)c->max_seq * c->n_layers * c->n_kv_heads * c->head_dim > (1ll << 40)) return MK_ERR_ARG;
+  return MK_OK;
+}
+
+int pick_body(const mk_cfg* c) {
+  for (const auto& b : kBodies)
+    if (b.H == c->hidden && b.D == c->head_dim && b.NQ == c->n_q_heads && b.NKV == c->n_kv_heads &&
+        b.I == c->intermediate && b.wdt == c->weight_dtype)
+      return b.body;
+  return -1;
+}
+
+// Layer layout of the packed arena (see the kernel's tile addressing).
+LayerLayout make_layout(const mk_cfg* c, int wb) {
+  const size_t H = c->hidden, D = c->head_dim, I = c->intermediate;
+  const size_t NG = c->n_kv_heads, QPG = c->n_q_heads / c->n_kv_heads;
+  const size_t RQKV = (QPG + 2) * D, OC = QPG * D, IX = I / mk::kXcds;
+  LayerLayout L{};
+  L.qkv = 0;
+  L.o = align_up(L.qkv + NG * RQKV * H * wb, 256);
+  L.gu = align_up(L.o + NG * H * OC * wb, 256);
+  L.down = align_up(L.gu + mk::kXcds * 2 * IX * H * wb, 256);
+  L.in_norm = align_up(L.down + mk::kXcds * H * IX * wb, 256);
+  L.post_norm = align_up(L.in_norm + H * 4, 256);
+  L.q_norm = align_up(L.post_norm + H * 4, 256);
+  L.k_norm = align_up(L.q_norm + D * 4, 256);
+  L.stride = align_up(L.k_norm + D * 4, 4096);
+  return L;
+}
+
+int copy2d(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height, hipStream_t s) {
+  return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToDevice, s) == hipSuccess ? MK_OK
+                                                                                                            : MK_ERR_HIP;
+}
+
+// Pack one layer's weights into the arena tiles the kernel reads.
+int pack_layer(mk_handle* h, const mk_weights* w, int l) {
+  const mk_cfg* c = &h->cfg;
+  const size_t H = c->hidden, D = c->head_dim, I = c->intermediate, wb = h->wb;
+  const size_t NG = c->n_kv_heads, QPG = c->n_q_heads / c->n_kv_heads;
+  const size_t RQKV = (QPG + 2) * D, OC = QPG * D, IX = I / mk::kXcds;
+  const size_t HALF = IX / mk::kPerXcd;
+  uint8_t* base = h->arena + (size_t)l * h->lay.stride;
+  hipStream_t s = h->stream;
+  const uint8_t* wq = (const uint8_t*)w->wq[l];
+  const uint8_t* wk = (const uint8_t*)w->wk[l];
+  const uint8_t* wv = (const uint8_t*)w->wv[l];
+  const uint8_t* wo = (const uint8_t*)w->wo[l];
+  const uint8_t* wg = (const uint8_t*)w->w_gate[l];
+  const uint8_t* wu = (const uint8_t*)w->w_up[l];
+  const uint8_t* wd = (const uint8_t*)w->w_down[l];
+  const size_t row = H * wb;
+  for (size_t g = 0; g < NG; ++g) {
+    uint8_t* q = base + h->lay.qkv + g * RQKV * row;
+    HIPCK(hipMemcpyAsync(q, wq + g * QPG * D * row, QPG * D * row, hipMemcpyDeviceToDevice, s));
+    HIPCK(hipMemcpyAsync(q + QPG * D * row, wk + g * D * row, D * row, hipMemcpyDeviceToDevice, s));
+    HIPCK(hipMemcpyAsync(q + (QPG + 1) * D * row, wv + g * D * row, D * row, hipMemcpyDeviceToDevice, s));
+    // O columns of the group's heads: [H][OC]
+    int e = copy2d(base + h->lay.o + g * H * OC * wb, OC * wb, wo + g * OC * wb, (size_t)c->n_q_heads * D * wb,
+                   OC * wb, H, s);
+    if (e) return e;
+  }
+  for (size_t x = 0; x < (size_t)mk::kXcds; ++x) {
+    // workgroup r of XCD x: [HALF gate rows][HALF up rows], rows x*IX + r*HALF ...
+    uint8_t* gu = base + h->lay.gu + x * 2 * IX * row;
+    int e = copy2d(gu, 2 * HALF * row, wg + x * IX * row, HALF * row, HALF * row, mk::kPerXcd, s);
+    if (e) return e;
+    e = copy2d(gu + HALF * row, 2 * HALF * row, wu + x * IX * row, HALF * row, HALF * row, mk::kPerXcd, s);
+    if (e) return e;
+    // down columns of the slice: [H][IX]
+    e = copy2d(base + h->lay.down + x * H * IX * wb, IX * wb, wd + x * IX * wb, I * wb, IX * wb, H, s);
+    if (e) return e;
+  }
+  const int bf = c->weight_dtype == MK_BF16;
+  if (mk::launch_widen(w->in_norm[l], (float*)(base + h->lay.in_norm), (int)H, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(w->post_norm[l], (float*)(base + h->lay.post_norm), (int)H, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(w->q_norm[l], (float*)(base + h->lay.q_norm), (int)D, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(w->k_norm[l], (float*)(base + h->lay.k_norm), (int)D, bf, s)) return MK_ERR_HIP;
+  return MK_OK;
+}
+
+void free_handle(mk_handle* h) {
+  if (!h) return;
+  hipStreamSynchronize(h->stream);
+  hipFree(h->arena);
+  hipFree(h->kcache);
+  hipFree(h->vcache);
+  hipFree(h->xbuf);
+  hipFree(h->ctl);
+  if (h->progress) hipHostFree(h->progress);
+  if (h->pinned_ids) hipHostFree(h->pinned_ids);
+  delete h;
+}
+
+int device_status(mk_handle* h, bool clear) {
+  uint32_t ctl[2];
+  HIPCK(hipStreamSynchronize(h->stream));
+  HIPCK(hipMemcpy(ctl, h->ctl, sizeof ctl, hipMemcpyDeviceToHost));
+  if (clear && (ctl[0] || ctl[1])) {
+    uint32_t z[2] = {0, 0};
+    HIPCK(hipMemcpy(h->ctl, z, sizeof z, hipMemcpyHostToDevice));
+  }
+  if (ctl[0] & mk::DEV_ERR_TIMEOUT) return MK_ERR_TIMEOUT;
+  if (ctl[0]) return MK_ERR_DEVICE;
+  if (ctl[1]) return MK_ERR_TIMEOUT;
+  return MK_OK;
+}
+
+int ensure_pinned(mk_handle* h, int32_t n) {
+  if (n <= h->pinned_cap) return MK_OK;
+  HIPCK(hipStreamSynchronize(h->stream));
+  if (h->pinned_ids) hipHostFree(h->pinned_ids);
+  h->pinned_ids = nullptr;
+  h->pinned_cap = 0;
+  if (hipHostMalloc((void**)&h->pinned_ids, sizeof(int32_t) * (size_t)n, hipHostMallocCoherent) != hipSuccess)
+    return MK_ERR_OOM;
+  h->pinned_cap = n;
+  return MK_OK;
+}
+
+int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const int32_t* pos3, int32_t* out,
+        int logits_from, int feedback) {
+  if (n <= 0) return MK_ERR_ARG;
+  if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
+  if (feedback && !h->have_last) return MK_ERR_STATE;
+  int e = ensure_pinned(h, n - logits_from);
+  if (e) return e;
+  Params P{};
+  P.layers = h->arena;
+  P.lay = h->lay;
+  P.embed = h->embed;
+  P.lm_head = h->lm_head;
+  P.final_norm = h->final_norm;
+  P.rope_cos = h->rope_cos;
+  P.rope_sin = h->rope_sin;
+  P.rope_positions = h->cfg.max_seq;
+  P.n_layers = h->cfg.n_layers;
+  P.vocab = h->cfg.vocab;
+  P.max_seq = h->cfg.max_seq;
+  P.n_sections = h->cfg.n_sections;
+  P.sec_end0 = h->cfg.sections[0];
+  P.sec_end1 = h->cfg.n_sections > 1 ? h->cfg.sections[0] + h->cfg.sections[1] : h->cfg.head_dim;
+  if (h->cfg.n_sections == 1) P.sec_end0 = h->cfg.head_dim;  // every pair reads stream 0
+  P.rms_eps = h->cfg.rms_eps;
+  P.kcache = h->kcache;
+  P.vcache = h->vcache;
+  P.kv_bf16 = h->cfg.kv_dtype == MK_BF16;
+  P.xq = h->xq; P.xatt = h->xatt; P.xop = h->xop; P.xxa = h->xxa;
+  P.xm = h->xm; P.xdp = h->xdp; P.xxb = h->xxb; P.xarg = h->xarg;
+  P.err = h->ctl;
+  P.abort_flag = h->ctl + 1;
+  P.last_id = (int32_t*)(h->ctl + 2);
+  P.n_pos = n;
+  P.pos0 = h->pos;
+  P.logits_from = logits_from;
+  P.feedback = feedback;
+  P.ids = ids;
+  P.rows = rows;
+  P.pos3 = pos3;
+  P.out_ids = out;
+  P.pinned_ids = h->pinned_ids;
+  h->call_seq += 1;
+  P.call_seq = h->call_seq;
+  P.progress = h->progress;
+  P.dbg_hidden = h->dbg_hidden;
+  P.dbg_trace = h->dbg_trace;
+  // tags are compared for equality: before they wrap, clear the buffers so that no old word can match
+  const uint32_t need = (uint32_t)n * mk::tags_per_position(h->cfg.n_layers);
+  if ((unsigned long long)h->tag + need >= 0xFFFFFFF0ull) {
+    if (hipMemsetAsync(h->xbuf, 0, h->xbuf_words * 8, h->stream) != hipSuccess) return MK_ERR_HIP;
+    h->tag = 1;
+  }
+  P.tag0 = h->tag;
+  P.lm_seq0 = h->lm_seq;
+  P.spin_limit = 1u << 22;
+  if (mk::launch_decode(h->body, P, h->stream)) return MK_ERR_HIP;
+  h->tag += need;
+  h->lm_seq = (h->lm_seq + (uint32_t)(n - logits_from)) & 0x3fffu;
+  h->pos += n;
+  h->have_last = true;
+  return MK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** out) {
+  if (!out) return MK_ERR_ARG;
+  *out = nullptr;
+  if (!w) return MK_ERR_ARG;
+  int e = validate_cfg(cfg);
+  if (e) return e;
+  const int L = cfg->n_layers;
+  if (!w->embed || !w->final_norm || (!cfg->tied && !w->lm_head)) return MK_ERR_ARG;
+  const void* const* arrs[] = {w->in_norm, w->wq, w->wk, w->wv, w->q_norm, w->k_norm, w->wo, w->post_norm,
+                               w->w_gate, w->w_up, w->w_down};
+  for (auto a : arrs) {
+    if (!a) return MK_ERR_ARG;
+    for (int l = 0; l < L; ++l)
+      if (!a[l]) return MK_ERR_ARG;
+  }
+  const int body = pick_body(cfg);
+  if (body < 0) return MK_ERR_UNSUPPORTED;
+  int blocks = 0;
+  if (mk::coop_ok(body, &blocks)) return MK_ERR_HIP;
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_ERR_OOM;
+  h->body = body;
+  h->cfg = *cfg;
+  h->stream = (hipStream_t)stream;
+  h->wb = cfg->weight_dtype == MK_BF16 ? 2 : 4;
+  h->kvb = cfg->kv_dtype == MK_BF16 ? 2 : 4;
+  hipGetDevice(&h->device);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) { free_handle(h); return MK_ERR_HIP; }
+  if (prop.multiProcessorCount != mk::kGrid || blocks < 1 || !prop.cooperativeLaunch) { free_handle(h); return MK_ERR_COOP; }
+
+  const size_t H = cfg->hidden, D = cfg->head_dim, V = cfg->vocab;
+  h->lay = make_layout(cfg, h->wb);
+  size_t off = (size_t)L * h->lay.stride;
+  const size_t embed_off = off;
+  off = align_up(off + V * H * h->wb, 4096);
+  size_t lm_off = embed_off;
+  if (!cfg->tied) { lm_off = off; off = align_up(off + V * H * h->wb, 4096); }
+  const size_t fn_off = off;
+  off = align_up(off + H * 4, 256);
+  const size_t rope_off = off;
+  const size_t rope_n = (size_t)cfg->max_seq * (D / 2);
+  off = align_up(off + 2 * rope_n * 4, 256);
+  h->arena_bytes = off;
+  if (hipMalloc((void**)&h->arena, h->arena_bytes) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
+  h->embed = h->arena + embed_off;
+  h->lm_head = h->arena + lm_off;
+  h->final_norm = (float*)(h->arena + fn_off);
+  h->rope_cos = (float*)(h->arena + rope_off);
+  h->rope_sin = h->rope_cos + rope_n;
+
+  const size_t kv_bytes = (size_t)L * cfg->n_kv_heads * cfg->max_seq * D * h->kvb;
+  if (hipMalloc(&h->kcache, kv_bytes) != hipSuccess || hipMalloc(&h->vcache, kv_bytes) != hipSuccess) {
+    free_handle(h);
+    return MK_ERR_OOM;
+  }
+  // exchange buffers
+  const size_t QPG = cfg->n_q_heads / cfg->n_kv_heads, IX = cfg->intermediate / mk::kXcds;
+  const size_t nq = 8 * (QPG + 2) * D, natt = 8 * mk::kPerXcd * QPG * (D + 2), nh = 8 * H, nm = 8 * IX;
+  h->xbuf_words = nq + natt + 5 * nh + nm + mk::kGrid + 64 * 8;
+  if (hipMalloc((void**)&h->xbuf, h->xbuf_words * 8) != hipSuccess ||
+      hipMalloc((void**)&h->ctl, 256) != hipSuccess) {
+    free_handle(h);
+    return MK_ERR_OOM;
+  }
+  unsigned long long* p = h->xbuf;
+  auto take = [&](size_t n) { unsigned long long* r = p; p += align_up(n, 64); return r; };
+  h->xq = take(nq); h->xatt = take(natt); h->xop = take(nh); h->xxa = take(nh); h->xm = take(nm);
+  h->xdp = take(nh); h->xxb = take(nh); h->xarg = take(mk::kGrid);
+  if ((size_t)(p - h->xbuf) > h->xbuf_words) { free_handle(h); return MK_ERR_ARG; }
+  if (hipHostMalloc((void**)&h->progress, 64, hipHostMallocCoherent) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
+  *(volatile unsigned long long*)h->progress = 0;
+
+  hipStream_t s = h->stream;
+  if (hipMemsetAsync(h->xbuf, 0, h->xbuf_words * 8, s) != hipSuccess || hipMemsetAsync(h->ctl, 0, 256, s) != hipSuccess) {
+    free_handle(h);
+    return MK_ERR_HIP;
+  }
+  for (int l = 0; l < L; ++l) {
+    e = pack_layer(h, w, l);
+    if (e) { free_handle(h); return e; }
+  }
+  if (hipMemcpyAsync(h->embed, w->embed, V * H * h->wb, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      (!cfg->tied && hipMemcpyAsync(h->lm_head, w->lm_head, V * H * h->wb, hipMemcpyDeviceToDevice, s) != hipSuccess) ||
+      mk::launch_widen(w->final_norm, h->final_norm, (int)H, cfg->weight_dtype == MK_BF16, s)) {
+    free_handle(h);
+    return MK_ERR_HIP;
+  }
+  // rotary table: cos/sin of pos * theta^(-2i/d), computed in double, stored as float
+  std::vector<float> tab(2 * rope_n);
+  for (size_t ps = 0; ps < (size_t)cfg->max_seq; ++ps)
+    for (size_t i = 0; i < D / 2; ++i) {
+      const double ang = (double)ps * std::pow((double)cfg->rope_theta, -2.0 * (double)i / (double)D);
+      tab[ps * (D / 2) + i] = (float)std::cos(ang);
+      tab[rope_n + ps * (D / 2) + i] = (float)std::sin(ang);
+    }
+  if (hipMemcpyAsync(h->rope_cos, tab.data(), tab.size() * 4, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    free_handle(h);
+    return MK_ERR_HIP;
+  }
+  *out = h;
+  return MK_OK;
+}
+
+int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3, int32_t n,
+               int32_t* d_out_first) {
+  if (!h || !d_ids || n <= 0) return MK_ERR_ARG;
+  return run(h, n, d_ids, d_rows, d_pos3, d_out_first, n - 1, 0);
+}
+
+int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf, const int32_t* d_pos3,
+              int32_t* d_out_ids) {
+  if (!h || n_steps <= 0 || !d_out_ids) return MK_ERR_ARG;
+  return run(h, n_steps, d_ids, d_embed_buf, d_pos3, d_out_ids, 0, d_ids == nullptr);
+}
+
+int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos) {
+  if (!h || !d_kv || n_pos < 0) return MK_ERR_ARG;
+  if (n_pos > h->cfg.max_seq) return MK_ERR_CAPACITY;
+  const size_t D = h->cfg.head_dim, NKV = h->cfg.n_kv_heads, row = D * h->kvb;
+  const uint8_t* src = (const uint8_t*)d_kv;
+  for (int l = 0; l < h->cfg.n_layers; ++l)
+    for (int kv = 0; kv < 2; ++kv) {
+      // source [l][kv][g][n_pos][D] -> cache [l][g][max_seq][D]; one 2D copy per (l, kv)
+      uint8_t* dst = (uint8_t*)(kv ? h->vcache : h->kcache) + (size_t)l * NKV * h->cfg.max_seq * row;
+      const uint8_t* s0 = src + (((size_t)l * 2 + kv) * NKV) * n_pos * row;
+      if (n_pos && copy2d(dst, (size_t)h->cfg.max_seq * row, s0, (size_t)n_pos * row, (size_t)n_pos * row, NKV,
+                          h->stream))
+        return MK_ERR_HIP;
+    }
+  h->pos = n_pos;
+  h->have_last = false;
+  return MK_OK;
+}
+
+int mk_reset(mk_handle* h) {
+  if (!h) return MK_ERR_ARG;
+  h->pos = 0;
+  h->have_last = false;
+  return MK_OK;
+}
+
+int mk_position(mk_handle* h, int32_t* pos) {
+  if (!h || !pos) return MK_ERR_ARG;
+  *pos = h->pos;
+  return MK_OK;
+}
+
+int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace) {
+  if (!h) return MK_ERR_ARG;
+  h->dbg_hidden = d_hidden;
+  h->dbg_trace = (unsigned long long*)d_trace;
+  return MK_OK;
+}
+
+int mk_progress(mk_handle* h, int64_t* steps_done) {
+  if (!h || !steps_done) return MK_ERR_ARG;
+  const unsigned long long v = *(volatile unsigned long long*)h->progress;
+  *steps_done = (uint32_t)(v >> 32) == h->call_seq ? (int64_t)(v & 0xffffffffu) : 0;
+  return MK_OK;
+}
+
+int mk_status(mk_handle* h) {
+  if (!h) return MK_ERR_ARG;
+  return device_status(h, true);
+}
+
+int mk_grid_size(mk_handle* h, int32_t* n) {
+  if (!h || !n) return MK_ERR_ARG;
+  *n = mk::kGrid;
+  return MK_OK;
+}
+
+int mk_embed_sum(const void* d_codebooks, int32_t n_codebooks, int32_t codebook_size, const void* d_text,
+                 int32_t text_vocab, int32_t hidden, int32_t dtype, const int32_t* d_ids, int32_t n, float* d_rows,
+                 int32_t* d_bad, void* stream) {
+  if (!d_codebooks || !d_text || !d_ids || !d_rows || n < 0 || n_codebooks <= 0 || codebook_size <= 0 ||
+      text_vocab <= 0 || hidden <= 0 || (dtype != MK_F32 && dtype != MK_BF16))
+    return MK_ERR_ARG;
+  return mk::launch_embed_sum(d_codebooks, n_codebooks, codebook_size, d_text, text_vocab, hidden,
+                              dtype == MK_BF16, d_ids, n, d_rows, d_bad, stream)
+             ? MK_ERR_HIP
+             : MK_OK;
+}
+
+const char* mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_ERR_ARG: return "invalid argument";
+    case MK_ERR_UNSUPPORTED: return "configuration has no compiled kernel body";
+    case MK_ERR_OOM: return "out of memory";
+    case MK_ERR_CAPACITY: return "KV cache capacity exceeded";
+    case MK_ERR_COOP: return "one workgroup per CU cannot be co-resident";
+    case MK_ERR_HIP: return "HIP runtime error";
+    case MK_ERR_DEVICE: return "device reported a bad id or position";
+    case MK_ERR_TIMEOUT: return "device wait timed out";
+    case MK_ERR_STATE: return "no previous id for feedback decode";
+  }
+  return "unknown error";
+}
+
+void mk_destroy(mk_handle* h) { free_handle(h); }
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+// Internal declarations shared by the host library and the persistent kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mk {
+
+// Grid geometry: one workgroup per CU, 8 XCDs of 32 CUs on MI355X.  Workgroups are
+// dispatched round-robin over the XCDs, so workgroup b runs on XCD b % 8 and is
+// rank b / 8 inside it.  Correctness never depends on that placement (all
+// cross-workgroup traffic is device-coherent); only locality does.
+constexpr int kXcds = 8;
+constexpr int kPerXcd = 32;
+constexpr int kGrid = kXcds * kPerXcd;
+constexpr int kWorkerWaves = 8;              // stream weights and do the dot products
+constexpr int kThreads = (kWorkerWaves + 1) * 64;  // + one control wave (polls, exchanges)
+constexpr int kLdsBytes = 96 * 1024;         // > half of the 160 KB LDS: one workgroup per CU
+
+enum BodyId : int { BODY_TINY = 0, BODY_Q06 = 1, BODY_Q17 = 2 };
+
+// Device error word values (bit flags).
+enum : uint32_t { DEV_ERR_ID = 1u, DEV_ERR_POS = 2u, DEV_ERR_TIMEOUT = 4u };
+
+// Offsets (bytes) of one layer's tensors inside the arena; every layer has the same layout.
+struct LayerLayout {
+  size_t qkv, o, gu, down;            // packed weight tiles (weight dtype)
+  size_t in_norm, post_norm, q_norm, k_norm;   // float32 gains
+  size_t stride;                       // bytes per layer
+};
+
+struct Params {
+  // weights
+  const uint8_t* layers;     // arena base of layer 0
+  LayerLayout lay;
+  const void* embed;         // [V][H] weight dtype
+  const void* lm_head;       // [V][H] weight dtype (== embed when tied)
+  const float* final_norm;   // [H]
+  const float* rope_cos;     // [rope_positions][D/2]
+  const float* rope_sin;
+  int32_t rope_positions;
+  // shape (runtime part)
+  int32_t n_layers, vocab, max_seq;
+  int32_t n_sections, sec_end0, sec_end1;  // pair i < sec_end0 -> stream 0, < sec_end1 -> 1, else 2
+  float rms_eps;
+  // KV cache [L][NKV][max_seq][D] for K and for V, kv dtype
+  void* kcache;
+  void* vcache;
+  int32_t kv_bf16;
+  // exchange buffers (64-bit tagged words, zero-initialised)
+  unsigned long long* xq;    // [8][QKV rows per XCD]          local hop
+  unsigned long long* xatt;  // [8][32][QPG][D+2]               local hop
+  unsigned long long* xop;   // [32][NG][H/32] O partials, by reader      cross hop
+  unsigned long long* xxa;   // [8][H] residual after attention local hop
+  unsigned long long* xm;    // [8][I/8]                         local hop
+  unsigned long long* xdp;   // [32][8][H/32] down partials, by reader    cross hop
+  unsigned long long* xxb;   // [8][H] residual after the MLP    local hop
+  unsigned long long* xarg;  // [grid] argmax keys               cross hop
+  uint32_t* err;             // device error word
+  uint32_t* abort_flag;      // set on timeout: every wait gives up
+  int32_t* last_id;          // feedback id carried between launches
+  // this launch
+  int32_t n_pos;             // positions to run
+  int32_t pos0;              // first position
+  int32_t logits_from;       // run the LM head for t >= logits_from (decode: 0; prefill: n-1)
+  int32_t feedback;          // 1: input id of step t>0 is the argmax of step t-1; step 0 reads *last_id
+  const int32_t* ids;        // [n_pos] or NULL (feedback)
+  const float* rows;         // [n_pos][H] or NULL
+  const int32_t* pos3;       // [n_pos][3] or NULL
+  int32_t* out_ids;          // [n_pos - logits_from] or NULL
+  int32_t* pinned_ids;       // host-pinned mirror of out_ids, or NULL
+  unsigned long long* progress;  // host-pinned step counter
+  float* dbg_hidden;         // [n_pos][L+1][H] or NULL
+  unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL
+  uint32_t tag0;             // first exchange tag of this launch
+  uint32_t lm_seq0;          // argmax key sequence of the first LM head of this launch (14 bits used)
+  uint32_t call_seq;         // high half of the progress word
+  uint32_t spin_limit;       // polls before a wait gives up
+};
+
+// Tags used by one position: kPhasesPerLayer per layer plus one for the LM head.
+constexpr uint32_t kPhasesPerLayer = 8;
+__host__ __device__ inline uint32_t tags_per_position(int n_layers) { return (uint32_t)n_layers * kPhasesPerLayer + 2; }
+
+// Host-side launcher implemented next to the kernel.
+int launch_decode(int body, const Params& p, void* stream);
+int coop_ok(int body, int* blocks_per_cu);
+int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* text, int text_vocab,
+                     int hidden, int bf16, const int32_t* ids, int n, float* rows, int32_t* bad, void* stream);
+int launch_widen(const void* src, float* dst, int n, int bf16, void* stream);
+
+}  // namespace mk

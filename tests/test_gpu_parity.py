@@ -1,0 +1,86 @@
+"""GPU parity: the HIP decode path (through the C ABI) against the oracle.
+
+Small cases span several tiles and a ragged vocabulary tail and run the oracle
+over every position; full-size cases run the launch configuration the
+benchmark times (one workgroup per CU, the whole prompt and a block of decode
+steps in single launches) and compare every position the oracle replays.
+"""
+import numpy as np
+import pytest
+
+from persistent_megakernel_loop_amd import workload as wl
+from tests.parity import compare, make_inputs, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=None, random_gains=False):
+    from persistent_megakernel_loop_amd.binding import weights_to_device
+
+    print(f"[case] {shape.name} L={shape.n_layers} V={shape.vocab} steps={n_steps} prompt={prompt_len} "
+          f"kv={kv_prefill}", flush=True)
+    weights = wl.make_weights(shape, random_gains=random_gains)
+    inp = make_inputs(shape, n_steps=n_steps, prompt_len=prompt_len, kv_prefill=kv_prefill)
+    dw = weights_to_device(weights)
+    gpu = run_gpu(shape, dw, inp)
+    del dw
+    orc = run_oracle(shape, weights, inp, gpu, steps=steps_checked)
+    summary = compare(gpu, orc)
+    print(f"[case] {shape.name}: {summary}", flush=True)
+    return gpu, summary
+
+
+def test_tiny_fp32_full_run():
+    """The tiny fp32 decoder: 8 prompt ids, 32 greedy steps."""
+    _case(wl.TINY)
+
+
+def test_tiny_random_gains_ragged_vocab():
+    shape = wl.TINY.replace(name="tiny-97", vocab=97)
+    _case(shape, n_steps=12, random_gains=True)
+
+
+def test_q06_text_two_layers_ragged_vocab():
+    shape = wl.TEXT_0P6B.replace(name="q06-2l-v1000", n_layers=2, vocab=1000, prompt_len=16, steps=24)
+    _case(shape)
+
+
+def test_q06_talker_two_layers():
+    shape = wl.TALKER_0P6B.replace(name="talker-2l", n_layers=2, prompt_len=32, steps=16)
+    _case(shape)
+
+
+def test_q06_talker_long_chunks_two_layers():
+    """Positions past 1024 use all 32 attention chunks of an XCD."""
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-kv1100", n_layers=2, kv_prefill=1100, prompt_len=0, steps=8)
+    _case(shape)
+
+
+def test_determinism_bitwise():
+    from persistent_megakernel_loop_amd.binding import weights_to_device
+
+    shape = wl.TEXT_0P6B.replace(name="q06-2l-det", n_layers=2, vocab=1000, prompt_len=16, steps=16)
+    weights = wl.make_weights(shape)
+    inp = make_inputs(shape)
+    dw = weights_to_device(weights)
+    a = run_gpu(shape, dw, inp)
+    b = run_gpu(shape, dw, inp)
+    assert a.first_id == b.first_id
+    assert np.array_equal(a.ids, b.ids)
+    assert np.array_equal(a.hidden.view(np.uint32), b.hidden.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["talker-0.6b"])
+def test_full_talker_0p6b(name):
+    """The 0.6B talker at full size: 32-row prompt and 32 decode steps, every layer compared."""
+    _case(wl.BY_NAME[name], n_steps=32)
+
+
+def test_full_text_0p6b():
+    """The Qwen3-0.6B-shaped text decoder (151936-row tied head), 16 prompt ids and 16 greedy steps."""
+    _case(wl.TEXT_0P6B, n_steps=16)
+
+
+def test_full_talker_long_context():
+    """The talker with 4096 pre-filled positions: 8 decode steps compared."""
+    _case(wl.TALKER_0P6B_LONG, n_steps=8)
