@@ -1,0 +1,249 @@
+"""Benchmark: batch-1 persistent-kernel decode of the 0.6B-shaped TTS talker on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 256] [--warmup 2] [--workload talker-0.6b]
+
+One "step" is one decode step (one position through all layers, the LM head and
+the argmax).  The timed region is ONE mk_decode launch of --steps steps whose
+inputs (summed 17-embedding rows, rotary position streams) already sit in HBM;
+the 32-row prompt is prefilled, untimed, before it.  Prints one JSON line.
+
+Roofline: the decode kernel is bound by HBM.  Its algorithmic bytes per step are
+every weight byte it reads (all layers, norms, LM head) plus the KV cache bytes
+of positions 0..p; achieved GB/s = those bytes over the launch, divided by the
+launch time measured with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from persistent_megakernel_loop_amd import workload as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "batch-1 decode ms/step + achieved HBM GB/s (% of peak); TTFC for first chunk"
+FRAME_MS = 80.0  # one talker step = one 12.5 Hz codec frame
+
+
+def weight_bytes_per_step(s: wl.DecoderShape) -> int:
+    """Bytes of weights one decode step reads (the input row excluded)."""
+    wb = 2 if s.weight_dtype == "bf16" else 4
+    H, D, I, V = s.hidden, s.head_dim, s.intermediate, s.vocab
+    layer = (s.n_q_heads * D * H + 2 * s.n_kv_heads * D * H + H * s.n_q_heads * D + 3 * I * H)
+    norms = 2 * H + 2 * D
+    return (s.n_layers * (layer + norms) + V * H + H) * wb
+
+
+def kv_bytes_per_position(s: wl.DecoderShape) -> int:
+    return 2 * s.n_layers * s.n_kv_heads * s.head_dim * (2 if s.kv_dtype == "bf16" else 4)
+
+
+def step_bytes(s: wl.DecoderShape, first_pos: int, n: int) -> int:
+    """Algorithmic bytes of n decode steps at positions first_pos .. first_pos+n-1."""
+    kv = kv_bytes_per_position(s) * sum(p + 1 for p in range(first_pos, first_pos + n))
+    return weight_bytes_per_step(s) * n + kv
+
+
+def gpu_inputs(shape, n_prompt, n_steps, torch):
+    """Talker rows built on the GPU by mk_embed_sum from seeded tables and ids; ids-mode prompt otherwise."""
+    from persistent_megakernel_loop_amd.binding import embed_sum, to_device
+
+    dev = "cuda"
+    kv0 = shape.kv_prefill
+    if shape.inputs == "ids":
+        return dict(prompt_ids=torch.from_numpy(wl.make_prompt_ids(shape, n_prompt)).to(dev), prompt_rows=None,
+                    prompt_pos3=None, step_ids=None, step_rows=None, step_pos3=None)
+    tables = wl.make_talker_tables(shape.hidden)
+    cb, tx = to_device(tables["codebooks"]), to_device(tables["text"])
+    tids = torch.from_numpy(wl.make_talker_ids(n_prompt + n_steps)).to(dev)
+    rows = embed_sum(cb, tx, tids)
+    pos3 = torch.from_numpy(wl.position_streams(kv0, n_prompt + n_steps)).to(dev)
+    sent = torch.full((n_prompt + n_steps,), -1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    del cb, tx
+    return dict(prompt_ids=sent[:n_prompt] if n_prompt else None, prompt_rows=rows[:n_prompt] if n_prompt else None,
+                prompt_pos3=pos3[:n_prompt] if n_prompt else None, step_ids=sent[n_prompt:],
+                step_rows=rows[n_prompt:].contiguous(), step_pos3=pos3[n_prompt:].contiguous())
+
+
+def cpu_baseline(shape, n_prompt, budget_s=15.0, max_steps=256):
+    """The oracle (float64 numpy) timed on this host on a bounded sample of the same workload."""
+    from oracle import Decoder as OracleDecoder
+    from oracle import embed_sum17
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    weights = wl.make_weights(shape)
+    dec = OracleDecoder.from_shape(shape, weights)
+    kv0 = shape.kv_prefill
+    if kv0:
+        dec.load_kv(wl.make_kv_prefill(shape))
+    if shape.inputs == "talker":
+        tables = wl.make_talker_tables(shape.hidden)
+        tids = wl.make_talker_ids(n_prompt + max_steps)
+        rows = np.stack([embed_sum17(tables["codebooks"], tables["text"], t) for t in tids])
+        pos3 = wl.position_streams(kv0, n_prompt + max_steps)
+        if n_prompt:
+            dec.prefill(wl.sentinel_ids(n_prompt), rows[:n_prompt], pos3[:n_prompt])
+        nxt = lambda s: (dec.input_row(-1, rows[n_prompt + s]), pos3[n_prompt + s])  # noqa: E731
+    else:
+        first, _, _ = dec.prefill(wl.make_prompt_ids(shape, n_prompt))
+        cur = [first]
+        nxt = lambda s: (dec.input_row(cur[-1]), None)  # noqa: E731
+    t0 = time.perf_counter()
+    done = 0
+    while done < max_steps and time.perf_counter() - t0 < budget_s:
+        x0, p3 = nxt(done)
+        logits, _ = dec.step(x0, p3)
+        if shape.inputs == "ids":
+            cur.append(int(np.argmax(logits.astype(np.float32))))
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} decode steps of {shape.name} (float64 numpy oracle, after a {n_prompt}-position "
+                      f"prefill), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="talker-0.6b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ttfc-trials", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from persistent_megakernel_loop_amd.binding import Decoder, to_device, weights_to_device
+
+    shape = wl.BY_NAME[args.workload]
+    K = args.steps
+    P = shape.prompt_len
+    shape = shape.replace(max_seq=shape.kv_prefill + P + K)
+    weights = wl.make_weights(shape)
+    dw = weights_to_device(weights)
+    dec = Decoder(shape, dw)
+    del dw
+    torch.cuda.empty_cache()
+    inp = gpu_inputs(shape, P, K, torch)
+    kv = to_device(wl.make_kv_prefill(shape)) if shape.kv_prefill else None
+    out = torch.empty(K, dtype=torch.int32, device="cuda")
+    first = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def prepare():
+        dec.reset()
+        if kv is not None:
+            dec.load_kv(kv, shape.kv_prefill)
+        if P:
+            dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first)
+
+    def decode():
+        dec.decode(K, inp["step_ids"], inp["step_rows"], inp["step_pos3"], out=out)
+
+    for _ in range(args.warmup):
+        prepare()
+        decode()
+    torch.cuda.synchronize()
+    dec.check()
+    # timed: one decode launch of K steps, events on the launch stream
+    prepare()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    decode()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    dec.check()
+    launch_ms = e0.elapsed_time(e1)
+    ms_step = launch_ms / K
+    first_pos = shape.kv_prefill + P
+    algo = step_bytes(shape, first_pos, K)
+    gbps = algo / (launch_ms * 1e-3) / 1e9
+
+    # time to first chunk: host clock from the prefill enqueue until the host sees k ids
+    ttfc = {}
+    if P:
+        for kf in (1, 2, 4, 8):
+            trials = []
+            for _ in range(args.ttfc_trials):
+                dec.reset()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first)
+                if kf == 1:
+                    while dec.progress() < 1:
+                        pass
+                else:
+                    dec.decode(kf - 1, inp["step_ids"], inp["step_rows"], inp["step_pos3"], out=out)
+                    while dec.progress() < kf - 1:
+                        pass
+                trials.append((time.perf_counter() - t0) * 1e3)
+                torch.cuda.synchronize()
+            ttfc[str(kf)] = round(float(np.median(trials)), 3)
+        dec.check()
+
+    # barrier share: in-kernel wait ticks over position ticks, one separate traced run
+    prepare()
+    trace = torch.zeros((K, dec.grid_size(), 2), dtype=torch.int64, device="cuda")
+    dec.set_debug(None, trace)
+    decode()
+    torch.cuda.synchronize()
+    dec.set_debug(None, None)
+    tr = trace.cpu().numpy().astype(np.float64)
+    share = float(tr[:, :, 0].sum() / max(tr[:, :, 1].sum(), 1.0))
+    dec.check()
+
+    res = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 2),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "layers": shape.n_layers, "hidden": shape.hidden, "vocab": shape.vocab,
+                   "prompt_positions": P, "kv_prefill": shape.kv_prefill, "decode_steps": K, "batch": 1,
+                   "weights": "bf16 N(0,0.02) random", "kv_cache": shape.kv_dtype, "launches_timed": 1},
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "ttfc_ms": ttfc,
+        "rtf_talker_only": round(ms_step / FRAME_MS, 5),
+        "barrier_share": round(share, 4),
+        "wall_ms_timed_launch": round(wall_ms, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(launch_ms, 4)},
+    }
+    dec.close()
+    del inp
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(shape, P)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
