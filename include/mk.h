@@ -59,6 +59,7 @@ extern "C" {
  *   hidden 256,  head_dim 64,  16/8 -> 4/2 heads, intermediate 768,  f32 weights  (tiny)
  *   hidden 1024, head_dim 128, 16 q / 8 kv heads, intermediate 3072, bf16 weights (Qwen3-0.6B body)
  *   hidden 2048, head_dim 128, 16 q / 8 kv heads, intermediate 6144, bf16 weights (1.7B-scale talker)
+ * The KV cache is kept in the body's weight dtype (kv_dtype must equal weight_dtype).
  * n_layers, vocab (< 2^18), max_seq, tied, rms_eps, rope_theta and the rotary
  * sections are free.  sections[0..n_sections) are counts of rotary PAIRS, contiguous
  * from pair 0, summing to head_dim/2; section k turns with position stream k
@@ -135,6 +136,15 @@ int mk_position(mk_handle* h, int32_t* pos);
  *            waiting for other workgroups and the ticks of the whole position. */
 int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
 
+/* Barrier timeline of one workgroup for the following prefill/decode calls (NULL
+ * turns it off): d_phase [n][2 + 10*n_layers][4] uint64 receives, for each position
+ * the call runs and each workgroup barrier of that position in program order (input
+ * fetch, ten per layer, LM head), the 100 MHz ticks at which workgroup wg's control
+ * wave arrived at it and left it, then the ticks at which the first two waits for
+ * other workgroups' words in the segment before that barrier completed (0 if none).
+ * MK_ERR_ARG if wg is not in [0, grid). */
+int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
+
 /* Ids published so far by the most recently enqueued prefill/decode call (0 until
  * its first id), read from pinned host memory without synchronizing: the basis of
  * time-to-first-chunk.  A prefill publishes one id. */
@@ -143,6 +153,17 @@ int mk_progress(mk_handle* h, int64_t* steps_done);
 /* Synchronize the stream and report the device error word (MK_OK when clean).
  * The word is cleared by the read. */
 int mk_status(mk_handle* h);
+
+/* Where the first wait that timed out was (after mk_status returned MK_ERR_TIMEOUT):
+ * info[0] = 1 if recorded, then the workgroup, the tag it waited for, the word offset
+ * of that word from the start of the handle's exchange buffers, and the tag found
+ * there.  Synchronizes the stream; reading re-arms the record. */
+int mk_error_info(mk_handle* h, int32_t* info /* [5] */);
+
+/* Self-test of the LDS DMA copy the kernel streams weights with: one workgroup copies
+ * n_chunks 16-byte chunks of d_src into LDS at byte offset offset_bytes, then back out to
+ * d_dst (device buffers of n_chunks * 16 bytes).  offset_bytes + 16 n_chunks <= 147456. */
+int mk_selftest_lds_dma(const void* d_src, void* d_dst, int32_t n_chunks, int32_t offset_bytes, void* stream);
 
 /* Number of workgroups of the persistent grid (one per CU). */
 int mk_grid_size(mk_handle* h, int32_t* n);

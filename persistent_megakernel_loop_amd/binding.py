@@ -18,11 +18,13 @@ _LIB_NAME = "libmk.so"
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_progress", "mk_status", "mk_grid_size", "mk_embed_sum", "mk_strerror", "mk_destroy")
+           "mk_set_phase_trace", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_grid_size",
+           "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, _LIB_NAME)
+    """The in-tree libmk.so, or the file MK_LIBRARY names (an alternative build of the same ABI)."""
+    return os.environ.get("MK_LIBRARY") or os.path.join(_PKG, _LIB_NAME)
 
 
 class MkError(RuntimeError):
@@ -68,8 +70,11 @@ def lib():
     L.mk_reset.argtypes = [vp]
     L.mk_position.argtypes = [vp, pi32]
     L.mk_set_debug.argtypes = [vp, vp, vp]
+    L.mk_set_phase_trace.argtypes = [vp, vp, i32]
     L.mk_progress.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
     L.mk_status.argtypes = [vp]
+    L.mk_error_info.argtypes = [vp, pi32]
+    L.mk_selftest_lds_dma.argtypes = [vp, vp, i32, i32, vp]
     L.mk_grid_size.argtypes = [vp, pi32]
     L.mk_embed_sum.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     L.mk_strerror.argtypes = [ctypes.c_int]
@@ -194,6 +199,9 @@ class Decoder:
     def set_debug(self, hidden=None, trace=None):
         _check(lib().mk_set_debug(self.handle, _ptr(hidden), _ptr(trace)), "mk_set_debug")
 
+    def set_phase_trace(self, phase=None, wg: int = 0):
+        _check(lib().mk_set_phase_trace(self.handle, _ptr(phase), wg), "mk_set_phase_trace")
+
     def progress(self) -> int:
         v = ctypes.c_int64()
         _check(lib().mk_progress(self.handle, ctypes.byref(v)), "mk_progress")
@@ -203,7 +211,12 @@ class Decoder:
         return lib().mk_status(self.handle)
 
     def check(self):
-        _check(self.status(), "device status")
+        code = self.status()
+        if code != 0:
+            info = (ctypes.c_int32 * 5)()
+            lib().mk_error_info(self.handle, info)
+            raise MkError(code, f"device status (first timeout: recorded={info[0]} wg={info[1]} tag={info[2]} "
+                                f"word={info[3]} seen={info[4]})")
 
     def grid_size(self) -> int:
         n = ctypes.c_int32()
@@ -220,6 +233,12 @@ class Decoder:
             self.close()
         except Exception:
             pass
+
+
+def selftest_lds_dma(src, dst, offset_bytes: int = 0, stream=None):
+    """Copy src -> LDS (at offset_bytes) -> dst through the kernel's LDS DMA path (both int32/uint8 device tensors)."""
+    n = src.numel() * src.element_size() // 16
+    _check(lib().mk_selftest_lds_dma(_ptr(src), _ptr(dst), n, offset_bytes, _stream_handle(stream)), "mk_selftest_lds_dma")
 
 
 def embed_sum(codebooks, text, ids, rows=None, bad=None, stream=None):

@@ -28,7 +28,7 @@ struct mk_handle {
   LayerLayout lay{};
   uint8_t* embed = nullptr;
   uint8_t* lm_head = nullptr;
-  float* final_norm = nullptr;
+  float* in_norm0 = nullptr;
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
   // cache and exchange
@@ -36,7 +36,7 @@ struct mk_handle {
   void* vcache = nullptr;
   unsigned long long* xbuf = nullptr;
   size_t xbuf_words = 0;
-  unsigned long long *xq, *xatt, *xop, *xxa, *xm, *xdp, *xxb, *xarg;
+  unsigned long long *xq, *xatt, *xop, *xxa, *xm, *xdp, *xxb, *xarg, *xplace;
   uint32_t* ctl = nullptr;  // [0] err, [1] abort, [2] last id
   // pinned
   unsigned long long* progress = nullptr;
@@ -50,6 +50,8 @@ struct mk_handle {
   uint32_t call_seq = 0;
   float* dbg_hidden = nullptr;
   unsigned long long* dbg_trace = nullptr;
+  unsigned long long* dbg_phase = nullptr;
+  int32_t dbg_phase_wg = 0;
 };
 
 namespace {
@@ -108,11 +110,8 @@ LayerLayout make_layout(const mk_cfg* c, int wb) {
   L.o = align_up(L.qkv + NG * RQKV * H * wb, 256);
   L.gu = align_up(L.o + NG * H * OC * wb, 256);
   L.down = align_up(L.gu + mk::kXcds * 2 * IX * H * wb, 256);
-  L.in_norm = align_up(L.down + mk::kXcds * H * IX * wb, 256);
-  L.post_norm = align_up(L.in_norm + H * 4, 256);
-  L.q_norm = align_up(L.post_norm + H * 4, 256);
-  L.k_norm = align_up(L.q_norm + D * 4, 256);
-  L.stride = align_up(L.k_norm + D * 4, 4096);
+  L.gains = align_up(L.down + mk::kXcds * H * IX * wb, 256);
+  L.stride = align_up(L.gains + (2 * H + 2 * D) * 4, 4096);
   return L;
 }
 
@@ -159,11 +158,15 @@ int pack_layer(mk_handle* h, const mk_weights* w, int l) {
     e = copy2d(base + h->lay.down + x * H * IX * wb, IX * wb, wd + x * IX * wb, I * wb, IX * wb, H, s);
     if (e) return e;
   }
+  // gains block of layer l, in the order the kernel consumes it: post-attention norm, q norm,
+  // k norm, then the input norm of layer l+1 (the final norm after the last layer)
   const int bf = c->weight_dtype == MK_BF16;
-  if (mk::launch_widen(w->in_norm[l], (float*)(base + h->lay.in_norm), (int)H, bf, s)) return MK_ERR_HIP;
-  if (mk::launch_widen(w->post_norm[l], (float*)(base + h->lay.post_norm), (int)H, bf, s)) return MK_ERR_HIP;
-  if (mk::launch_widen(w->q_norm[l], (float*)(base + h->lay.q_norm), (int)D, bf, s)) return MK_ERR_HIP;
-  if (mk::launch_widen(w->k_norm[l], (float*)(base + h->lay.k_norm), (int)D, bf, s)) return MK_ERR_HIP;
+  float* g = (float*)(base + h->lay.gains);
+  const void* next_in = l + 1 < c->n_layers ? w->in_norm[l + 1] : w->final_norm;
+  if (mk::launch_widen(w->post_norm[l], g, (int)H, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(w->q_norm[l], g + H, (int)D, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(w->k_norm[l], g + H + D, (int)D, bf, s)) return MK_ERR_HIP;
+  if (mk::launch_widen(next_in, g + H + 2 * D, (int)H, bf, s)) return MK_ERR_HIP;
   return MK_OK;
 }
 
@@ -218,7 +221,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.lay = h->lay;
   P.embed = h->embed;
   P.lm_head = h->lm_head;
-  P.final_norm = h->final_norm;
+  P.in_norm0 = h->in_norm0;
   P.rope_cos = h->rope_cos;
   P.rope_sin = h->rope_sin;
   P.rope_positions = h->cfg.max_seq;
@@ -235,6 +238,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.kv_bf16 = h->cfg.kv_dtype == MK_BF16;
   P.xq = h->xq; P.xatt = h->xatt; P.xop = h->xop; P.xxa = h->xxa;
   P.xm = h->xm; P.xdp = h->xdp; P.xxb = h->xxb; P.xarg = h->xarg;
+  P.xplace = h->xplace;
   P.err = h->ctl;
   P.abort_flag = h->ctl + 1;
   P.last_id = (int32_t*)(h->ctl + 2);
@@ -252,8 +256,10 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.progress = h->progress;
   P.dbg_hidden = h->dbg_hidden;
   P.dbg_trace = h->dbg_trace;
+  P.dbg_phase = h->dbg_phase;
+  P.dbg_phase_wg = h->dbg_phase_wg;
   // tags are compared for equality: before they wrap, clear the buffers so that no old word can match
-  const uint32_t need = (uint32_t)n * mk::tags_per_position(h->cfg.n_layers);
+  const uint32_t need = (uint32_t)n * mk::tags_per_position(h->cfg.n_layers) + 1;
   if ((unsigned long long)h->tag + need >= 0xFFFFFFF0ull) {
     if (hipMemsetAsync(h->xbuf, 0, h->xbuf_words * 8, h->stream) != hipSuccess) return MK_ERR_HIP;
     h->tag = 1;
@@ -290,6 +296,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   }
   const int body = pick_body(cfg);
   if (body < 0) return MK_ERR_UNSUPPORTED;
+  if (cfg->kv_dtype != cfg->weight_dtype) return MK_ERR_UNSUPPORTED;  // each body caches in its weight dtype
   int blocks = 0;
   if (mk::coop_ok(body, &blocks)) return MK_ERR_HIP;
   mk_handle* h = new (std::nothrow) mk_handle();
@@ -320,7 +327,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   if (hipMalloc((void**)&h->arena, h->arena_bytes) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
   h->embed = h->arena + embed_off;
   h->lm_head = h->arena + lm_off;
-  h->final_norm = (float*)(h->arena + fn_off);
+  h->in_norm0 = (float*)(h->arena + fn_off);
   h->rope_cos = (float*)(h->arena + rope_off);
   h->rope_sin = h->rope_cos + rope_n;
 
@@ -332,7 +339,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   // exchange buffers
   const size_t QPG = cfg->n_q_heads / cfg->n_kv_heads, IX = cfg->intermediate / mk::kXcds;
   const size_t nq = 8 * (QPG + 2) * D, natt = 8 * mk::kPerXcd * QPG * (D + 2), nh = 8 * H, nm = 8 * IX;
-  h->xbuf_words = nq + natt + 5 * nh + nm + mk::kGrid + 64 * 8;
+  h->xbuf_words = nq + natt + 5 * nh + nm + 2 * mk::kGrid + 64 * 9;
   if (hipMalloc((void**)&h->xbuf, h->xbuf_words * 8) != hipSuccess ||
       hipMalloc((void**)&h->ctl, 256) != hipSuccess) {
     free_handle(h);
@@ -342,6 +349,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   auto take = [&](size_t n) { unsigned long long* r = p; p += align_up(n, 64); return r; };
   h->xq = take(nq); h->xatt = take(natt); h->xop = take(nh); h->xxa = take(nh); h->xm = take(nm);
   h->xdp = take(nh); h->xxb = take(nh); h->xarg = take(mk::kGrid);
+  h->xplace = take(mk::kGrid);
   if ((size_t)(p - h->xbuf) > h->xbuf_words) { free_handle(h); return MK_ERR_ARG; }
   if (hipHostMalloc((void**)&h->progress, 64, hipHostMallocCoherent) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
   *(volatile unsigned long long*)h->progress = 0;
@@ -357,7 +365,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   }
   if (hipMemcpyAsync(h->embed, w->embed, V * H * h->wb, hipMemcpyDeviceToDevice, s) != hipSuccess ||
       (!cfg->tied && hipMemcpyAsync(h->lm_head, w->lm_head, V * H * h->wb, hipMemcpyDeviceToDevice, s) != hipSuccess) ||
-      mk::launch_widen(w->final_norm, h->final_norm, (int)H, cfg->weight_dtype == MK_BF16, s)) {
+      mk::launch_widen(w->in_norm[0], h->in_norm0, (int)H, cfg->weight_dtype == MK_BF16, s)) {
     free_handle(h);
     return MK_ERR_HIP;
   }
@@ -429,6 +437,13 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace) {
   return MK_OK;
 }
 
+int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg) {
+  if (!h || wg < 0 || wg >= mk::kGrid) return MK_ERR_ARG;
+  h->dbg_phase = (unsigned long long*)d_phase;
+  h->dbg_phase_wg = wg;
+  return MK_OK;
+}
+
 int mk_progress(mk_handle* h, int64_t* steps_done) {
   if (!h || !steps_done) return MK_ERR_ARG;
   const unsigned long long v = *(volatile unsigned long long*)h->progress;
@@ -439,6 +454,25 @@ int mk_progress(mk_handle* h, int64_t* steps_done) {
 int mk_status(mk_handle* h) {
   if (!h) return MK_ERR_ARG;
   return device_status(h, true);
+}
+
+int mk_error_info(mk_handle* h, int32_t* info) {
+  if (!h || !info) return MK_ERR_ARG;
+  uint32_t c[8];
+  HIPCK(hipStreamSynchronize(h->stream));
+  HIPCK(hipMemcpy(c, h->ctl, sizeof c, hipMemcpyDeviceToHost));
+  info[0] = (int32_t)c[3];
+  for (int k = 1; k < 5; ++k) info[k] = (int32_t)c[3 + k];
+  const uint32_t z = 0;
+  HIPCK(hipMemcpy(h->ctl + 3, &z, sizeof z, hipMemcpyHostToDevice));  // re-arm the record
+  return MK_OK;
+}
+
+int mk_selftest_lds_dma(const void* d_src, void* d_dst, int32_t n_chunks, int32_t offset_bytes, void* stream) {
+  if (!d_src || !d_dst || n_chunks <= 0 || offset_bytes < 0 || offset_bytes % 16 ||
+      offset_bytes + 16 * n_chunks > 144 * 1024)
+    return MK_ERR_ARG;
+  return mk::launch_lds_dma_selftest(d_src, d_dst, n_chunks, offset_bytes, stream) ? MK_ERR_HIP : MK_OK;
 }
 
 int mk_grid_size(mk_handle* h, int32_t* n) {

@@ -13,9 +13,9 @@ namespace mk {
 constexpr int kXcds = 8;
 constexpr int kPerXcd = 32;
 constexpr int kGrid = kXcds * kPerXcd;
-constexpr int kWorkerWaves = 8;              // stream weights and do the dot products
-constexpr int kThreads = (kWorkerWaves + 1) * 64;  // + one control wave (polls, exchanges)
-constexpr int kLdsBytes = 96 * 1024;         // > half of the 160 KB LDS: one workgroup per CU
+constexpr int kWorkerWaves = 7;              // stream weights and do the dot products
+constexpr int kThreads = (kWorkerWaves + 1) * 64;  // + one control wave (polls, exchanges): 8 waves,
+                                                   // two per SIMD, so each wave may use 256 VGPRs
 
 enum BodyId : int { BODY_TINY = 0, BODY_Q06 = 1, BODY_Q17 = 2 };
 
@@ -25,7 +25,7 @@ enum : uint32_t { DEV_ERR_ID = 1u, DEV_ERR_POS = 2u, DEV_ERR_TIMEOUT = 4u };
 // Offsets (bytes) of one layer's tensors inside the arena; every layer has the same layout.
 struct LayerLayout {
   size_t qkv, o, gu, down;            // packed weight tiles (weight dtype)
-  size_t in_norm, post_norm, q_norm, k_norm;   // float32 gains
+  size_t gains;                        // float32 block [post H][q_norm D][k_norm D][next input norm H]
   size_t stride;                       // bytes per layer
 };
 
@@ -35,7 +35,7 @@ struct Params {
   LayerLayout lay;
   const void* embed;         // [V][H] weight dtype
   const void* lm_head;       // [V][H] weight dtype (== embed when tied)
-  const float* final_norm;   // [H]
+  const float* in_norm0;     // [H] input norm of layer 0 (the next-input norm of layer L-1 is the final norm)
   const float* rope_cos;     // [rope_positions][D/2]
   const float* rope_sin;
   int32_t rope_positions;
@@ -56,7 +56,8 @@ struct Params {
   unsigned long long* xdp;   // [32][8][H/32] down partials, by reader    cross hop
   unsigned long long* xxb;   // [8][H] residual after the MLP    local hop
   unsigned long long* xarg;  // [grid] argmax keys               cross hop
-  uint32_t* err;             // device error word
+  unsigned long long* xplace;  // [grid] XCD of every workgroup, once per launch
+  uint32_t* err;             // device error word; err[3..7]: where the first timeout happened
   uint32_t* abort_flag;      // set on timeout: every wait gives up
   int32_t* last_id;          // feedback id carried between launches
   // this launch
@@ -72,13 +73,16 @@ struct Params {
   unsigned long long* progress;  // host-pinned step counter
   float* dbg_hidden;         // [n_pos][L+1][H] or NULL
   unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL
+  unsigned long long* dbg_phase; // [n_pos][2 + 10 L][4] barrier arrive/leave + 2 wait-done ticks of one workgroup, or NULL
+  int32_t dbg_phase_wg;
   uint32_t tag0;             // first exchange tag of this launch
   uint32_t lm_seq0;          // argmax key sequence of the first LM head of this launch (14 bits used)
   uint32_t call_seq;         // high half of the progress word
   uint32_t spin_limit;       // polls before a wait gives up
 };
 
-// Tags used by one position: kPhasesPerLayer per layer plus one for the LM head.
+// Tags used by one position: kPhasesPerLayer per layer plus two.  A launch also uses one
+// tag (its first) for the placement check.
 constexpr uint32_t kPhasesPerLayer = 8;
 __host__ __device__ inline uint32_t tags_per_position(int n_layers) { return (uint32_t)n_layers * kPhasesPerLayer + 2; }
 
@@ -88,5 +92,6 @@ int coop_ok(int body, int* blocks_per_cu);
 int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* text, int text_vocab,
                      int hidden, int bf16, const int32_t* ids, int n, float* rows, int32_t* bad, void* stream);
 int launch_widen(const void* src, float* dst, int n, int bf16, void* stream);
+int launch_lds_dma_selftest(const void* src, void* dst, int n_chunks, int offset_bytes, void* stream);
 
 }  // namespace mk

@@ -26,6 +26,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "mk_internal.h"
 
 namespace mk {
@@ -61,24 +64,20 @@ using BodyTiny = Body<256, 64, 4, 2, 768, false>;
 using BodyQ06 = Body<1024, 128, 16, 8, 3072, true>;
 using BodyQ17 = Body<2048, 128, 16, 8, 6144, true>;
 
-constexpr int largest_divisor_le8(int r) {
-  for (int d = kWorkerWaves; d >= 1; --d)
-    if (r % d == 0) return d;
-  return 1;
-}
-
 // A weight tile: ROWS consecutive rows of COLS columns, contiguous in the arena.
-// Wave w < NWA owns rows [w*RPW, (w+1)*RPW); its chunks are read lane-linearly.
+// Worker wave w < NWA owns rows [w*RPW, (w+1)*RPW) (the last wave may own fewer):
+// chunks w*CPW .. w*CPW+CPW-1 of the tile, read lane-linearly, 16 bytes per lane.
 template <class B, int ROWS, int COLS>
 struct Tile {
-  static constexpr int NWA = largest_divisor_le8(ROWS);
-  static constexpr int RPW = ROWS / NWA;
+  static constexpr int NWA = ROWS < kWorkerWaves ? ROWS : kWorkerWaves;
+  static constexpr int RPW = (ROWS + NWA - 1) / NWA;
   static constexpr int CPR = COLS / B::E;
   static constexpr int CPW = RPW * CPR;
+  static constexpr int TOTAL = ROWS * CPR;     // chunks in the tile
   static constexpr int LPL = (CPW + 63) / 64;
+  static constexpr bool EXACT = CPW % 64 == 0 && NWA * CPW == TOTAL;  // no chunk needs a guard
   static constexpr size_t BYTES = (size_t)ROWS * COLS * B::WB;
   static_assert(COLS % B::E == 0, "chunk");
-  static_assert(CPR % 64 == 0 || 64 % CPR == 0 || true, "");
   u4 v[LPL];
 };
 
@@ -107,8 +106,16 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 __device__ __forceinline__ u64 tagword(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
+// Cross-XCD words are written through to the device coherence point.
 __device__ __forceinline__ void st_tag(u64* p, float v, uint32_t tag) {
   __hip_atomic_store(p, tagword(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Words read only inside the writer's XCD: a plain store that stays in the XCD's L2,
+// where the readers' device-coherent loads find it.  Only used once the launch has
+// checked that every workgroup runs on XCD b % 8; otherwise written through too.
+__device__ __forceinline__ void st_local(u64* p, float v, uint32_t tag, bool plain) {
+  if (plain) __hip_atomic_store(p, tagword(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+  else __hip_atomic_store(p, tagword(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ u64 ld_coh(const u64* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -117,26 +124,55 @@ __device__ __forceinline__ uint32_t ld_coh32(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ void raise_error(const Params& P, uint32_t bits) {
+__device__ __forceinline__ void raise_error(const Params& P, uint32_t bits) {
   __hip_atomic_fetch_or(P.err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Control wave: wait until words src[0..n) all carry `tag`, copy their values to dst.
-// Returns false if the wait gave up (spin limit or another workgroup's abort).
+// A wait that gave up: latch the timeout, tell every workgroup to stop waiting, and let
+// the first one record where it was (workgroup, expected tag, word offset from the start
+// of the exchange buffers, tag found there).
+__device__ __forceinline__ void raise_timeout(const Params& P, const unsigned long long* where, uint32_t tag, uint32_t seen) {
+  raise_error(P, DEV_ERR_TIMEOUT);
+  __hip_atomic_store(P.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t expected = 0;
+  if (__hip_atomic_compare_exchange_strong(P.err + 3, &expected, 1u, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    P.err[4] = blockIdx.x;
+    P.err[5] = tag;
+    P.err[6] = (uint32_t)(where - P.xq);
+    P.err[7] = seen;
+  }
+}
+
+// Control wave: gather words src[0..n) that other workgroups publish, waiting until each
+// carries `tag`, into dst[0..n) (LDS).  Words [own0, own1) are this workgroup's own: the
+// caller writes them to dst itself and they are not read back.  `publish` (the caller's
+// own stores) runs right after the first round of loads is issued, so those loads do not
+// queue behind the stores in the wave's in-order memory counter.  Returns false if the
+// wait gave up (spin limit, or another workgroup's abort).
 constexpr int kPollK = 16;  // words in flight per lane per round
-__device__ bool poll_words(const u64* src, int n, uint32_t tag, float* dst, int lane, const Params& P) {
+template <class F>
+__device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, F&& publish, int lane,
+                         const Params& P) {
+  bool published = false;
   for (int base = 0; base < n; base += 64 * kPollK) {
     const int cnt = min(n - base, 64 * kPollK);
     uint32_t pending = 0;
 #pragma unroll
-    for (int k = 0; k < kPollK; ++k)
-      if (lane + 64 * k < cnt) pending |= 1u << k;
+    for (int k = 0; k < kPollK; ++k) {
+      const int i = base + lane + 64 * k;
+      if (lane + 64 * k < cnt && (i < own0 || i >= own1)) pending |= 1u << k;
+    }
     uint32_t it = 0;
     while (true) {
       u64 w[kPollK];
 #pragma unroll
       for (int k = 0; k < kPollK; ++k)
         if (pending & (1u << k)) w[k] = ld_coh(src + base + lane + 64 * k);
+      if (!published) {
+        publish();
+        published = true;
+      }
 #pragma unroll
       for (int k = 0; k < kPollK; ++k)
         if ((pending & (1u << k)) && (uint32_t)(w[k] >> 32) == tag) {
@@ -145,26 +181,35 @@ __device__ bool poll_words(const u64* src, int n, uint32_t tag, float* dst, int 
         }
       if (!__any(pending != 0)) break;
       if (++it >= P.spin_limit) {
-        raise_error(P, DEV_ERR_TIMEOUT);
-        __hip_atomic_store(P.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (pending) {  // record the first word still behind (selected without indexing w at run time)
+          const int k0 = __builtin_ctz(pending);
+          uint32_t seen = 0;
+#pragma unroll
+          for (int k = 0; k < kPollK; ++k) seen = k == k0 ? (uint32_t)(w[k] >> 32) : seen;
+          raise_timeout(P, src + base + lane + 64 * k0, tag, seen);
+        }
         return false;
       }
       if ((it & 63) == 0 && ld_coh32(P.abort_flag)) return false;
       __builtin_amdgcn_s_sleep(1);
     }
   }
+  if (!published) publish();
   return true;
 }
 
 // ------------------------------------------------------------------ GEMV tiles
+// Issue the wave's loads of a tile.  Unconditional on purpose: waves without rows
+// and chunks past the tile read the last valid chunk (never used), so the compiler
+// never has to merge loaded and unloaded register states.
 template <class T>
 __device__ __forceinline__ void tile_load(T& t, const uint8_t* base, int wave, int lane) {
-  if (wave >= T::NWA) return;
-  const u4* p = reinterpret_cast<const u4*>(base) + (size_t)wave * T::CPW;
+  const int w = min(wave, T::NWA - 1);
+  const u4* p = reinterpret_cast<const u4*>(base);
 #pragma unroll
   for (int j = 0; j < T::LPL; ++j) {
-    const int k = j * 64 + lane;
-    if (T::CPW % 64 == 0 || k < T::CPW) t.v[j] = __builtin_nontemporal_load(p + k);
+    const int g = w * T::CPW + j * 64 + lane;
+    t.v[j] = __builtin_nontemporal_load(p + (T::EXACT ? g : min(g, T::TOTAL - 1)));
   }
 }
 
@@ -202,7 +247,7 @@ __device__ __forceinline__ void tile_dot(const T& t, const float* act, float* re
 #pragma unroll
   for (int j = 0; j < T::LPL; ++j) {
     const int k = j * 64 + lane;
-    if (T::CPW % 64 == 0 || k < T::CPW) {
+    if (T::EXACT || (k < T::CPW && wave * T::CPW + k < T::TOTAL)) {
       const int row = k / T::CPR;
       const int col = (k - row * T::CPR) * B::E;
       const float d = dot_chunk<B>(t.v[j], act + col);
@@ -218,7 +263,41 @@ __device__ __forceinline__ void tile_dot(const T& t, const float* act, float* re
   for (int r = 0; r < T::RPW; ++r) acc[r] = wave_sum(acc[r]);
   if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < T::RPW; ++r) res[wave * T::RPW + r] = acc[r];
+    for (int r = 0; r < T::RPW; ++r)
+      if (wave * T::RPW + r < T::TOTAL / T::CPR)
+        res[wave * T::RPW + r] = acc[r];
+  }
+}
+
+// tile_dot with the tile in LDS: chunk g of the tile at slot[g].
+template <class B, class T>
+__device__ __forceinline__ void tile_dot_lds(const u4* slot, const float* act, float* res, int wave, int lane) {
+  if (wave >= T::NWA) return;
+  float acc[T::RPW];
+#pragma unroll
+  for (int r = 0; r < T::RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < T::LPL; ++j) {
+    const int k = j * 64 + lane;
+    if (T::EXACT || (k < T::CPW && wave * T::CPW + k < T::TOTAL)) {
+      const u4 w = slot[wave * T::CPW + k];
+      const int row = k / T::CPR;
+      const int col = (k - row * T::CPR) * B::E;
+      const float d = dot_chunk<B>(w, act + col);
+      if constexpr (T::CPR % 64 == 0) {
+        acc[(j * 64) / T::CPR] += d;
+      } else {
+#pragma unroll
+        for (int r = 0; r < T::RPW; ++r) acc[r] += (row == r) ? d : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < T::RPW; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < T::RPW; ++r)
+      if (wave * T::RPW + r < T::TOTAL / T::CPR) res[wave * T::RPW + r] = acc[r];
   }
 }
 
@@ -236,7 +315,12 @@ struct Lds {
   float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
   float wbest_v[kWorkerWaves];
   int wbest_i[kWorkerWaves];
-  int streams[3];
+  float g_in0[B::H];         // input norm of layer 0 (constant for the launch)
+  // gains of layer j in G[j % 2] (j counted from the launch start), filled by the workers
+  // ahead of use: [post-attention norm H][q norm D][k norm D][input norm of the next layer H],
+  // each buffer padded to whole KB because an LDS copy instruction always writes 1 KB
+  float G[2][(2 * B::H + 2 * B::D + 255) / 256 * 256];
+  float rope_c[B::D / 2], rope_s[B::D / 2];  // cos/sin of every rotary pair at this position
   int abort_;
 };
 
@@ -267,11 +351,12 @@ struct TileAddr {
   const Params& P;
   int x, r;
   __device__ const uint8_t* layer(int l) const { return P.layers + (size_t)l * P.lay.stride; }
+  // XCDs without a KV group (fewer groups than XCDs) address group x % NG: in bounds, unused
   __device__ const uint8_t* qkv(int l) const {
-    return layer(l) + P.lay.qkv + ((size_t)x * B::RQKV + (size_t)r * B::T_QKV) * B::H * B::WB;
+    return layer(l) + P.lay.qkv + ((size_t)(x % B::NG) * B::RQKV + (size_t)r * B::T_QKV) * B::H * B::WB;
   }
   __device__ const uint8_t* o(int l) const {
-    return layer(l) + P.lay.o + ((size_t)x * B::H + (size_t)r * B::T_O) * B::OC * B::WB;
+    return layer(l) + P.lay.o + ((size_t)(x % B::NG) * B::H + (size_t)r * B::T_O) * B::OC * B::WB;
   }
   __device__ const uint8_t* gu(int l) const {
     return layer(l) + P.lay.gu + ((size_t)x * kPerXcd + r) * (size_t)B::T_GU * B::H * B::WB;
@@ -279,182 +364,330 @@ struct TileAddr {
   __device__ const uint8_t* down(int l) const {
     return layer(l) + P.lay.down + ((size_t)x * B::H + (size_t)r * B::T_D) * B::IX * B::WB;
   }
-  __device__ const float* gain(int l, size_t off) const { return reinterpret_cast<const float*>(layer(l) + off); }
+  __device__ const uint8_t* gains(int l) const { return layer(l) + P.lay.gains; }
 };
 
-// Bodies whose four tiles fit in registers together are loaded a whole layer ahead;
-// the larger body loads each tile one phase ahead.
+// Bodies whose QKV and gate/up tiles fit in one LDS slot and O and down tiles in another
+// stream their tiles through LDS; the larger body holds them in registers, one phase ahead.
 template <class B>
-constexpr bool layer_ahead() { return B::H <= 1024; }
+constexpr bool lds_tiles() { return B::H <= 1024; }
+template <class B>
+constexpr int slot_a_bytes() { return lds_tiles<B>() ? (int)((((B::T_QKV > B::T_GU ? B::T_QKV : B::T_GU) * B::H * B::WB + 1023) / 1024) * 1024) : 16; }
+template <class B>
+constexpr int slot_b_bytes() {
+  return lds_tiles<B>() ? (int)((((B::T_O * B::OC > B::T_D * B::IX ? B::T_O * B::OC : B::T_D * B::IX) * B::WB + 1023) / 1024) * 1024) : 16;
+}
+constexpr int kGainFloats(int H, int D) { return 2 * H + 2 * D; }
+
+// ------------------------------------------------------------------ LDS DMA
+// One 16-byte chunk per lane from global memory straight into LDS: lane i's chunk lands at
+// lds + 16 i.  Issued through inline assembly so that the compiler neither waits for it at
+// barriers nor before unrelated LDS reads; completion is awaited explicitly with
+// wait_vmem<N>() by the issuing wave, before a barrier, where N counts the vector-memory
+// instructions this wave issued after it.  M0 (the LDS base register) is restored.
+__device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(g), "s"(l) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most the last M chunk-DMA instructions of this wave may still be pending,
+// where M is what worker wave w issues of a copy of NI instructions dealt round-robin.
+template <int NI>
+__device__ __forceinline__ void wait_after(int w) {
+  if constexpr (NI % kWorkerWaves == 0) wait_vmem<NI / kWorkerWaves>();
+  else if (w < NI % kWorkerWaves) wait_vmem<NI / kWorkerWaves + 1>();
+  else wait_vmem<NI / kWorkerWaves>();
+}
+// Copy `chunks` 16-byte chunks src -> lds; instruction i (64 chunks) is issued by wave i % 7.
+template <int CHUNKS>
+__device__ __forceinline__ void dma_copy(const uint8_t* src, void* lds, int wave, int lane) {
+  constexpr int NI = (CHUNKS + 63) / 64;
+  for (int i = wave; i < NI; i += kWorkerWaves) {
+    const int g = min(i * 64 + lane, CHUNKS - 1);
+    lds_dma16(src + (size_t)g * 16, reinterpret_cast<uint8_t*>(lds) + (size_t)i * 1024);
+  }
+}
 
 // ------------------------------------------------------------------ worker waves
+// LM head rows of one pass: 2 per worker wave from rb, wave w holds rows rb + 2w, rb + 2w + 1.
+// Rows at or past row_end read row_end-1 (in bounds, ignored by the argmax).
+template <class B, class T>
+__device__ __forceinline__ void lm_load(T& tl, const Params& P, int rb, int row_end, int wave, int lane) {
+  const int last = max(0, row_end - 1);
+#pragma unroll
+  for (int j = 0; j < T::LPL; ++j) {
+    const int k = min(j * 64 + lane, T::CPW - 1);
+    const int row = min(rb + wave * T::RPW + k / T::CPR, last);
+    const u4* p = reinterpret_cast<const u4*>(reinterpret_cast<const uint8_t*>(P.lm_head) + (size_t)row * B::H * B::WB);
+    tl.v[j] = __builtin_nontemporal_load(p + (k - (k / T::CPR) * T::CPR));
+  }
+}
+
+template <class B, class T>
+__device__ __forceinline__ void lm_dot(const T& tl, const float* an, int rb, int row_end, int wave, int lane,
+                                       float& bv, int& bi) {
+  float acc[T::RPW];
+#pragma unroll
+  for (int q = 0; q < T::RPW; ++q) acc[q] = 0.f;
+#pragma unroll
+  for (int j = 0; j < T::LPL; ++j) {
+    const int k = j * 64 + lane;
+    if (T::CPW % 64 == 0 || k < T::CPW) {
+      const int row = k / T::CPR;
+      const float d = dot_chunk<B>(tl.v[j], an + (k - row * T::CPR) * B::E);
+#pragma unroll
+      for (int q = 0; q < T::RPW; ++q) acc[q] += (row == q) ? d : 0.f;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < T::RPW; ++q) {
+    const float v = wave_sum(acc[q]);
+    const int row = rb + wave * T::RPW + q;
+    if (row < row_end && (v > bv || (v == bv && row < bi))) { bv = v; bi = row; }
+  }
+}
+
+// Attention of this rank's chunk [c0, c1) of positions for the group's query heads.  A
+// cache row (one position's K or V of one KV head) is 256 bytes: 16 lanes hold 16 bytes
+// each, so one load instruction covers 4 positions (lane group sub = lane / 16).  Each
+// worker wave takes a contiguous share of the chunk; all its row loads of a batch are in
+// flight together (device-coherent 128-bit buffer loads).  Every lane group keeps an online
+// softmax over its positions; the four groups are merged at the end.  The current position
+// p is taken from LDS (K rotated and both rounded to cache precision by the control wave).
 template <class B>
-__device__ void worker_loop(const Params& P, Lds<B>& S, int x, int r, int wave, int lane) {
+__device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int x, int l, int p, int c0, int c1,
+                                                int wave, int lane) {
+  constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
+  static_assert(ROWB == 256, "a cache row is 16 lanes x 16 bytes");
+  constexpr int DPC = B::BF16 ? 8 : 4;  // head dims per 16-byte chunk
+  constexpr int UNR = 4;                // load instructions (4 positions each) per batch
+  const int sub = lane >> 4, li = lane & 15;
+  float q[B::QPG][DPC];
+#pragma unroll
+  for (int h = 0; h < B::QPG; ++h)
+#pragma unroll
+    for (int e = 0; e < DPC; ++e) q[h][e] = S.qkv[h * B::D + li * DPC + e];
+  float m[B::QPG], ls[B::QPG], acc[B::QPG][DPC];
+#pragma unroll
+  for (int h = 0; h < B::QPG; ++h) {
+    m[h] = -INFINITY;
+    ls[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPC; ++e) acc[h][e] = 0.f;
+  }
+  const int n = c1 - c0;
+  const int per = (n + kWorkerWaves - 1) / kWorkerWaves;
+  const int w0 = c0 + wave * per, w1 = min(c1, w0 + per);
+  const size_t row0 = ((size_t)l * B::NKV + x) * P.max_seq;
+  const int nbytes = P.max_seq * ROWB;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.kcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.vcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
+  constexpr int kCoherent = 16;  // cache-policy bit: device-coherent load
+  for (int jb = w0; jb < w1; jb += 4 * UNR) {
+    u4 kr[UNR], vr[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int jj = min(jb + 4 * u + sub, w1 - 1);
+      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, jj * ROWB + li * 16, 0, kCoherent);
+      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, jj * ROWB + li * 16, 0, kCoherent);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int j = jb + 4 * u + sub;
+      float kf[DPC], vf[DPC];
+      if (j == p) {
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) { kf[e] = S.kp[li * DPC + e]; vf[e] = S.vp[li * DPC + e]; }
+      } else if constexpr (B::BF16) {
+        const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[2 * e] = bf16lo(kw[e]); kf[2 * e + 1] = bf16hi(kw[e]);
+          vf[2 * e] = bf16lo(vw[e]); vf[2 * e + 1] = bf16hi(vw[e]);
+        }
+      } else {
+        kf[0] = __uint_as_float(kr[u].x); kf[1] = __uint_as_float(kr[u].y);
+        kf[2] = __uint_as_float(kr[u].z); kf[3] = __uint_as_float(kr[u].w);
+        vf[0] = __uint_as_float(vr[u].x); vf[1] = __uint_as_float(vr[u].y);
+        vf[2] = __uint_as_float(vr[u].z); vf[3] = __uint_as_float(vr[u].w);
+      }
+      const bool valid = j < w1;
+#pragma unroll
+      for (int h = 0; h < B::QPG; ++h) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPC; ++e) sc = fmaf(q[h][e], kf[e], sc);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sc += __shfl_xor(sc, o);  // within the 16-lane group
+        if (valid) {
+          const float mn = fmaxf(m[h], sc);
+          const float corr = __expf(m[h] - mn);  // 0 while m is still -inf
+          const float ee = __expf(sc - mn);
+          ls[h] = ls[h] * corr + ee;
+#pragma unroll
+          for (int e = 0; e < DPC; ++e) acc[h][e] = fmaf(acc[h][e], corr, ee * vf[e]);
+          m[h] = mn;
+        }
+      }
+    }
+  }
+  // merge the four position groups of the wave (lanes xor 16, xor 32)
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+#pragma unroll
+    for (int h = 0; h < B::QPG; ++h) {
+      const float mo = __shfl_xor(m[h], o), lo = __shfl_xor(ls[h], o);
+      const float M = fmaxf(m[h], mo);
+      const float fa = m[h] == -INFINITY ? 0.f : __expf(m[h] - M);
+      const float fb = mo == -INFINITY ? 0.f : __expf(mo - M);
+      ls[h] = ls[h] * fa + lo * fb;
+#pragma unroll
+      for (int e = 0; e < DPC; ++e) {
+        const float ao = __shfl_xor(acc[h][e], o);
+        acc[h][e] = acc[h][e] * fa + ao * fb;
+      }
+      m[h] = M;
+    }
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int h = 0; h < B::QPG; ++h) {
+#pragma unroll
+      for (int e = 0; e < DPC; ++e) S.wpart[wave][h][2 + li * DPC + e] = acc[h][e];
+      if (li == 0) {
+        S.wpart[wave][h][0] = m[h];
+        S.wpart[wave][h][1] = ls[h];
+      }
+    }
+  }
+}
+
+template <class B>
+__device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int x, int r, int wave, int lane) {
   using TQKV = Tile<B, B::T_QKV, B::H>;
   using TO = Tile<B, B::T_O, B::OC>;
   using TGU = Tile<B, B::T_GU, B::H>;
   using TD = Tile<B, B::T_D, B::IX>;
-  using TLM = Tile<B, 16, B::H>;
+  using TLM = Tile<B, 2 * kWorkerWaves, B::H>;
+  constexpr int LMR = 2 * kWorkerWaves;  // LM head rows per pass
   const TileAddr<B> A{P, x, r};
-  const bool grp = x < B::NG;
+  const bool grp = B::NG == kXcds || x < B::NG;
   const int L = P.n_layers;
   const int b = blockIdx.x;
-  constexpr bool LA = layer_ahead<B>();
+  const int rpb = (P.vocab + kGrid - 1) / kGrid;
+  const int lm0 = b * rpb, lm1 = min(P.vocab, lm0 + rpb);
+  constexpr bool LA = false;  // tiles one phase ahead (the whole layer does not fit)
+  __builtin_assume(wave >= 0 && wave < kWorkerWaves);
 
+  // Every load below is unconditional (addresses clamped in bounds): a conditional
+  // load would make the compiler copy the tile registers and wait for them.
   TQKV tq;
   TO to;
   TGU tg;
   TD td;
-  if (grp) tile_load(tq, A.qkv(0), wave, lane);
+  TLM tl;
+  // Gains block of the layer entered next, held in registers one layer ahead and
+  // written to LDS (G[layer count % 2]) at that layer's first phase.
+  constexpr int NT = kWorkerWaves * 64;
+  constexpr int NGF = kGainFloats(B::H, B::D);
+  constexpr int GPT = (NGF + NT - 1) / NT;
+  const int tid = wave * 64 + lane;
+  float r_g[GPT];
+  auto gload = [&](int l) {
+    const float* g = reinterpret_cast<const float*>(A.gains(l));
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) r_g[k] = g[min(tid + NT * k, NGF - 1)];
+  };
+  int gc = 0;  // layers entered since the launch started
+  auto gstore = [&]() {
+    float* G = S.G[gc & 1];
+#pragma unroll
+    for (int k = 0; k < GPT; ++k)
+      if (tid + NT * k < NGF) G[tid + NT * k] = r_g[k];
+  };
+  gload(0);
+  tile_load(tq, A.qkv(0), wave, lane);
   if constexpr (LA) {
-    if (grp) tile_load(to, A.o(0), wave, lane);
+    tile_load(to, A.o(0), wave, lane);
     tile_load(tg, A.gu(0), wave, lane);
     tile_load(td, A.down(0), wave, lane);
   }
 
   for (int t = 0; t < P.n_pos; ++t) {
     const int p = P.pos0 + t;
-    const bool last_t = t + 1 == P.n_pos;
+    const bool lm = t >= P.logits_from;
     __syncthreads();  // input fetched
     if (S.abort_) return;
-    for (int l = 0; l < L; ++l) {
-      const bool more = (l + 1 < L) || !last_t;
+    auto layer = [&](int l, auto last) -> bool {
       const int ln = (l + 1 < L) ? l + 1 : 0;
       // q, k, v rows
-      if (grp) {
-        tile_dot<B>(tq, S.an, S.res, wave, lane);
-        if constexpr (LA) { if (more) tile_load(tq, A.qkv(ln), wave, lane); }
-        else tile_load(to, A.o(l), wave, lane);
-      }
+      gstore();
+      if (grp) tile_dot<B>(tq, S.an, S.res, wave, lane);
+      gload(ln);
+      if constexpr (!LA) tile_load(to, A.o(l), wave, lane);
       __syncthreads();
       __syncthreads();  // q rotated, k/v of position p in LDS
-      if (S.abort_) return;
+      if (S.abort_) return false;
       // attention over this rank's chunk of positions
       const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
-      if (grp && r < nc) {
-        const int c0 = r * csz, c1 = min(p + 1, c0 + csz);
-        float m[B::QPG], ls[B::QPG], acc[B::QPG][B::DPL];
-#pragma unroll
-        for (int h = 0; h < B::QPG; ++h) {
-          m[h] = -INFINITY;
-          ls[h] = 0.f;
-#pragma unroll
-          for (int k = 0; k < B::DPL; ++k) acc[h][k] = 0.f;
-        }
-        const size_t cbase = (((size_t)l * B::NKV + x) * P.max_seq) * B::D;
-        for (int j = c0 + wave; j < c1; j += kWorkerWaves) {
-          float kk[B::DPL], vv[B::DPL];
-          if (j == p) {
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) { kk[k] = S.kp[lane + 64 * k]; vv[k] = S.vp[lane + 64 * k]; }
-          } else {
-            const size_t off = cbase + (size_t)j * B::D;
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) {
-              const int i = lane + 64 * k;
-              if (P.kv_bf16) {
-                kk[k] = bf16_to_f(__hip_atomic_load(reinterpret_cast<const uint16_t*>(P.kcache) + off + i,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                vv[k] = bf16_to_f(__hip_atomic_load(reinterpret_cast<const uint16_t*>(P.vcache) + off + i,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-              } else {
-                kk[k] = __hip_atomic_load(reinterpret_cast<const float*>(P.kcache) + off + i, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-                vv[k] = __hip_atomic_load(reinterpret_cast<const float*>(P.vcache) + off + i, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-              }
-            }
-          }
-#pragma unroll
-          for (int h = 0; h < B::QPG; ++h) {
-            float s = 0.f;
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) s = fmaf(S.qkv[h * B::D + lane + 64 * k], kk[k], s);
-            s = wave_sum(s);
-            const float mn = fmaxf(m[h], s);
-            const float corr = __expf(m[h] - mn);
-            const float e = __expf(s - mn);
-            ls[h] = ls[h] * corr + e;
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) acc[h][k] = fmaf(acc[h][k], corr, e * vv[k]);
-            m[h] = mn;
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < B::QPG; ++h) {
-#pragma unroll
-          for (int k = 0; k < B::DPL; ++k) S.wpart[wave][h][2 + lane + 64 * k] = acc[h][k];
-          if (lane == 0) {
-            S.wpart[wave][h][0] = m[h];
-            S.wpart[wave][h][1] = ls[h];
-          }
-        }
-      }
+      if (grp && r < nc) attention_chunk<B>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane);
       __syncthreads();
       __syncthreads();  // attention output of the group in LDS
-      if (S.abort_) return;
+      if (S.abort_) return false;
       // O partial
-      if (grp) {
-        tile_dot<B>(to, S.ov, S.res, wave, lane);
-        if constexpr (LA) { if (more) tile_load(to, A.o(ln), wave, lane); }
+      if (grp) tile_dot<B>(to, S.ov, S.res, wave, lane);
+      if constexpr (LA) {
+        tile_load(tq, A.qkv(ln), wave, lane);
+        tile_load(to, A.o(ln), wave, lane);
+      } else {
+        tile_load(tg, A.gu(l), wave, lane);
       }
-      if constexpr (!LA) tile_load(tg, A.gu(l), wave, lane);
       __syncthreads();
       __syncthreads();  // residual after attention, normalised
-      if (S.abort_) return;
+      if (S.abort_) return false;
       // gate / up
       tile_dot<B>(tg, S.an, S.res, wave, lane);
-      if constexpr (LA) { if (more) tile_load(tg, A.gu(ln), wave, lane); }
+      if constexpr (LA) tile_load(tg, A.gu(ln), wave, lane);
       else tile_load(td, A.down(l), wave, lane);
       __syncthreads();
       __syncthreads();  // SwiGLU slice of the XCD
-      if (S.abort_) return;
+      if (S.abort_) return false;
       // down partial
       tile_dot<B>(td, S.mv, S.res, wave, lane);
-      if constexpr (LA) { if (more) tile_load(td, A.down(ln), wave, lane); }
-      else if (grp && more) tile_load(tq, A.qkv(ln), wave, lane);
+      if constexpr (LA) tile_load(td, A.down(ln), wave, lane);
+      else tile_load(tq, A.qkv(ln), wave, lane);
+      if constexpr (decltype(last)::value) {
+        if (lm) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
+      }
       __syncthreads();
       __syncthreads();  // residual after the MLP, normalised for the next layer or the head
-      if (S.abort_) return;
-    }
-    // LM head rows of this workgroup, 16 rows per pass, best (value, lowest row) per wave
-    if (t >= P.logits_from) {
-      const int rpb = (P.vocab + kGrid - 1) / kGrid;
-      const int row0 = b * rpb, row1 = min(P.vocab, row0 + rpb);
+      ++gc;
+      return S.abort_ == 0;
+    };
+    for (int l = 0; l + 1 < L; ++l)
+      if (!layer(l, std::false_type{})) return;
+    if (!layer(L - 1, std::true_type{})) return;
+
+    // LM head: this workgroup's rows, LMR per pass, two passes in flight
+    if (lm) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-      TLM tl;
-      for (int rb = row0; rb < row1; rb += 16) {
-        const int myrow0 = rb + wave * TLM::RPW;
-        const u4* pp = reinterpret_cast<const u4*>(reinterpret_cast<const uint8_t*>(P.lm_head) +
-                                                    (size_t)rb * B::H * B::WB) + (size_t)wave * TLM::CPW;
-#pragma unroll
-        for (int j = 0; j < TLM::LPL; ++j) {
-          const int k = j * 64 + lane;
-          const int row = myrow0 + k / TLM::CPR;
-          if (k < TLM::CPW && row < row1) tl.v[j] = __builtin_nontemporal_load(pp + k);
-          else tl.v[j] = u4{0, 0, 0, 0};
-        }
-        float acc[TLM::RPW];
-#pragma unroll
-        for (int q = 0; q < TLM::RPW; ++q) acc[q] = 0.f;
-#pragma unroll
-        for (int j = 0; j < TLM::LPL; ++j) {
-          const int k = j * 64 + lane;
-          if (k < TLM::CPW) {
-            const int row = k / TLM::CPR;
-            const float d = dot_chunk<B>(tl.v[j], S.an + (k - row * TLM::CPR) * B::E);
-#pragma unroll
-            for (int q = 0; q < TLM::RPW; ++q) acc[q] += (row == q) ? d : 0.f;
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < TLM::RPW; ++q) {
-          const float v = wave_sum(acc[q]);
-          const int row = myrow0 + q;
-          if (row < row1 && (v > bv || (v == bv && row < bi))) { bv = v; bi = row; }
-        }
+      for (int rb = lm0; rb < lm1; rb += 2 * LMR) {
+        TLM t2;
+        if (rb + LMR < lm1) lm_load<B>(t2, P, rb + LMR, lm1, wave, lane);
+        lm_dot<B>(tl, S.an, rb, lm1, wave, lane, bv, bi);
+        if (rb + LMR >= lm1) break;
+        if (rb + 2 * LMR < lm1) lm_load<B>(tl, P, rb + 2 * LMR, lm1, wave, lane);
+        lm_dot<B>(t2, S.an, rb + LMR, lm1, wave, lane, bv, bi);
       }
       if (lane == 0) { S.wbest_v[wave] = bv; S.wbest_i[wave] = bi; }
       __syncthreads();
@@ -462,27 +695,147 @@ __device__ void worker_loop(const Params& P, Lds<B>& S, int x, int r, int wave, 
   }
 }
 
+// Wait until at most c vector-memory instructions of this wave are pending (c wave-uniform).
+template <int... I>
+__device__ __forceinline__ void wait_vmem_table(int c, std::integer_sequence<int, I...>) {
+  ((c == I ? (wait_vmem<I>(), 0) : 0), ...);
+}
+__device__ __forceinline__ void wait_vmem_rt(int c) {
+  wait_vmem_table(min(c, 63), std::make_integer_sequence<int, 64>{});
+}
+// Chunk-DMA instructions worker wave w issues for a copy of NI instructions.
+__device__ __forceinline__ constexpr int dma_count(int ni, int w) { return (ni - w + kWorkerWaves - 1) / kWorkerWaves; }
+
+// Worker waves with the weight tiles in LDS.  Slot A holds the q/k/v tile, then gate/up;
+// slot B the O tile, then down.  Each tile is copied (LDS DMA, all seven worker waves)
+// as soon as its slot is free, two exchanges before its dot product, and every wave
+// confirms its own copies have landed before the barrier that precedes the dot.
+template <class B>
+__device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* slotA, u4* slotB, int x, int r, int wave,
+                                int lane) {
+  using TQKV = Tile<B, B::T_QKV, B::H>;
+  using TO = Tile<B, B::T_O, B::OC>;
+  using TGU = Tile<B, B::T_GU, B::H>;
+  using TD = Tile<B, B::T_D, B::IX>;
+  using TLM = Tile<B, 2 * kWorkerWaves, B::H>;
+  constexpr int LMR = 2 * kWorkerWaves;
+  constexpr int GCH = kGainFloats(B::H, B::D) * 4 / 16;
+  static_assert(kGainFloats(B::H, B::D) % 4 == 0, "gains block in whole chunks");
+  static_assert(TQKV::TOTAL * 16 <= slot_a_bytes<B>() && TGU::TOTAL * 16 <= slot_a_bytes<B>(), "slot A");
+  static_assert(TO::TOTAL * 16 <= slot_b_bytes<B>() && TD::TOTAL * 16 <= slot_b_bytes<B>(), "slot B");
+  // every copy writes whole 1 KB instructions: destinations must hold them
+  static_assert(slot_a_bytes<B>() % 1024 == 0 && slot_b_bytes<B>() % 1024 == 0, "slots in whole KB");
+  static_assert(sizeof(S.G[0]) >= (size_t)((GCH + 63) / 64) * 1024, "gains buffer in whole KB");
+  constexpr int NI_Q = (TQKV::TOTAL + 63) / 64, NI_O = (TO::TOTAL + 63) / 64, NI_D = (TD::TOTAL + 63) / 64;
+  constexpr int NI_GA = (GCH + 63) / 64;
+  const TileAddr<B> A{P, x, r};
+  const bool grp = B::NG == kXcds || x < B::NG;
+  const int L = P.n_layers;
+  const int b = blockIdx.x;
+  const int rpb = (P.vocab + kGrid - 1) / kGrid;
+  const int lm0 = b * rpb, lm1 = min(P.vocab, lm0 + rpb);
+  __builtin_assume(wave >= 0 && wave < kWorkerWaves);
+
+  int gc = 0;  // layers entered since the launch started; gains of layer gc in G[gc % 2]
+  dma_copy<GCH>(A.gains(0), S.G[0], wave, lane);
+  dma_copy<TQKV::TOTAL>(A.qkv(0), slotA, wave, lane);
+  dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);
+  wait_vmem<0>();
+  TLM tl;
+
+  for (int t = 0; t < P.n_pos; ++t) {
+    const int p = P.pos0 + t;
+    const bool lm = t >= P.logits_from;
+    __syncthreads();  // input fetched
+    if (S.abort_) return;
+    for (int l = 0; l < L; ++l) {
+      const int ln = (l + 1 < L) ? l + 1 : 0;
+      const bool lm_now = lm && l + 1 == L;
+      // q, k, v rows (slot A)
+      if (grp) tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
+      __syncthreads();
+      __syncthreads();  // q rotated, k/v of position p in LDS
+      if (S.abort_) return;
+      // attention over this rank's chunk of positions
+      const int nc = n_chunks(p);
+      const int csz = (p + 1 + nc - 1) / nc;
+      if (grp && r < nc) attention_chunk<B>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane);
+      wait_vmem<0>();  // the O tile (and all earlier copies of this wave) has landed
+      __syncthreads();
+      __syncthreads();  // attention output of the group in LDS
+      if (S.abort_) return;
+      // O partial (slot B); slot A is free: copy the gate/up tile into it
+      dma_copy<TGU::TOTAL>(A.gu(l), slotA, wave, lane);
+      if (grp) tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
+      __syncthreads();
+      dma_copy<TD::TOTAL>(A.down(l), slotB, wave, lane);
+      wait_vmem_rt(dma_count(NI_D, wave));  // gate/up tile landed
+      __syncthreads();  // residual after attention, normalised
+      if (S.abort_) return;
+      // gate / up (slot A)
+      tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
+      __syncthreads();
+      dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
+      dma_copy<TQKV::TOTAL>(A.qkv(ln), slotA, wave, lane);
+      wait_vmem_rt(dma_count(NI_GA, wave) + dma_count(NI_Q, wave));  // down tile landed
+      __syncthreads();  // SwiGLU slice of the XCD
+      if (S.abort_) return;
+      // down partial (slot B)
+      tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
+      if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
+      __syncthreads();
+      if (!lm_now) {
+        dma_copy<TO::TOTAL>(A.o(ln), slotB, wave, lane);
+        wait_vmem_rt(dma_count(NI_O, wave));  // next gains and q/k/v tile landed
+      }
+      __syncthreads();  // residual after the MLP, normalised for the next layer or the head
+      ++gc;
+      if (S.abort_) return;
+    }
+    // LM head: this workgroup's rows, LMR per pass, two passes in flight
+    if (lm) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int rb = lm0; rb < lm1; rb += 2 * LMR) {
+        TLM t2;
+        if (rb + LMR < lm1) lm_load<B>(t2, P, rb + LMR, lm1, wave, lane);
+        lm_dot<B>(tl, S.an, rb, lm1, wave, lane, bv, bi);
+        if (rb + LMR >= lm1) break;
+        if (rb + 2 * LMR < lm1) lm_load<B>(tl, P, rb + 2 * LMR, lm1, wave, lane);
+        lm_dot<B>(t2, S.an, rb + LMR, lm1, wave, lane, bv, bi);
+      }
+      if (lane == 0) { S.wbest_v[wave] = bv; S.wbest_i[wave] = bi; }
+      wait_vmem<0>();  // next gains and q/k/v tile landed
+      dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);
+      __syncthreads();
+    }
+  }
+}
+
 // ------------------------------------------------------------------ control wave
 template <class B>
-__device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane) {
+__device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane) {
   const TileAddr<B> A{P, x, r};
-  const bool grp = x < B::NG;
+  const bool grp = B::NG == kXcds || x < B::NG;
   const int L = P.n_layers;
   const int b = blockIdx.x;
   const uint32_t tpp = tags_per_position(L);
+  const bool trace_phases = P.dbg_phase != nullptr && b == P.dbg_phase_wg;
+  const int n_sync = 2 + 10 * L;  // workgroup barriers per position
+  int cur_t = 0, ph = 0;
   const float eps = P.rms_eps;
   const float qscale = rsqrtf((float)B::D);
   unsigned long long wait_ticks = 0, t_start = 0;
 
   auto fail = [&]() { if (lane == 0) S.abort_ = 1; };
-  auto abort_all = [&]() {
-    raise_error(P, DEV_ERR_TIMEOUT);
-    __hip_atomic_store(P.abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto timed_poll = [&](const u64* src, int n, uint32_t tag, float* dst) {
+  int n_marks = 0;  // gathers completed in the current segment (first two are traced)
+  auto timed_exchange = [&](const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, auto&& publish) {
     const unsigned long long a = wall_clock64();
-    const bool ok = poll_words(src, n, tag, dst, lane, P);
-    wait_ticks += wall_clock64() - a;
+    const bool ok = exchange(src, n, tag, dst, own0, own1, publish, lane, P);
+    const unsigned long long e = wall_clock64();
+    wait_ticks += e - a;
+    if (trace_phases && lane == 0 && n_marks < 2) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 4 + 2 + n_marks] = e;
+    ++n_marks;
     if (!ok) fail();
     return ok;
   };
@@ -502,7 +855,17 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
       for (int k = 0; k < K; ++k)
         if ((pending & (1u << k)) && ((w[k] >> 18) & 0x3fffu) == tag14) pending &= ~(1u << k);
       if (!__any(pending != 0)) break;
-      if (++it >= P.spin_limit) { abort_all(); fail(); return false; }
+      if (++it >= P.spin_limit) {
+        if (pending) {
+          const int k0 = __builtin_ctz(pending);
+          uint32_t seen = 0;
+#pragma unroll
+          for (int k = 0; k < K; ++k) seen = k == k0 ? (uint32_t)((w[k] >> 18) & 0x3fffu) : seen;
+          raise_timeout(P, P.xarg + lane + 64 * k0, tag14, seen);
+        }
+        fail();
+        return false;
+      }
       if ((it & 63) == 0 && ld_coh32(P.abort_flag)) { fail(); return false; }
       __builtin_amdgcn_s_sleep(1);
     }
@@ -529,12 +892,45 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
                          __HIP_MEMORY_SCOPE_SYSTEM);
     }
   };
-  auto sync = [&]() { __syncthreads(); return S.abort_ == 0; };
+  // workgroup barrier; with the phase trace on, this workgroup's arrival and departure times
+  auto sync = [&]() {
+    unsigned long long* rec = P.dbg_phase + ((size_t)cur_t * n_sync + ph) * 4;
+    if (trace_phases && lane == 0) rec[0] = wall_clock64();
+    __syncthreads();
+    if (trace_phases && lane == 0) rec[1] = wall_clock64();
+    ++ph;
+    n_marks = 0;
+    return S.abort_ == 0;
+  };
 
   int pending_lm = -1;  // position whose LM head ran and whose id is not published yet
+  int gc = 0;           // layers entered since the launch started (gains in S.G[gc % 2])
+  // Placement check, once per launch: every workgroup publishes the XCD it runs on.  If
+  // all sit on XCD b % 8, words read only within an XCD may stay in its L2 (plain stores).
+  bool lp = false;
+  {
+    const float* g0 = P.in_norm0;
+#pragma unroll
+    for (int k = 0; k < B::HPL; ++k) S.g_in0[lane + 64 * k] = g0[lane + 64 * k];
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    float* seen = &S.part[0][0][0];
+    if (timed_exchange(P.xplace, kGrid, P.tag0, seen, b, b + 1, [&]() {
+          if (lane == 0) {
+            st_tag(P.xplace + b, __uint_as_float(xcc & 0xfu), P.tag0);
+            seen[b] = __uint_as_float(xcc & 0xfu);
+          }
+        })) {
+      bool ok = true;
+      for (int i = lane; i < kGrid; i += 64) ok &= __float_as_uint(seen[i]) == (uint32_t)(i % kXcds);
+      lp = __all(ok);
+    }
+  }
   for (int t = 0; t < P.n_pos; ++t) {
     const int p = P.pos0 + t;
-    const uint32_t tbase = P.tag0 + (uint32_t)t * tpp;
+    const uint32_t tbase = P.tag0 + 1 + (uint32_t)t * tpp;
+    cur_t = t;
+    ph = 0;
     t_start = wall_clock64();
     wait_ticks = 0;
     // ---------------------------------------------------------------- input of position t
@@ -572,15 +968,19 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
 #pragma unroll
           for (int k = 0; k < B::HPL; ++k) S.xs[lane + 64 * k] = row[lane + 64 * k];
         }
-        if (lane < 3) {
-          int v = P.pos3 ? P.pos3[t * 3 + lane] : p;
-          if (v < 0 || v >= P.rope_positions) {
-            if (lane < P.n_sections) raise_error(P, DEV_ERR_POS);
-            v = 0;
-          }
-          S.streams[lane] = v;
+        if (lane < P.n_sections) {  // a stream outside the rotary table is flagged and read as 0
+          const int v = P.pos3 ? P.pos3[t * 3 + lane] : p;
+          if (v < 0 || v >= P.rope_positions) raise_error(P, DEV_ERR_POS);
         }
-        norm_to<B>(S.xs, A.gain(0, P.lay.in_norm), S.an, eps, lane);
+        // cos/sin of every rotary pair at this position (pair i turns with its section's stream)
+        for (int i = lane; i < B::D / 2; i += 64) {
+          const int sct = i < P.sec_end0 ? 0 : (i < P.sec_end1 ? 1 : 2);
+          int ps = P.pos3 ? P.pos3[t * 3 + sct] : p;
+          ps = (ps < 0 || ps >= P.rope_positions) ? 0 : ps;
+          S.rope_c[i] = P.rope_cos[(size_t)ps * (B::D / 2) + i];
+          S.rope_s[i] = P.rope_sin[(size_t)ps * (B::D / 2) + i];
+        }
+        norm_to<B>(S.xs, S.g_in0, S.an, eps, lane);
         if (P.dbg_hidden && b == 0)
           for (int k = 0; k < B::HPL; ++k)
             P.dbg_hidden[((size_t)t * (L + 1)) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
@@ -594,11 +994,15 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
       if (!sync()) return;
       if (grp) {
         u64* xq = P.xq + (size_t)x * B::RQKV;
-        if (lane < B::T_QKV) st_tag(xq + r * B::T_QKV + lane, S.res[lane], tg0 + 0);
-        if (timed_poll(xq, B::RQKV, tg0 + 0, S.qkv)) {
+        if (timed_exchange(xq, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV, (r + 1) * B::T_QKV, [&]() {
+              if (lane < B::T_QKV) {
+                st_local(xq + r * B::T_QKV + lane, S.res[lane], tg0 + 0, lp);
+                S.qkv[r * B::T_QKV + lane] = S.res[lane];
+              }
+            })) {
           // per-head RMSNorm of q and k, rotation, rounding of the cache entry
-          const float* qn = A.gain(l, P.lay.q_norm);
-          const float* kn = A.gain(l, P.lay.k_norm);
+          const float* qn = S.G[gc & 1] + B::H;
+          const float* kn = S.G[gc & 1] + B::H + B::D;
           for (int h = 0; h <= B::QPG; ++h) {  // h == QPG is k
             float* v = S.qkv + h * B::D;
             const float* g = h < B::QPG ? qn : kn;
@@ -612,10 +1016,8 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
             // LDS accesses of one wave are performed in order: the lane owning pair i
             // sees every lane's normalised value
             for (int i = lane; i < B::D / 2; i += 64) {
-              const int s = i < P.sec_end0 ? 0 : (i < P.sec_end1 ? 1 : 2);
-              const int ps = S.streams[s];
-              const float c = P.rope_cos[(size_t)ps * (B::D / 2) + i];
-              const float sn = P.rope_sin[(size_t)ps * (B::D / 2) + i];
+              const float c = S.rope_c[i];
+              const float sn = S.rope_s[i];
               const float a0 = v[i], a1 = v[i + B::D / 2];
               float o0 = a0 * c - a1 * sn, o1 = a1 * c + a0 * sn;
               if (h < B::QPG) {
@@ -660,31 +1062,47 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
       if (grp) {
         const int nc = n_chunks(p);
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
+        // this rank's chunk partial: the worker waves' partials merged in a fixed order
+        float cM[B::QPG], cL[B::QPG], ca[B::QPG][B::DPL];
         if (r < nc) {
-          // merge the 8 waves' partials, fixed order, into this chunk's partial
+#pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
             float M = -INFINITY;
             for (int w = 0; w < kWorkerWaves; ++w) M = fmaxf(M, S.wpart[w][h][0]);
-            float Ls = 0.f, a[B::DPL];
+            float Ls = 0.f;
 #pragma unroll
-            for (int k = 0; k < B::DPL; ++k) a[k] = 0.f;
+            for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
             for (int w = 0; w < kWorkerWaves; ++w) {
               const float mw = S.wpart[w][h][0];
               const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
               Ls = fmaf(S.wpart[w][h][1], f, Ls);
 #pragma unroll
-              for (int k = 0; k < B::DPL; ++k) a[k] = fmaf(S.wpart[w][h][2 + lane + 64 * k], f, a[k]);
+              for (int k = 0; k < B::DPL; ++k) ca[h][k] = fmaf(S.wpart[w][h][2 + lane + 64 * k], f, ca[h][k]);
             }
-            u64* dst = xa + ((size_t)r * B::QPG + h) * (B::D + 2);
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) st_tag(dst + 2 + lane + 64 * k, a[k], tg0 + 1);
-            if (lane == 0) {
-              st_tag(dst, M, tg0 + 1);
-              st_tag(dst + 1, Ls, tg0 + 1);
-            }
+            cM[h] = M;
+            cL[h] = Ls;
           }
         }
-        if (timed_poll(xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0])) {
+        auto publish_chunk = [&]() {
+          if (r >= nc) return;
+#pragma unroll
+          for (int h = 0; h < B::QPG; ++h) {
+            u64* dst = xa + ((size_t)r * B::QPG + h) * (B::D + 2);
+#pragma unroll
+            for (int k = 0; k < B::DPL; ++k) {
+              st_local(dst + 2 + lane + 64 * k, ca[h][k], tg0 + 1, lp);
+              S.part[r][h][2 + lane + 64 * k] = ca[h][k];
+            }
+            if (lane == 0) {
+              st_local(dst, cM[h], tg0 + 1, lp);
+              st_local(dst + 1, cL[h], tg0 + 1, lp);
+              S.part[r][h][0] = cM[h];
+              S.part[r][h][1] = cL[h];
+            }
+          }
+        };
+        const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
+        if (timed_exchange(xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk)) {
           for (int h = 0; h < B::QPG; ++h) {
             float M = -INFINITY;
             for (int c = 0; c < nc; ++c) M = fmaxf(M, S.part[c][h][0]);
@@ -710,15 +1128,27 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
       {
         // group x's partial of rows [r*T_O, (r+1)*T_O) goes to slot [r][x]: the reader of
         // those rows finds every group's partial in one contiguous run
-        if (grp && lane < B::T_O) st_tag(P.xop + ((size_t)r * B::NG + x) * B::T_O + lane, S.res[lane], tg0 + 2);
-        if (timed_poll(P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, &S.part[0][0][0])) {
+        float* pp = &S.part[0][0][0];
+        if (timed_exchange(P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, pp, grp ? x * B::T_O : 0,
+                           grp ? (x + 1) * B::T_O : 0, [&]() {
+                             if (grp && lane < B::T_O) {
+                               st_tag(P.xop + ((size_t)r * B::NG + x) * B::T_O + lane, S.res[lane], tg0 + 2);
+                               pp[x * B::T_O + lane] = S.res[lane];
+                             }
+                           })) {
+          float nv = 0.f;
           if (lane < B::T_O) {
             float d = 0.f;
-            for (int g = 0; g < B::NG; ++g) d += (&S.part[0][0][0])[g * B::T_O + lane];
-            st_tag(P.xxa + (size_t)x * B::H + r * B::T_O + lane, S.xs[r * B::T_O + lane] + d, tg0 + 3);
+            for (int g = 0; g < B::NG; ++g) d += pp[g * B::T_O + lane];
+            nv = S.xs[r * B::T_O + lane] + d;
           }
-          if (timed_poll(P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs))
-            norm_to<B>(S.xs, A.gain(l, P.lay.post_norm), S.an, eps, lane);
+          if (timed_exchange(P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O, (r + 1) * B::T_O, [&]() {
+                if (lane < B::T_O) {
+                  st_local(P.xxa + (size_t)x * B::H + r * B::T_O + lane, nv, tg0 + 3, lp);
+                  S.xs[r * B::T_O + lane] = nv;
+                }
+              }))
+            norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
         }
       }
       if (!sync()) return;
@@ -726,38 +1156,56 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
       if (!sync()) return;
       {
         constexpr int HALF = B::T_GU / 2;
+        float mm = 0.f;
         if (lane < HALF) {
           const float gt = S.res[lane], up = S.res[HALF + lane];
-          st_tag(P.xm + (size_t)x * B::IX + r * HALF + lane, gt / (1.f + __expf(-gt)) * up, tg0 + 4);
+          mm = gt / (1.f + __expf(-gt)) * up;
         }
-        timed_poll(P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv);
+        timed_exchange(P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF, (r + 1) * HALF, [&]() {
+          if (lane < HALF) {
+            st_local(P.xm + (size_t)x * B::IX + r * HALF + lane, mm, tg0 + 4, lp);
+            S.mv[r * HALF + lane] = mm;
+          }
+        });
       }
       if (!sync()) return;
       // ------------------------------------------------------------ down partials -> residual
       if (!sync()) return;
       {
-        if (lane < B::T_D) st_tag(P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane, S.res[lane], tg0 + 5);
-        if (timed_poll(P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, &S.part[0][0][0])) {
+        float* pp = &S.part[0][0][0];
+        if (timed_exchange(P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, pp, x * B::T_D, (x + 1) * B::T_D,
+                           [&]() {
+                             if (lane < B::T_D) {
+                               st_tag(P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane, S.res[lane], tg0 + 5);
+                               pp[x * B::T_D + lane] = S.res[lane];
+                             }
+                           })) {
+          float nv = 0.f;
           if (lane < B::T_D) {
             float d = 0.f;
-            for (int g = 0; g < kXcds; ++g) d += (&S.part[0][0][0])[g * B::T_D + lane];
-            st_tag(P.xxb + (size_t)x * B::H + r * B::T_D + lane, S.xs[r * B::T_D + lane] + d, tg0 + 6);
+            for (int g = 0; g < kXcds; ++g) d += pp[g * B::T_D + lane];
+            nv = S.xs[r * B::T_D + lane] + d;
           }
-          if (timed_poll(P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs)) {
-            const float* g = (l + 1 < L) ? A.gain(l + 1, P.lay.in_norm) : P.final_norm;
-            norm_to<B>(S.xs, g, S.an, eps, lane);
+          if (timed_exchange(P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D, (r + 1) * B::T_D, [&]() {
+                if (lane < B::T_D) {
+                  st_local(P.xxb + (size_t)x * B::H + r * B::T_D + lane, nv, tg0 + 6, lp);
+                  S.xs[r * B::T_D + lane] = nv;
+                }
+              })) {
+            norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
             if (P.dbg_hidden && b == 0)
               for (int k = 0; k < B::HPL; ++k)
                 P.dbg_hidden[((size_t)t * (L + 1) + l + 1) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
           }
         }
       }
+      ++gc;
       if (!sync()) return;
     }  // layers
 
     // ---------------------------------------------------------------- argmax key of this workgroup
     if (t >= P.logits_from) {
-      __syncthreads();  // workers' per-wave best
+      sync();  // workers' per-wave best
       float bv = -INFINITY;
       int bi = 0x3ffff;
       for (int w = 0; w < kWorkerWaves; ++w) {
@@ -789,16 +1237,33 @@ __device__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane)
 
 template <class B>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) {
-  extern __shared__ __align__(16) uint8_t lds_raw[];
-  Lds<B>& S = *reinterpret_cast<Lds<B>*>(lds_raw);
+  __shared__ __align__(16) u4 slotA[slot_a_bytes<B>() / 16];
+  __shared__ __align__(16) u4 slotB[slot_b_bytes<B>() / 16];
+  __shared__ __align__(16) Lds<B> S;
   const int b = blockIdx.x, x = b % kXcds, r = b / kXcds;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x == 0) S.abort_ = 0;
   if (wave == kWorkerWaves) control_loop<B>(P, S, x, r, lane);
-  else worker_loop<B>(P, S, x, r, wave, lane);
+  else if constexpr (lds_tiles<B>()) worker_loop_lds<B>(P, S, slotA, slotB, x, r, wave, lane);
+  else worker_loop_regs<B>(P, S, x, r, wave, lane);
 }
 
 // ------------------------------------------------------------------ small kernels
+// Self-test of the LDS DMA primitive: the seven worker waves copy n chunks of src into LDS
+// at byte offset off, wait for their copies, and every thread copies LDS back to dst.
+__global__ void __launch_bounds__(kThreads) lds_dma_selftest_kernel(const u4* src, u4* dst, int n, int off) {
+  __shared__ __align__(16) u4 buf[144 * 1024 / 16];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  u4* base = buf + off / 16;
+  if (wave < kWorkerWaves) {
+    const int ni = (n + 63) / 64;
+    for (int i = wave; i < ni; i += kWorkerWaves) lds_dma16(src + min(i * 64 + lane, n - 1), base + i * 64);
+    wait_vmem<0>();
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = base[i];
+}
+
 __global__ void widen_kernel(const void* src, float* dst, int n, int bf16) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) dst[i] = bf16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(src)[i]) : reinterpret_cast<const float*>(src)[i];
@@ -824,21 +1289,34 @@ __global__ void embed_sum_kernel(const void* cb, int n_cb, int cb_size, const vo
   }
 }
 
+// Dynamic LDS added to the kernel's static LDS so that a workgroup takes more than half
+// of a CU's 160 KB: the grid then places exactly one workgroup on each CU.
+template <class B>
+static int lds_padding() {
+  hipFuncAttributes a;
+  if (hipFuncGetAttributes(&a, (const void*)decode_kernel<B>) != hipSuccess) return -1;
+  const int need = 80 * 1024 + 1024 - (int)a.sharedSizeBytes;
+  return need > 0 ? need : 0;
+}
+
 template <class B>
 static int launch_t(const Params& p, void* stream) {
   Params pp = p;
   void* args[] = {&pp};
+  const int pad = lds_padding<B>();
+  if (pad < 0) return -1;
   hipError_t e = hipLaunchCooperativeKernel((const void*)decode_kernel<B>, dim3(kGrid), dim3(kThreads), args,
-                                            kLdsBytes, (hipStream_t)stream);
+                                            (unsigned)pad, (hipStream_t)stream);
   return e == hipSuccess ? 0 : -1;
 }
 
 template <class B>
 static int coop_t(int* blocks) {
-  static_assert(sizeof(Lds<B>) <= (size_t)kLdsBytes, "LDS plan");
-  if (hipFuncSetAttribute((const void*)decode_kernel<B>, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) != hipSuccess)
+  const int pad = lds_padding<B>();
+  if (pad < 0) return -1;
+  if (pad > 0 && hipFuncSetAttribute((const void*)decode_kernel<B>, hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess)
     return -1;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_kernel<B>, kThreads, kLdsBytes) == hipSuccess ? 0 : -1;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_kernel<B>, kThreads, pad) == hipSuccess ? 0 : -1;
 }
 
 int launch_decode(int body, const Params& p, void* stream) {
@@ -864,6 +1342,12 @@ int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* t
   if (n == 0) return 0;
   hipLaunchKernelGGL(embed_sum_kernel, dim3(n), dim3(256), 0, (hipStream_t)stream, codebooks, n_cb, cb_size, text,
                      text_vocab, hidden, bf16, ids, rows, bad);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_lds_dma_selftest(const void* src, void* dst, int n_chunks, int offset_bytes, void* stream) {
+  hipLaunchKernelGGL(lds_dma_selftest_kernel, dim3(1), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u4*)src, (u4*)dst, n_chunks, offset_bytes);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
