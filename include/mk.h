@@ -137,11 +137,13 @@ int mk_position(mk_handle* h, int32_t* pos);
 int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
 
 /* Barrier timeline of one workgroup for the following prefill/decode calls (NULL
- * turns it off): d_phase [n][2 + 10*n_layers][4] uint64 receives, for each position
+ * turns it off): d_phase [n][2 + 10*n_layers][8] uint64 receives, for each position
  * the call runs and each workgroup barrier of that position in program order (input
  * fetch, ten per layer, LM head), the 100 MHz ticks at which workgroup wg's control
  * wave arrived at it and left it, then the ticks at which the first two waits for
- * other workgroups' words in the segment before that barrier completed (0 if none).
+ * other workgroups' words in the segment before that barrier completed, then (first
+ * worker wave) when it had issued its weight copies, finished its dot product and
+ * arrived at the barrier (0 where an event does not occur).
  * MK_ERR_ARG if wg is not in [0, grid). */
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
 

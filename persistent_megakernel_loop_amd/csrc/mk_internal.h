@@ -73,7 +73,7 @@ struct Params {
   unsigned long long* progress;  // host-pinned step counter
   float* dbg_hidden;         // [n_pos][L+1][H] or NULL
   unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL
-  unsigned long long* dbg_phase; // [n_pos][2 + 10 L][4] barrier arrive/leave + 2 wait-done ticks of one workgroup, or NULL
+  unsigned long long* dbg_phase; // [n_pos][2 + 10 L][8] barrier arrive/leave + 2 wait-done ticks of one workgroup, or NULL
   int32_t dbg_phase_wg;
   uint32_t tag0;             // first exchange tag of this launch
   uint32_t lm_seq0;          // argmax key sequence of the first LM head of this launch (14 bits used)

@@ -94,15 +94,39 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f) {
 }
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f(f_to_bf16(f)); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Cross-lane reductions with DPP (data-parallel primitives of the vector ALU) instead of
+// LDS permutes: xor-1 and xor-2 quad permutes, half-row and row mirrors (16-lane sums),
+// then row broadcasts that fold rows 0..3 into lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Sum over each group of 16 lanes, in every lane of the group.
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<kQuadXor1, 0xf>(0.f, v);
+  v += dpp<kQuadXor2, 0xf>(0.f, v);
+  v += dpp<kRowHalfMirror, 0xf>(0.f, v);
+  v += dpp<kRowMirror, 0xf>(0.f, v);
   return v;
 }
+// Sum over the wave, returned to every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = sum16(v);
+  v += dpp<kRowBcast15, 0xa>(0.f, v);  // rows 1, 3 += last lane of rows 0, 2
+  v += dpp<kRowBcast31, 0xc>(0.f, v);  // rows 2, 3 += last lane of row 1
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp<kQuadXor1, 0xf>(v, v));
+  v = fmaxf(v, dpp<kQuadXor2, 0xf>(v, v));
+  v = fmaxf(v, dpp<kRowHalfMirror, 0xf>(v, v));
+  v = fmaxf(v, dpp<kRowMirror, 0xf>(v, v));
+  v = fmaxf(v, dpp<kRowBcast15, 0xa>(v, v));
+  v = fmaxf(v, dpp<kRowBcast31, 0xc>(v, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ u64 tagword(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
@@ -525,8 +549,7 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
         float sc = 0.f;
 #pragma unroll
         for (int e = 0; e < DPC; ++e) sc = fmaf(q[h][e], kf[e], sc);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sc += __shfl_xor(sc, o);  // within the 16-lane group
+        sc = sum16(sc);  // within the 16-lane group of this position
         if (valid) {
           const float mn = fmaxf(m[h], sc);
           const float corr = __expf(m[h] - mn);  // 0 while m is still -inf
@@ -737,6 +760,19 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   __builtin_assume(wave >= 0 && wave < kWorkerWaves);
 
   int gc = 0;  // layers entered since the launch started; gains of layer gc in G[gc % 2]
+  // phase trace: worker wave 0 of the traced workgroup stamps, for the barrier it is about
+  // to reach, when its copies were issued, when its dot product finished and when it arrived
+  const bool trace = P.dbg_phase != nullptr && b == P.dbg_phase_wg && wave == 0 && lane == 0;
+  const int n_sync = 2 + 10 * L;
+  int cur_t = 0, ph = 0;
+  auto mark = [&](int k) {
+    if (trace) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 8 + 4 + k] = wall_clock64();
+  };
+  auto wsync = [&]() {
+    mark(2);
+    __syncthreads();
+    ++ph;
+  };
   dma_copy<GCH>(A.gains(0), S.G[0], wave, lane);
   dma_copy<TQKV::TOTAL>(A.qkv(0), slotA, wave, lane);
   dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);
@@ -746,49 +782,57 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   for (int t = 0; t < P.n_pos; ++t) {
     const int p = P.pos0 + t;
     const bool lm = t >= P.logits_from;
-    __syncthreads();  // input fetched
+    cur_t = t;
+    ph = 0;
+    wsync();  // input fetched
     if (S.abort_) return;
     for (int l = 0; l < L; ++l) {
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const bool lm_now = lm && l + 1 == L;
       // q, k, v rows (slot A)
       if (grp) tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
-      __syncthreads();
-      __syncthreads();  // q rotated, k/v of position p in LDS
+      mark(1);
+      wsync();
+      wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
       // attention over this rank's chunk of positions
       const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
       if (grp && r < nc) attention_chunk<B>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane);
+      mark(1);
       wait_vmem<0>();  // the O tile (and all earlier copies of this wave) has landed
-      __syncthreads();
-      __syncthreads();  // attention output of the group in LDS
+      wsync();
+      wsync();  // attention output of the group in LDS
       if (S.abort_) return;
       // O partial (slot B); slot A is free: copy the gate/up tile into it
       dma_copy<TGU::TOTAL>(A.gu(l), slotA, wave, lane);
+      mark(0);
       if (grp) tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
-      __syncthreads();
+      mark(1);
+      wsync();
       dma_copy<TD::TOTAL>(A.down(l), slotB, wave, lane);
       wait_vmem_rt(dma_count(NI_D, wave));  // gate/up tile landed
-      __syncthreads();  // residual after attention, normalised
+      wsync();  // residual after attention, normalised
       if (S.abort_) return;
       // gate / up (slot A)
       tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
-      __syncthreads();
+      mark(1);
+      wsync();
       dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
       dma_copy<TQKV::TOTAL>(A.qkv(ln), slotA, wave, lane);
       wait_vmem_rt(dma_count(NI_GA, wave) + dma_count(NI_Q, wave));  // down tile landed
-      __syncthreads();  // SwiGLU slice of the XCD
+      wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return;
       // down partial (slot B)
       tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
+      mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
-      __syncthreads();
+      wsync();
       if (!lm_now) {
         dma_copy<TO::TOTAL>(A.o(ln), slotB, wave, lane);
         wait_vmem_rt(dma_count(NI_O, wave));  // next gains and q/k/v tile landed
       }
-      __syncthreads();  // residual after the MLP, normalised for the next layer or the head
+      wsync();  // residual after the MLP, normalised for the next layer or the head
       ++gc;
       if (S.abort_) return;
     }
@@ -807,7 +851,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (lane == 0) { S.wbest_v[wave] = bv; S.wbest_i[wave] = bi; }
       wait_vmem<0>();  // next gains and q/k/v tile landed
       dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);
-      __syncthreads();
+      wsync();
     }
   }
 }
@@ -834,7 +878,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
     const bool ok = exchange(src, n, tag, dst, own0, own1, publish, lane, P);
     const unsigned long long e = wall_clock64();
     wait_ticks += e - a;
-    if (trace_phases && lane == 0 && n_marks < 2) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 4 + 2 + n_marks] = e;
+    if (trace_phases && lane == 0 && n_marks < 2) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 8 + 2 + n_marks] = e;
     ++n_marks;
     if (!ok) fail();
     return ok;
@@ -894,7 +938,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
   };
   // workgroup barrier; with the phase trace on, this workgroup's arrival and departure times
   auto sync = [&]() {
-    unsigned long long* rec = P.dbg_phase + ((size_t)cur_t * n_sync + ph) * 4;
+    unsigned long long* rec = P.dbg_phase + ((size_t)cur_t * n_sync + ph) * 8;
     if (trace_phases && lane == 0) rec[0] = wall_clock64();
     __syncthreads();
     if (trace_phases && lane == 0) rec[1] = wall_clock64();
