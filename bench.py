@@ -73,8 +73,11 @@ def gpu_inputs(shape, n_prompt, n_steps, torch):
                 step_rows=rows[n_prompt:].contiguous(), step_pos3=pos3[n_prompt:].contiguous())
 
 
-def cpu_baseline(shape, n_prompt, budget_s=15.0, max_steps=256):
-    """The oracle (float64 numpy) timed on this host on a bounded sample of the same workload."""
+def cpu_baseline(shape, n_prompt, n_steps, budget_s=12.0):
+    """The oracle (float64 numpy) timed on this host on a bounded sample of the same workload.
+
+    The sample replays the timed workload (prefill untimed, then n_steps decode steps)
+    until about budget_s seconds of decode steps have run; steps/s over those steps."""
     from oracle import Decoder as OracleDecoder
     from oracle import embed_sum17
 
@@ -86,32 +89,122 @@ def cpu_baseline(shape, n_prompt, budget_s=15.0, max_steps=256):
     weights = wl.make_weights(shape)
     dec = OracleDecoder.from_shape(shape, weights)
     kv0 = shape.kv_prefill
-    if kv0:
-        dec.load_kv(wl.make_kv_prefill(shape))
+    kv = wl.make_kv_prefill(shape) if kv0 else None
     if shape.inputs == "talker":
         tables = wl.make_talker_tables(shape.hidden)
-        tids = wl.make_talker_ids(n_prompt + max_steps)
+        tids = wl.make_talker_ids(n_prompt + n_steps)
         rows = np.stack([embed_sum17(tables["codebooks"], tables["text"], t) for t in tids])
-        pos3 = wl.position_streams(kv0, n_prompt + max_steps)
-        if n_prompt:
-            dec.prefill(wl.sentinel_ids(n_prompt), rows[:n_prompt], pos3[:n_prompt])
-        nxt = lambda s: (dec.input_row(-1, rows[n_prompt + s]), pos3[n_prompt + s])  # noqa: E731
-    else:
+        pos3 = wl.position_streams(kv0, n_prompt + n_steps)
+
+    def start():  # untimed: back to the state the timed launch starts from
+        dec.reset()
+        if kv is not None:
+            dec.load_kv(kv)
+        if shape.inputs == "talker":
+            if n_prompt:
+                dec.prefill(wl.sentinel_ids(n_prompt), rows[:n_prompt], pos3[:n_prompt])
+            return None
         first, _, _ = dec.prefill(wl.make_prompt_ids(shape, n_prompt))
-        cur = [first]
-        nxt = lambda s: (dec.input_row(cur[-1]), None)  # noqa: E731
-    t0 = time.perf_counter()
-    done = 0
-    while done < max_steps and time.perf_counter() - t0 < budget_s:
-        x0, p3 = nxt(done)
-        logits, _ = dec.step(x0, p3)
-        if shape.inputs == "ids":
-            cur.append(int(np.argmax(logits.astype(np.float32))))
-        done += 1
-    el = time.perf_counter() - t0
+        return [first]
+
+    el, done, passes = 0.0, 0, 0
+    while el < budget_s:
+        cur = start()
+        passes += 1
+        t0 = time.perf_counter()
+        for s in range(n_steps):
+            if shape.inputs == "talker":
+                logits, _ = dec.step(dec.input_row(-1, rows[n_prompt + s]), pos3[n_prompt + s])
+            else:
+                logits, _ = dec.step(dec.input_row(cur[-1]), None)
+                cur.append(int(np.argmax(logits.astype(np.float32))))
+            done += 1
+            if time.perf_counter() - t0 + el >= budget_s:
+                break
+        el += time.perf_counter() - t0
     return {"value": done / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode steps of {shape.name} (float64 numpy oracle, after a {n_prompt}-position "
-                      f"prefill), {el:.1f} s"}
+            "sample": f"{done} decode steps of {shape.name} ({passes} pass(es) over the {n_steps}-step workload after "
+                      f"an untimed {n_prompt}-position prefill; float64 numpy oracle), {el:.1f} s"}
+
+
+CSRC = os.path.join(ROOT, "persistent_megakernel_loop_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def csrc_digest() -> str:
+    """sha256 over the library's HIP/C++ sources: names the kernel build HBM counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def counters_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"decode_kernel_{workload}_hbm_counters.txt")
+
+
+def load_traffic(workload: str, steps: int):
+    """HBM bytes per decode launch from the committed counter summary, or None when it is
+    absent, was taken for another step count, or the kernel sources changed since."""
+    path = counters_path(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.split()[0] if v.split() else ""
+    if kv.get("steps") != str(steps) or kv.get("csrc_sha256") != csrc_digest():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def _pmc_mean(csv_path: str, prefix: str):
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path)) if r["Kernel_Name"].startswith(prefix)]
+    return (sum(vals) / len(vals), vals) if vals else (None, vals)
+
+
+def hbm_summary(outdir: str, workload: str, steps: int, copy_mib: int) -> str:
+    """Summary text of the four counter passes under outdir (decode launches and a plain copy, FETCH_SIZE
+    and WRITE_SIZE in KiB per dispatch): each decode figure is scaled by known/measured of the copy."""
+    copy_kib = copy_mib * 1024
+    f_dec, f_all = _pmc_mean(os.path.join(outdir, "pmc_FETCH_SIZE", "p_counter_collection.csv"), "void mk::decode_kernel")
+    w_dec, w_all = _pmc_mean(os.path.join(outdir, "pmc_WRITE_SIZE", "p_counter_collection.csv"), "void mk::decode_kernel")
+    f_cp, _ = _pmc_mean(os.path.join(outdir, "pmccopy_FETCH_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    w_cp, _ = _pmc_mean(os.path.join(outdir, "pmccopy_WRITE_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    fs, ws = copy_kib / f_cp, copy_kib / w_cp
+    fetch_b, write_b = f_dec * fs * 1024, w_dec * ws * 1024
+    shape = wl.BY_NAME[workload]
+    algo = step_bytes(shape, shape.kv_prefill + shape.prompt_len, steps)
+    base = "--ttfc-trials 0 --no-cpu-baseline" + ("" if workload == "talker-0.6b" else f" --workload {workload}")
+    if steps != 256:
+        base += f" --steps {steps}"
+    lines = [
+        f"# HBM counters of decode_kernel on {workload}: one launch of {steps} decode steps after the prompt",
+        "# commands (repository root, TMPDIR=/tmp), one counter per pass:",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir}/pmc_FETCH_SIZE -o p --output-format csv -- python3 bench.py {base}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir}/pmc_WRITE_SIZE -o p --output-format csv -- python3 bench.py {base}",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir}/pmccopy_FETCH_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir}/pmccopy_WRITE_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"# summarised by: python3 bench.py --hbm-summary {outdir}" + ("" if workload == "talker-0.6b" else f" --workload {workload}"),
+        f"workload: {workload}",
+        f"steps: {steps}",
+        f"csrc_sha256: {csrc_digest()}",
+        f"decode_fetch_kib_per_dispatch: {f_dec:.0f} (dispatches: {', '.join(f'{v:.0f}' for v in f_all)})",
+        f"decode_write_kib_per_dispatch: {w_dec:.0f} (dispatches: {', '.join(f'{v:.0f}' for v in w_all)})",
+        f"copy_fetch_kib: {f_cp:.0f} for {copy_kib} KiB copied, scale {fs:.4f}",
+        f"copy_write_kib: {w_cp:.0f} for {copy_kib} KiB copied, scale {ws:.4f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"algorithmic_bytes_per_launch: {algo}",
+        f"traffic_over_algorithmic: {(fetch_b + write_b) / algo:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def main():
@@ -122,13 +215,28 @@ def main():
     ap.add_argument("--workload", default="talker-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ttfc-trials", type=int, default=10)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (known bytes for scaling HBM counters) and exit")
+    ap.add_argument("--hbm-summary", metavar="DIR", help="only print the HBM counter summary of the passes under DIR")
     args = ap.parse_args()
+    if args.hbm_summary:
+        sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
                                    "run with --gpus 1"}))
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "copies": 3}), flush=True)
+        return
     from persistent_megakernel_loop_amd.binding import Decoder, to_device, weights_to_device
 
     shape = wl.BY_NAME[args.workload]
@@ -234,14 +342,14 @@ def main():
         "barrier_share": round(share, 4),
         "wall_ms_timed_launch": round(wall_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(shape.name, K),
                      "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(launch_ms, 4)},
     }
     dec.close()
     del inp
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(shape, P)
+        res["cpu_baseline"] = cpu_baseline(shape, P, K)
     print(json.dumps(res), flush=True)
 
 

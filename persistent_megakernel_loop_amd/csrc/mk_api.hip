@@ -210,7 +210,7 @@ int ensure_pinned(mk_handle* h, int32_t n) {
 }
 
 int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const int32_t* pos3, int32_t* out,
-        int logits_from, int feedback) {
+        int logits_from, int feedback, bool prompt) {
   if (n <= 0) return MK_ERR_ARG;
   if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
   if (feedback && !h->have_last) return MK_ERR_STATE;
@@ -267,7 +267,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.tag0 = h->tag;
   P.lm_seq0 = h->lm_seq;
   P.spin_limit = 1u << 22;
-  if (mk::launch_decode(h->body, P, h->stream)) return MK_ERR_HIP;
+  if (mk::launch_decode(h->body, P, prompt, h->stream)) return MK_ERR_HIP;
   h->tag += need;
   h->lm_seq = (h->lm_seq + (uint32_t)(n - logits_from)) & 0x3fffu;
   h->pos += n;
@@ -389,13 +389,13 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
 int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3, int32_t n,
                int32_t* d_out_first) {
   if (!h || !d_ids || n <= 0) return MK_ERR_ARG;
-  return run(h, n, d_ids, d_rows, d_pos3, d_out_first, n - 1, 0);
+  return run(h, n, d_ids, d_rows, d_pos3, d_out_first, n - 1, 0, true);
 }
 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf, const int32_t* d_pos3,
               int32_t* d_out_ids) {
   if (!h || n_steps <= 0 || !d_out_ids) return MK_ERR_ARG;
-  return run(h, n_steps, d_ids, d_embed_buf, d_pos3, d_out_ids, 0, d_ids == nullptr);
+  return run(h, n_steps, d_ids, d_embed_buf, d_pos3, d_out_ids, 0, d_ids == nullptr, false);
 }
 
 int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos) {

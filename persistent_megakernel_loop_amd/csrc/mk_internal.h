@@ -87,7 +87,7 @@ constexpr uint32_t kPhasesPerLayer = 8;
 __host__ __device__ inline uint32_t tags_per_position(int n_layers) { return (uint32_t)n_layers * kPhasesPerLayer + 2; }
 
 // Host-side launcher implemented next to the kernel.
-int launch_decode(int body, const Params& p, void* stream);
+int launch_decode(int body, const Params& p, bool prompt, void* stream);  // prompt: prefill_kernel
 int coop_ok(int body, int* blocks_per_cu);
 int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* text, int text_vocab,
                      int hidden, int bf16, const int32_t* ids, int n, float* rows, int32_t* bad, void* stream);

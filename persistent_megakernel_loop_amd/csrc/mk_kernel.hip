@@ -1280,7 +1280,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 }
 
 template <class B>
-__global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) {
+__device__ __forceinline__ void persistent_body(const Params& P) {
   __shared__ __align__(16) u4 slotA[slot_a_bytes<B>() / 16];
   __shared__ __align__(16) u4 slotB[slot_b_bytes<B>() / 16];
   __shared__ __align__(16) Lds<B> S;
@@ -1291,6 +1291,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) {
   else if constexpr (lds_tiles<B>()) worker_loop_lds<B>(P, S, slotA, slotB, x, r, wave, lane);
   else worker_loop_regs<B>(P, S, x, r, wave, lane);
 }
+
+// The same persistent body under two names, so that a profile tells decode launches
+// (the LM head at every step) from prompt launches (the LM head at the last position).
+template <class B>
+__global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) { persistent_body<B>(P); }
+template <class B>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(Params P) { persistent_body<B>(P); }
 
 // ------------------------------------------------------------------ small kernels
 // Self-test of the LDS DMA primitive: the seven worker waves copy n chunks of src into LDS
@@ -1344,13 +1351,13 @@ static int lds_padding() {
 }
 
 template <class B>
-static int launch_t(const Params& p, void* stream) {
+static int launch_t(const Params& p, bool prompt, void* stream) {
   Params pp = p;
   void* args[] = {&pp};
   const int pad = lds_padding<B>();
   if (pad < 0) return -1;
-  hipError_t e = hipLaunchCooperativeKernel((const void*)decode_kernel<B>, dim3(kGrid), dim3(kThreads), args,
-                                            (unsigned)pad, (hipStream_t)stream);
+  const void* fn = prompt ? (const void*)prefill_kernel<B> : (const void*)decode_kernel<B>;
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(kGrid), dim3(kThreads), args, (unsigned)pad, (hipStream_t)stream);
   return e == hipSuccess ? 0 : -1;
 }
 
@@ -1358,16 +1365,21 @@ template <class B>
 static int coop_t(int* blocks) {
   const int pad = lds_padding<B>();
   if (pad < 0) return -1;
-  if (pad > 0 && hipFuncSetAttribute((const void*)decode_kernel<B>, hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess)
-    return -1;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, decode_kernel<B>, kThreads, pad) == hipSuccess ? 0 : -1;
+  int nb[2] = {0, 0};
+  const void* fns[2] = {(const void*)decode_kernel<B>, (const void*)prefill_kernel<B>};
+  for (int k = 0; k < 2; ++k) {
+    if (pad > 0 && hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb[k], fns[k], kThreads, pad) != hipSuccess) return -1;
+  }
+  *blocks = nb[0] < nb[1] ? nb[0] : nb[1];
+  return 0;
 }
 
-int launch_decode(int body, const Params& p, void* stream) {
+int launch_decode(int body, const Params& p, bool prompt, void* stream) {
   switch (body) {
-    case BODY_TINY: return launch_t<BodyTiny>(p, stream);
-    case BODY_Q06: return launch_t<BodyQ06>(p, stream);
-    case BODY_Q17: return launch_t<BodyQ17>(p, stream);
+    case BODY_TINY: return launch_t<BodyTiny>(p, prompt, stream);
+    case BODY_Q06: return launch_t<BodyQ06>(p, prompt, stream);
+    case BODY_Q17: return launch_t<BodyQ17>(p, prompt, stream);
   }
   return -1;
 }
