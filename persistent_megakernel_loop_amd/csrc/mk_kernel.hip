@@ -20,9 +20,11 @@
 // needs carries the tag of the current phase, so data and readiness travel
 // together and no counter or grid barrier is needed.
 //
-// Workgroup: 8 worker waves hold weight tiles in registers, loaded one layer
-// ahead, and do the dot products; one control wave does every exchange.  Worker
-// loads never sit in front of a poll in the control wave's in-order load counter.
+// Workgroup: 7 worker waves stream this workgroup's weight tiles into two LDS
+// slots with the LDS DMA load, a couple of exchanges before they are needed (the
+// hidden-2048 body keeps them in registers instead, loaded one phase ahead), and
+// do the dot products; one control wave does every exchange, so worker loads never
+// sit in front of a poll in the in-order memory counter of the polling wave.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
