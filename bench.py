@@ -132,12 +132,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def csrc_digest() -> str:
-    """sha256 over the library's HIP/C++ sources: names the kernel build HBM counters were taken on."""
+    """sha256 over the code of the library's HIP/C++ sources (line comments and blank lines
+    dropped): names the kernel build HBM counters were taken on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for n in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, n), "rb") as f:
-            h.update(n.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, n)) as f:
+            code = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
+        h.update(n.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()
 
 
