@@ -179,6 +179,8 @@ int mk_grid_size(mk_handle* h, int32_t* n);
  *   both in dtype (MK_F32 | MK_BF16); d_ids [n][n_codebooks+1] int32;
  *   d_rows [n][hidden] float32 (output).  An id outside its table reads row 0 of
  *   that table and adds one to d_bad[0] (device int32) when d_bad is not NULL.
+ *   n == 0 does nothing (the pointers may then be NULL).  MK_ERR_ARG for a negative
+ *   n, a non-positive size, an unknown dtype or a NULL pointer with n > 0.
  *   Stream-ordered on `stream` (a hipStream_t, NULL = null stream). */
 int mk_embed_sum(const void* d_codebooks, int32_t n_codebooks, int32_t codebook_size,
                  const void* d_text, int32_t text_vocab, int32_t hidden, int32_t dtype,

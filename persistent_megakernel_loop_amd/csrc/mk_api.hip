@@ -484,9 +484,11 @@ int mk_grid_size(mk_handle* h, int32_t* n) {
 int mk_embed_sum(const void* d_codebooks, int32_t n_codebooks, int32_t codebook_size, const void* d_text,
                  int32_t text_vocab, int32_t hidden, int32_t dtype, const int32_t* d_ids, int32_t n, float* d_rows,
                  int32_t* d_bad, void* stream) {
-  if (!d_codebooks || !d_text || !d_ids || !d_rows || n < 0 || n_codebooks <= 0 || codebook_size <= 0 ||
-      text_vocab <= 0 || hidden <= 0 || (dtype != MK_F32 && dtype != MK_BF16))
+  if (n < 0 || n_codebooks <= 0 || codebook_size <= 0 || text_vocab <= 0 || hidden <= 0 ||
+      (dtype != MK_F32 && dtype != MK_BF16))
     return MK_ERR_ARG;
+  if (n == 0) return MK_OK;  // nothing to read or write: the pointers may be NULL
+  if (!d_codebooks || !d_text || !d_ids || !d_rows) return MK_ERR_ARG;
   return mk::launch_embed_sum(d_codebooks, n_codebooks, codebook_size, d_text, text_vocab, hidden,
                               dtype == MK_BF16, d_ids, n, d_rows, d_bad, stream)
              ? MK_ERR_HIP

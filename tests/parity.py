@@ -101,8 +101,13 @@ class OracleRun:
     hidden: np.ndarray       # [P + n][L+1][H]
 
 
-def run_oracle(shape, weights, inp: Inputs, gpu: GpuRun, dtype=np.float64, steps: Optional[int] = None) -> OracleRun:
-    """Teacher-forced replay of the GPU's realised inputs (feedback ids come from the GPU)."""
+def run_oracle(shape, weights, inp: Inputs, gpu: GpuRun, dtype=np.float64, steps: Optional[int] = None,
+               logits_every: int = 1) -> OracleRun:
+    """Teacher-forced replay of the GPU's realised inputs (feedback ids come from the GPU).
+
+    Every position's hidden states are computed; logits only at decode steps s with
+    s % logits_every == 0 and at the last step (rows of NaN elsewhere), since a large
+    LM head dominates the oracle's time."""
     dec = OracleDecoder.from_shape(shape, weights, dtype=dtype)
     if inp.kv is not None:
         dec.load_kv(inp.kv)
@@ -118,9 +123,14 @@ def run_oracle(shape, weights, inp: Inputs, gpu: GpuRun, dtype=np.float64, steps
         ids = np.array(prev[:n], np.int32)
     else:
         ids = inp.step_ids[:n]
-    out, logits, hs = dec.decode(ids, None if inp.step_rows is None else inp.step_rows[:n],
-                                 None if inp.step_pos3 is None else inp.step_pos3[:n])
-    hid.extend(hs)
+    logits = np.full((n, shape.vocab), np.nan)
+    for s in range(n):
+        x0 = dec.input_row(int(ids[s]), None if inp.step_rows is None else inp.step_rows[s])
+        want = s % logits_every == 0 or s == n - 1
+        lg, h = dec.step(x0, None if inp.step_pos3 is None else inp.step_pos3[s], want_logits=want)
+        if want:
+            logits[s] = lg
+        hid.append(h)
     return OracleRun(first, first_logits, logits, np.stack(hid))
 
 
@@ -142,11 +152,15 @@ def compare(gpu: GpuRun, orc: OracleRun, n_steps: Optional[int] = None):
     strict = 0
     if orc.first_logits is not None:
         strict += check_id(gpu.first_id, orc.first_logits, "prefill")
+    checked = 0
     for s in range(n):
+        if np.isnan(orc.logits[s, 0]):
+            continue
         strict += check_id(int(gpu.ids[s]), orc.logits[s], f"step {s}")
+        checked += 1
     npos = orc.hidden.shape[0]
     g, o = gpu.hidden[:npos].astype(np.float64), orc.hidden
     err = np.linalg.norm(g - o, axis=-1) / np.maximum(np.linalg.norm(o, axis=-1), 1e-30)
     worst = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= HIDDEN_RTOL, f"hidden rel-L2 {err.max():.3e} at position {worst[0]} layer {worst[1]}"
-    return {"strict_ids": strict, "max_hidden_rel_l2": float(err.max()), "median_hidden_rel_l2": float(np.median(err))}
+    return {"ids_checked": checked, "strict_ids": strict, "max_hidden_rel_l2": float(err.max()), "median_hidden_rel_l2": float(np.median(err))}

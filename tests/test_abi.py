@@ -191,3 +191,4 @@ def test_selftest_and_embed_sum_argument_checks(lib):
                dict(cbs=0), dict(tv=0), dict(h=0), dict(dt=2)):
         assert call(**kw) == -1, kw
     assert call(n=0) == 0  # nothing to do, nothing launched
+    assert call(n=0, cb=None, tx=None, ids=None, rows=None) == 0

@@ -14,7 +14,8 @@ from tests.parity import compare, make_inputs, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 
-def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=None, random_gains=False):
+def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=None, random_gains=False,
+          logits_every=1):
     from persistent_megakernel_loop_amd.binding import weights_to_device
 
     print(f"[case] {shape.name} L={shape.n_layers} V={shape.vocab} steps={n_steps} prompt={prompt_len} "
@@ -24,7 +25,7 @@ def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=N
     dw = weights_to_device(weights)
     gpu = run_gpu(shape, dw, inp)
     del dw
-    orc = run_oracle(shape, weights, inp, gpu, steps=steps_checked)
+    orc = run_oracle(shape, weights, inp, gpu, steps=steps_checked, logits_every=logits_every)
     summary = compare(gpu, orc)
     print(f"[case] {shape.name}: {summary}", flush=True)
     return gpu, summary
@@ -56,6 +57,12 @@ def test_q06_talker_long_chunks_two_layers():
     _case(shape)
 
 
+def test_q17_talker_two_layers():
+    """The hidden-2048 body (register-resident tiles) on two layers with a short pre-filled cache."""
+    shape = wl.TALKER_1P7B.replace(name="talker-1.7b-2l", n_layers=2, kv_prefill=40, prompt_len=8, steps=8)
+    _case(shape)
+
+
 def test_determinism_bitwise():
     from persistent_megakernel_loop_amd.binding import weights_to_device
 
@@ -70,17 +77,23 @@ def test_determinism_bitwise():
     assert np.array_equal(a.hidden.view(np.uint32), b.hidden.view(np.uint32))
 
 
-@pytest.mark.parametrize("name", ["talker-0.6b"])
-def test_full_talker_0p6b(name):
-    """The 0.6B talker at full size: 32-row prompt and 32 decode steps, every layer compared."""
-    _case(wl.BY_NAME[name], n_steps=32)
+def test_full_talker_0p6b():
+    """The 0.6B talker exactly as the benchmark launches it: 32-row prompt, then ONE
+    launch of 256 decode steps; every step's id and every layer at every position compared."""
+    _case(wl.TALKER_0P6B, n_steps=256)
 
 
 def test_full_text_0p6b():
-    """The Qwen3-0.6B-shaped text decoder (151936-row tied head), 16 prompt ids and 16 greedy steps."""
-    _case(wl.TEXT_0P6B, n_steps=16)
+    """The Qwen3-0.6B-shaped text decoder (151936-row tied head): 16 prompt ids, one launch of
+    64 greedy steps; every layer at every position, ids at every 4th step and the last."""
+    _case(wl.TEXT_0P6B, n_steps=64, logits_every=4)
 
 
 def test_full_talker_long_context():
-    """The talker with 4096 pre-filled positions: 8 decode steps compared."""
-    _case(wl.TALKER_0P6B_LONG, n_steps=8)
+    """The talker with 4096 pre-filled positions: one launch of 48 decode steps."""
+    _case(wl.TALKER_0P6B_LONG, n_steps=48)
+
+
+def test_full_talker_1p7b():
+    """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions: one launch of 12 steps."""
+    _case(wl.TALKER_1P7B, n_steps=12)
