@@ -143,8 +143,11 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
  * wave arrived at it and left it, then the ticks at which the first two waits for
  * other workgroups' words in the segment before that barrier completed, then (first
  * worker wave) when it had issued its weight copies, finished its dot product and
- * arrived at the barrier (0 where an event does not occur).
- * MK_ERR_ARG if wg is not in [0, grid). */
+ * arrived at the barrier, and last, for the first wait of the segment, its poll rounds
+ * (bits 56..63), the ticks of its first round (bits 32..55) and all its ticks (bits
+ * 0..31) (0 where an event does not occur).  wg = -1 traces every
+ * workgroup: d_phase is then [n][grid][2 + 10*n_layers][8].
+ * MK_ERR_ARG if wg is not in [-1, grid). */
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
 
 /* Ids published so far by the most recently enqueued prefill/decode call (0 until

@@ -36,7 +36,7 @@ struct mk_handle {
   void* vcache = nullptr;
   unsigned long long* xbuf = nullptr;
   size_t xbuf_words = 0;
-  unsigned long long *xq, *xatt, *xop, *xxa, *xm, *xdp, *xxb, *xarg, *xplace;
+  unsigned long long *xq, *xatt, *xop, *xxa, *xm, *xdp, *xxb, *xarg, *xplace, *xsink;
   uint32_t* ctl = nullptr;  // [0] err, [1] abort, [2] last id
   // pinned
   unsigned long long* progress = nullptr;
@@ -239,6 +239,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.xq = h->xq; P.xatt = h->xatt; P.xop = h->xop; P.xxa = h->xxa;
   P.xm = h->xm; P.xdp = h->xdp; P.xxb = h->xxb; P.xarg = h->xarg;
   P.xplace = h->xplace;
+  P.xsink = h->xsink;
   P.err = h->ctl;
   P.abort_flag = h->ctl + 1;
   P.last_id = (int32_t*)(h->ctl + 2);
@@ -339,7 +340,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   // exchange buffers
   const size_t QPG = cfg->n_q_heads / cfg->n_kv_heads, IX = cfg->intermediate / mk::kXcds;
   const size_t nq = 8 * (QPG + 2) * D, natt = 8 * mk::kPerXcd * QPG * (D + 2), nh = 8 * H, nm = 8 * IX;
-  h->xbuf_words = nq + natt + 5 * nh + nm + 2 * mk::kGrid + 64 * 9;
+  h->xbuf_words = nq + natt + 5 * nh + nm + 2 * mk::kGrid + 64 * mk::kGrid + 64 * 10;
   if (hipMalloc((void**)&h->xbuf, h->xbuf_words * 8) != hipSuccess ||
       hipMalloc((void**)&h->ctl, 256) != hipSuccess) {
     free_handle(h);
@@ -350,6 +351,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   h->xq = take(nq); h->xatt = take(natt); h->xop = take(nh); h->xxa = take(nh); h->xm = take(nm);
   h->xdp = take(nh); h->xxb = take(nh); h->xarg = take(mk::kGrid);
   h->xplace = take(mk::kGrid);
+  h->xsink = take(64 * mk::kGrid);
   if ((size_t)(p - h->xbuf) > h->xbuf_words) { free_handle(h); return MK_ERR_ARG; }
   if (hipHostMalloc((void**)&h->progress, 64, hipHostMallocCoherent) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
   *(volatile unsigned long long*)h->progress = 0;
@@ -438,7 +440,7 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace) {
 }
 
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg) {
-  if (!h || wg < 0 || wg >= mk::kGrid) return MK_ERR_ARG;
+  if (!h || wg < -1 || wg >= mk::kGrid) return MK_ERR_ARG;
   h->dbg_phase = (unsigned long long*)d_phase;
   h->dbg_phase_wg = wg;
   return MK_OK;

@@ -57,6 +57,7 @@ struct Params {
   unsigned long long* xxb;   // [8][H] residual after the MLP    local hop
   unsigned long long* xarg;  // [grid] argmax keys               cross hop
   unsigned long long* xplace;  // [grid] XCD of every workgroup, once per launch
+  unsigned long long* xsink;   // [grid][64] never read: lanes with nothing to publish store here
   uint32_t* err;             // device error word; err[3..7]: where the first timeout happened
   uint32_t* abort_flag;      // set on timeout: every wait gives up
   int32_t* last_id;          // feedback id carried between launches
@@ -73,8 +74,8 @@ struct Params {
   unsigned long long* progress;  // host-pinned step counter
   float* dbg_hidden;         // [n_pos][L+1][H] or NULL
   unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL
-  unsigned long long* dbg_phase; // [n_pos][2 + 10 L][8] barrier arrive/leave + 2 wait-done ticks of one workgroup, or NULL
-  int32_t dbg_phase_wg;
+  unsigned long long* dbg_phase; // barrier timeline: [n_pos][2 + 10 L][8] of one workgroup, or NULL
+  int32_t dbg_phase_wg;          // the traced workgroup; -1: all, [n_pos][grid][2 + 10 L][8]
   uint32_t tag0;             // first exchange tag of this launch
   uint32_t lm_seq0;          // argmax key sequence of the first LM head of this launch (14 bits used)
   uint32_t call_seq;         // high half of the progress word

@@ -172,56 +172,90 @@ __device__ __forceinline__ void raise_timeout(const Params& P, const unsigned lo
 
 // Control wave: gather words src[0..n) that other workgroups publish, waiting until each
 // carries `tag`, into dst[0..n) (LDS).  Words [own0, own1) are this workgroup's own: the
-// caller writes them to dst itself and they are not read back.  `publish` (the caller's
-// own stores) runs right after the first round of loads is issued, so those loads do not
-// queue behind the stores in the wave's in-order memory counter.  Returns false if the
-// wait gave up (spin limit, or another workgroup's abort).
-constexpr int kPollK = 16;  // words in flight per lane per round
-template <class F>
-__device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, F&& publish, int lane,
-                         const Params& P) {
+// caller writes them to dst itself and they are not read back.
+//
+// Polling is pipelined: two rounds of KP loads per lane are in flight at a time, and a
+// round is consumed while the next one travels.  Every round loads all KP words of a
+// lane (indices clamped into the block), and `publish` (the caller's own stores, issued
+// after the first round) stores unconditionally, so the number of memory operations
+// between a round and its use is fixed and the wait before it covers that round only:
+// not the stores, and not the round behind it.  Returns false if the wait gave up
+// (spin limit, or another workgroup's abort).
+// Loads per lane per poll round for an exchange of at most N words.
+template <int N>
+struct Kp : std::integral_constant<int, (N + 63) / 64 < 8 ? (N + 63) / 64 : 8> {};
+
+template <int KP, class F>
+__device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, F&& publish,
+                                         int lane, const Params& P, uint32_t& rounds, unsigned long long& first_round) {
+  static_assert(KP >= 1 && KP <= 16, "words per lane per round");
   bool published = false;
-  for (int base = 0; base < n; base += 64 * kPollK) {
-    const int cnt = min(n - base, 64 * kPollK);
+  for (int base = 0; base < n; base += 64 * KP) {
+    const int cnt = min(n - base, 64 * KP);
     uint32_t pending = 0;
 #pragma unroll
-    for (int k = 0; k < kPollK; ++k) {
+    for (int k = 0; k < KP; ++k) {
       const int i = base + lane + 64 * k;
       if (lane + 64 * k < cnt && (i < own0 || i >= own1)) pending |= 1u << k;
     }
-    uint32_t it = 0;
-    while (true) {
-      u64 w[kPollK];
+    const u64* s0 = src + base;
+    const int last = cnt - 1;
+    u64 wa[KP], wb[KP];
+    auto issue = [&](u64(&w)[KP]) {
 #pragma unroll
-      for (int k = 0; k < kPollK; ++k)
-        if (pending & (1u << k)) w[k] = ld_coh(src + base + lane + 64 * k);
-      if (!published) {
-        publish();
-        published = true;
-      }
+      for (int k = 0; k < KP; ++k) w[k] = ld_coh(s0 + min(lane + 64 * k, last));
+    };
+    auto absorb = [&](const u64(&w)[KP]) -> bool {
 #pragma unroll
-      for (int k = 0; k < kPollK; ++k)
-        if ((pending & (1u << k)) && (uint32_t)(w[k] >> 32) == tag) {
+      for (int k = 0; k < KP; ++k)
+        if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == tag) {
           dst[base + lane + 64 * k] = __uint_as_float((uint32_t)w[k]);
           pending &= ~(1u << k);
         }
-      if (!__any(pending != 0)) break;
-      if (++it >= P.spin_limit) {
-        if (pending) {  // record the first word still behind (selected without indexing w at run time)
-          const int k0 = __builtin_ctz(pending);
-          uint32_t seen = 0;
+      if (rounds++ == 0) first_round = wall_clock64();
+      return !__any(pending != 0);
+    };
+    auto give_up = [&](const u64(&w)[KP]) {
+      if (pending) {  // record the first word still behind (selected without indexing w at run time)
+        const int k0 = __builtin_ctz(pending);
+        uint32_t seen = 0;
 #pragma unroll
-          for (int k = 0; k < kPollK; ++k) seen = k == k0 ? (uint32_t)(w[k] >> 32) : seen;
-          raise_timeout(P, src + base + lane + 64 * k0, tag, seen);
-        }
+        for (int k = 0; k < KP; ++k) seen = k == k0 ? (uint32_t)(w[k] >> 32) : seen;
+        raise_timeout(P, s0 + lane + 64 * k0, tag, seen);
+      }
+    };
+    issue(wa);
+    if (!published) {
+      publish();
+      published = true;
+    }
+    issue(wb);
+    uint32_t it = 0;
+    while (true) {
+      if (absorb(wa)) break;
+      issue(wa);
+      if (absorb(wb)) break;
+      if (++it >= P.spin_limit) {
+        give_up(wb);
         return false;
       }
       if ((it & 63) == 0 && ld_coh32(P.abort_flag)) return false;
-      __builtin_amdgcn_s_sleep(1);
+      issue(wb);
     }
   }
   if (!published) publish();
   return true;
+}
+
+// Phase trace: one workgroup (dbg_phase_wg >= 0, records [n][n_sync][8]) or every
+// workgroup (dbg_phase_wg < 0, records [n][grid][n_sync][8]).
+__device__ __forceinline__ bool phase_traced(const Params& P, int b) {
+  return P.dbg_phase != nullptr && (P.dbg_phase_wg < 0 || b == P.dbg_phase_wg);
+}
+__device__ __forceinline__ unsigned long long* phase_record(const Params& P, int b, int t, int n_sync, int ph) {
+  const size_t per_t = (size_t)n_sync * (P.dbg_phase_wg < 0 ? kGrid : 1);
+  const size_t wg = P.dbg_phase_wg < 0 ? (size_t)b : 0;
+  return P.dbg_phase + ((size_t)t * per_t + wg * n_sync + ph) * 8;
 }
 
 // ------------------------------------------------------------------ GEMV tiles
@@ -486,13 +520,70 @@ __device__ __forceinline__ void lm_dot(const T& tl, const float* an, int rb, int
 // flight together (device-coherent 128-bit buffer loads).  Every lane group keeps an online
 // softmax over its positions; the four groups are merged at the end.  The current position
 // p is taken from LDS (K rotated and both rounded to cache precision by the control wave).
+// Attention over cache positions [c0, c1) of KV group x at layer l, for the group's
+// query heads: 16 lanes per 256-byte cache row (4 positions per load instruction), UNR
+// load instructions per batch; position p comes from LDS (k/v of this step).
+constexpr int kAttnUnroll = 4;
+constexpr int kCoherent = 16;  // cache-policy bit of a buffer load: device-coherent
+
 template <class B>
+struct KvBatch {
+  u4 k[kAttnUnroll], v[kAttnUnroll];
+};
+
+template <class B>
+struct KvRange {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int w0, w1;  // this wave's positions
+};
+
+template <class B>
+__device__ __forceinline__ KvRange<B> kv_range(const Params& P, int x, int l, int c0, int c1, int wave) {
+  constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
+  const int n = c1 - c0;
+  const int per = (n + kWorkerWaves - 1) / kWorkerWaves;
+  KvRange<B> R;
+  R.w0 = c0 + wave * per;
+  R.w1 = min(c1, R.w0 + per);
+  const size_t row0 = ((size_t)l * B::NKV + x) * P.max_seq;
+  const int nbytes = P.max_seq * ROWB;
+  R.rk = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.kcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
+  R.rv = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.vcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
+  return R;
+}
+
+// Issue the loads of one batch: positions jb + 4u + (lane / 16), clamped into the range
+// (rows past it are loaded again and ignored).  Rows at or past the current position
+// hold data of an earlier step or nothing yet: they are replaced or ignored by the caller.
+template <class B>
+__device__ __forceinline__ void kv_batch_load(const KvRange<B>& R, int jb, int lane, KvBatch<B>& kb) {
+  constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
+  const int sub = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int u = 0; u < kAttnUnroll; ++u) {
+    const int jj = max(min(jb + 4 * u + sub, R.w1 - 1), 0);
+    kb.k[u] = __builtin_amdgcn_raw_buffer_load_b128(R.rk, jj * ROWB + li * 16, 0, kCoherent);
+    kb.v[u] = __builtin_amdgcn_raw_buffer_load_b128(R.rv, jj * ROWB + li * 16, 0, kCoherent);
+  }
+}
+
+// The first batch of a wave's positions, loaded ahead of the attention phase: the cache
+// rows before position p do not depend on this step, so they can be in flight while
+// the q/k/v rows are computed and exchanged.
+template <class B>
+__device__ __forceinline__ void attention_prefetch(const Params& P, int x, int l, int c0, int c1, int wave, int lane,
+                                                   KvBatch<B>& kb) {
+  const KvRange<B> R = kv_range<B>(P, x, l, c0, c1, wave);
+  if (R.w0 < R.w1) kv_batch_load<B>(R, R.w0, lane, kb);
+}
+
+template <class B, bool PREFETCHED>
 __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int x, int l, int p, int c0, int c1,
-                                                int wave, int lane) {
+                                                int wave, int lane, const KvBatch<B>& first) {
   constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
   static_assert(ROWB == 256, "a cache row is 16 lanes x 16 bytes");
   constexpr int DPC = B::BF16 ? 8 : 4;  // head dims per 16-byte chunk
-  constexpr int UNR = 4;                // load instructions (4 positions each) per batch
+  constexpr int UNR = kAttnUnroll;
   const int sub = lane >> 4, li = lane & 15;
   float q[B::QPG][DPC];
 #pragma unroll
@@ -507,24 +598,14 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
 #pragma unroll
     for (int e = 0; e < DPC; ++e) acc[h][e] = 0.f;
   }
-  const int n = c1 - c0;
-  const int per = (n + kWorkerWaves - 1) / kWorkerWaves;
-  const int w0 = c0 + wave * per, w1 = min(c1, w0 + per);
-  const size_t row0 = ((size_t)l * B::NKV + x) * P.max_seq;
-  const int nbytes = P.max_seq * ROWB;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.kcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint8_t*>(P.vcache) + row0 * ROWB, (short)0, nbytes, 0x00020000);
-  constexpr int kCoherent = 16;  // cache-policy bit: device-coherent load
+  const KvRange<B> R = kv_range<B>(P, x, l, c0, c1, wave);
+  const int w0 = R.w0, w1 = R.w1;
   for (int jb = w0; jb < w1; jb += 4 * UNR) {
-    u4 kr[UNR], vr[UNR];
-#pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int jj = min(jb + 4 * u + sub, w1 - 1);
-      kr[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, jj * ROWB + li * 16, 0, kCoherent);
-      vr[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, jj * ROWB + li * 16, 0, kCoherent);
-    }
+    KvBatch<B> kb;
+    if (PREFETCHED && jb == w0) kb = first;
+    else kv_batch_load<B>(R, jb, lane, kb);
+    const u4* kr = kb.k;
+    const u4* vr = kb.v;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int j = jb + 4 * u + sub;
@@ -664,7 +745,7 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       // attention over this rank's chunk of positions
       const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
-      if (grp && r < nc) attention_chunk<B>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane);
+      if (grp && r < nc) attention_chunk<B, false>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane, KvBatch<B>{});
       __syncthreads();
       __syncthreads();  // attention output of the group in LDS
       if (S.abort_) return false;
@@ -764,11 +845,11 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   int gc = 0;  // layers entered since the launch started; gains of layer gc in G[gc % 2]
   // phase trace: worker wave 0 of the traced workgroup stamps, for the barrier it is about
   // to reach, when its copies were issued, when its dot product finished and when it arrived
-  const bool trace = P.dbg_phase != nullptr && b == P.dbg_phase_wg && wave == 0 && lane == 0;
+  const bool trace = phase_traced(P, b) && wave == 0 && lane == 0;
   const int n_sync = 2 + 10 * L;
   int cur_t = 0, ph = 0;
   auto mark = [&](int k) {
-    if (trace) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 8 + 4 + k] = wall_clock64();
+    if (trace) phase_record(P, b, cur_t, n_sync, ph)[4 + k] = wall_clock64();
   };
   auto wsync = [&]() {
     mark(2);
@@ -791,16 +872,21 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
     for (int l = 0; l < L; ++l) {
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const bool lm_now = lm && l + 1 == L;
+      // this rank's chunk of cache positions: its first batch is loaded now
+      const int nc = n_chunks(p);
+      const int csz = (p + 1 + nc - 1) / nc;
+      const bool attn = grp && r < nc;
+      const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
+      KvBatch<B> kb;
+      if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // q, k, v rows (slot A)
       if (grp) tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
-      // attention over this rank's chunk of positions
-      const int nc = n_chunks(p);
-      const int csz = (p + 1 + nc - 1) / nc;
-      if (grp && r < nc) attention_chunk<B>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane);
+      // attention over the chunk
+      if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
       wait_vmem<0>();  // the O tile (and all earlier copies of this wave) has landed
       wsync();
@@ -866,7 +952,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
   const int L = P.n_layers;
   const int b = blockIdx.x;
   const uint32_t tpp = tags_per_position(L);
-  const bool trace_phases = P.dbg_phase != nullptr && b == P.dbg_phase_wg;
+  const bool trace_phases = phase_traced(P, b);
   const int n_sync = 2 + 10 * L;  // workgroup barriers per position
   int cur_t = 0, ph = 0;
   const float eps = P.rms_eps;
@@ -875,12 +961,21 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 
   auto fail = [&]() { if (lane == 0) S.abort_ = 1; };
   int n_marks = 0;  // gathers completed in the current segment (first two are traced)
-  auto timed_exchange = [&](const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, auto&& publish) {
+  // a word every lane may store to when it has nothing to publish: publishing stays branch-free
+  u64* const sink = P.xsink + (size_t)b * 64 + lane;
+  auto timed_exchange = [&](auto kp, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, auto&& publish) {
     const unsigned long long a = wall_clock64();
-    const bool ok = exchange(src, n, tag, dst, own0, own1, publish, lane, P);
+    uint32_t rounds = 0;
+    unsigned long long r1 = a;
+    const bool ok = exchange<decltype(kp)::value>(src, n, tag, dst, own0, own1, publish, lane, P, rounds, r1);
     const unsigned long long e = wall_clock64();
     wait_ticks += e - a;
-    if (trace_phases && lane == 0 && n_marks < 2) P.dbg_phase[((size_t)cur_t * n_sync + ph) * 8 + 2 + n_marks] = e;
+    if (trace_phases && lane == 0 && n_marks < 2) {
+      unsigned long long* rec = phase_record(P, b, cur_t, n_sync, ph);
+      rec[2 + n_marks] = e;
+      // first wait: poll rounds (bits 56..63), ticks of its first round (32..55), all its ticks (0..31)
+      if (n_marks == 0) rec[7] = ((u64)min(rounds, 255u) << 56) | ((u64)min(r1 - a, 0xffffffull) << 32) | (e - a);
+    }
     ++n_marks;
     if (!ok) fail();
     return ok;
@@ -940,7 +1035,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
   };
   // workgroup barrier; with the phase trace on, this workgroup's arrival and departure times
   auto sync = [&]() {
-    unsigned long long* rec = P.dbg_phase + ((size_t)cur_t * n_sync + ph) * 8;
+    unsigned long long* rec = trace_phases ? phase_record(P, b, cur_t, n_sync, ph) : nullptr;
     if (trace_phases && lane == 0) rec[0] = wall_clock64();
     __syncthreads();
     if (trace_phases && lane == 0) rec[1] = wall_clock64();
@@ -961,11 +1056,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     float* seen = &S.part[0][0][0];
-    if (timed_exchange(P.xplace, kGrid, P.tag0, seen, b, b + 1, [&]() {
-          if (lane == 0) {
-            st_tag(P.xplace + b, __uint_as_float(xcc & 0xfu), P.tag0);
-            seen[b] = __uint_as_float(xcc & 0xfu);
-          }
+    if (timed_exchange(Kp<kGrid>{}, P.xplace, kGrid, P.tag0, seen, b, b + 1, [&]() {
+          st_tag(lane == 0 ? P.xplace + b : sink, __uint_as_float(xcc & 0xfu), P.tag0);
+          if (lane == 0) seen[b] = __uint_as_float(xcc & 0xfu);
         })) {
       bool ok = true;
       for (int i = lane; i < kGrid; i += 64) ok &= __float_as_uint(seen[i]) == (uint32_t)(i % kXcds);
@@ -1040,11 +1133,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
       if (!sync()) return;
       if (grp) {
         u64* xq = P.xq + (size_t)x * B::RQKV;
-        if (timed_exchange(xq, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV, (r + 1) * B::T_QKV, [&]() {
-              if (lane < B::T_QKV) {
-                st_local(xq + r * B::T_QKV + lane, S.res[lane], tg0 + 0, lp);
-                S.qkv[r * B::T_QKV + lane] = S.res[lane];
-              }
+        if (timed_exchange(Kp<B::RQKV>{}, xq, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV, (r + 1) * B::T_QKV, [&]() {
+              st_local(lane < B::T_QKV ? xq + r * B::T_QKV + lane : sink, S.res[lane], tg0 + 0, lp);
+              if (lane < B::T_QKV) S.qkv[r * B::T_QKV + lane] = S.res[lane];
             })) {
           // per-head RMSNorm of q and k, rotation, rounding of the cache entry
           const float* qn = S.G[gc & 1] + B::H;
@@ -1110,6 +1201,12 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
         // this rank's chunk partial: the worker waves' partials merged in a fixed order
         float cM[B::QPG], cL[B::QPG], ca[B::QPG][B::DPL];
+#pragma unroll
+        for (int h = 0; h < B::QPG; ++h) {
+          cM[h] = cL[h] = 0.f;
+#pragma unroll
+          for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
+        }
         if (r < nc) {
 #pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
@@ -1129,26 +1226,27 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
             cL[h] = Ls;
           }
         }
-        auto publish_chunk = [&]() {
-          if (r >= nc) return;
+        auto publish_chunk = [&]() {  // ranks without a chunk store to the sink
+          const bool mine = r < nc;
 #pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
-            u64* dst = xa + ((size_t)r * B::QPG + h) * (B::D + 2);
+            u64* dst = xa + ((size_t)(mine ? r : 0) * B::QPG + h) * (B::D + 2);
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) {
-              st_local(dst + 2 + lane + 64 * k, ca[h][k], tg0 + 1, lp);
-              S.part[r][h][2 + lane + 64 * k] = ca[h][k];
+              st_local(mine ? dst + 2 + lane + 64 * k : sink, ca[h][k], tg0 + 1, lp);
+              if (mine) S.part[r][h][2 + lane + 64 * k] = ca[h][k];
             }
-            if (lane == 0) {
-              st_local(dst, cM[h], tg0 + 1, lp);
-              st_local(dst + 1, cL[h], tg0 + 1, lp);
+            st_local(mine && lane == 0 ? dst : sink, cM[h], tg0 + 1, lp);
+            st_local(mine && lane == 0 ? dst + 1 : sink, cL[h], tg0 + 1, lp);
+            if (mine && lane == 0) {
               S.part[r][h][0] = cM[h];
               S.part[r][h][1] = cL[h];
             }
           }
         };
         const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
-        if (timed_exchange(xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk)) {
+        if (timed_exchange(Kp<kPerXcd * B::QPG * (B::D + 2)>{}, xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+                           own0, own1, publish_chunk)) {
           for (int h = 0; h < B::QPG; ++h) {
             float M = -INFINITY;
             for (int c = 0; c < nc; ++c) M = fmaxf(M, S.part[c][h][0]);
@@ -1175,12 +1273,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
         // group x's partial of rows [r*T_O, (r+1)*T_O) goes to slot [r][x]: the reader of
         // those rows finds every group's partial in one contiguous run
         float* pp = &S.part[0][0][0];
-        if (timed_exchange(P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, pp, grp ? x * B::T_O : 0,
-                           grp ? (x + 1) * B::T_O : 0, [&]() {
-                             if (grp && lane < B::T_O) {
-                               st_tag(P.xop + ((size_t)r * B::NG + x) * B::T_O + lane, S.res[lane], tg0 + 2);
-                               pp[x * B::T_O + lane] = S.res[lane];
-                             }
+        if (timed_exchange(Kp<B::NG * B::T_O>{}, P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, pp,
+                           grp ? x * B::T_O : 0, grp ? (x + 1) * B::T_O : 0, [&]() {
+                             const bool mine = grp && lane < B::T_O;
+                             st_tag(mine ? P.xop + ((size_t)r * B::NG + x) * B::T_O + lane : sink, S.res[lane], tg0 + 2);
+                             if (mine) pp[x * B::T_O + lane] = S.res[lane];
                            })) {
           float nv = 0.f;
           if (lane < B::T_O) {
@@ -1188,11 +1285,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
             for (int g = 0; g < B::NG; ++g) d += pp[g * B::T_O + lane];
             nv = S.xs[r * B::T_O + lane] + d;
           }
-          if (timed_exchange(P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O, (r + 1) * B::T_O, [&]() {
-                if (lane < B::T_O) {
-                  st_local(P.xxa + (size_t)x * B::H + r * B::T_O + lane, nv, tg0 + 3, lp);
-                  S.xs[r * B::T_O + lane] = nv;
-                }
+          if (timed_exchange(Kp<B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O, (r + 1) * B::T_O, [&]() {
+                st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
+                if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
               }))
             norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
         }
@@ -1207,11 +1302,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           const float gt = S.res[lane], up = S.res[HALF + lane];
           mm = gt / (1.f + __expf(-gt)) * up;
         }
-        timed_exchange(P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF, (r + 1) * HALF, [&]() {
-          if (lane < HALF) {
-            st_local(P.xm + (size_t)x * B::IX + r * HALF + lane, mm, tg0 + 4, lp);
-            S.mv[r * HALF + lane] = mm;
-          }
+        timed_exchange(Kp<B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF, (r + 1) * HALF, [&]() {
+          st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm, tg0 + 4, lp);
+          if (lane < HALF) S.mv[r * HALF + lane] = mm;
         });
       }
       if (!sync()) return;
@@ -1219,12 +1312,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
       if (!sync()) return;
       {
         float* pp = &S.part[0][0][0];
-        if (timed_exchange(P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, pp, x * B::T_D, (x + 1) * B::T_D,
-                           [&]() {
-                             if (lane < B::T_D) {
-                               st_tag(P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane, S.res[lane], tg0 + 5);
-                               pp[x * B::T_D + lane] = S.res[lane];
-                             }
+        if (timed_exchange(Kp<kXcds * B::T_D>{}, P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, pp,
+                           x * B::T_D, (x + 1) * B::T_D, [&]() {
+                             st_tag(lane < B::T_D ? P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane : sink, S.res[lane],
+                                    tg0 + 5);
+                             if (lane < B::T_D) pp[x * B::T_D + lane] = S.res[lane];
                            })) {
           float nv = 0.f;
           if (lane < B::T_D) {
@@ -1232,11 +1324,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
             for (int g = 0; g < kXcds; ++g) d += pp[g * B::T_D + lane];
             nv = S.xs[r * B::T_D + lane] + d;
           }
-          if (timed_exchange(P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D, (r + 1) * B::T_D, [&]() {
-                if (lane < B::T_D) {
-                  st_local(P.xxb + (size_t)x * B::H + r * B::T_D + lane, nv, tg0 + 6, lp);
-                  S.xs[r * B::T_D + lane] = nv;
-                }
+          if (timed_exchange(Kp<B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D, (r + 1) * B::T_D, [&]() {
+                st_local(lane < B::T_D ? P.xxb + (size_t)x * B::H + r * B::T_D + lane : sink, nv, tg0 + 6, lp);
+                if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
               })) {
             norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
             if (P.dbg_hidden && b == 0)
