@@ -131,6 +131,16 @@ __device__ __forceinline__ float wave_max(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Value of lane ^ 16 and of lane ^ 32, through the row-swap instructions (no LDS).
+__device__ __forceinline__ float xor16(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(((lane >> 4) & 1) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(lane >= 32 ? r[0] : r[1]);
+}
+
 __device__ __forceinline__ u64 tagword(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 // Cross-XCD words are written through to the device coherence point.
 __device__ __forceinline__ void st_tag(u64* p, float v, uint32_t tag) {
@@ -361,25 +371,165 @@ __device__ __forceinline__ void tile_dot_lds(const u4* slot, const float* act, f
   }
 }
 
+// ------------------------------------------------------------------ bf16 GEMV with split inputs
+// An fp32 input v is carried as two bf16 values, hi = bf16(v) and lo = bf16(v - hi)
+// (rounded to nearest even), so hi + lo keeps 16 significant bits; a weight pair times an
+// input pair is then one packed dot-product instruction (bf16 products, fp32 sum), two per
+// weight pair for hi and lo instead of a conversion and a multiply-add per weight.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// 8 consecutive inputs -> hi and lo chunks
+__device__ __forceinline__ void split8(const float* v, u4& hi, u4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = v[2 * e], b = v[2 * e + 1];
+    h[e] = pack_bf16(a, b);
+    l[e] = pack_bf16(a - bf16lo(h[e]), b - bf16hi(h[e]));
+  }
+  hi = u4{h[0], h[1], h[2], h[3]};
+  lo = u4{l[0], l[1], l[2], l[3]};
+}
+// Control wave: split n inputs (n % 8 == 0) for the next GEMV.
+template <int N>
+__device__ __forceinline__ void split_act(const float* v, u4* hi, u4* lo, int lane) {
+  static_assert(N % 8 == 0, "whole chunks");
+#pragma unroll
+  for (int c0 = 0; c0 < N / 8; c0 += 64) {
+    const int c = c0 + lane;
+    if (c < N / 8) split8(v + 8 * c, hi[c], lo[c]);
+  }
+}
+// (through a copy: a bit cast applied directly to a vector element has been seen to read
+// element 0 instead)
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t u) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf2(w), as_bf2(a), acc, false);
+}
+__device__ __forceinline__ float dot8(const u4& w, const u4& hi, const u4& lo, float acc) {
+  acc = dot2(w.x, hi.x, acc);
+  acc = dot2(w.y, hi.y, acc);
+  acc = dot2(w.z, hi.z, acc);
+  acc = dot2(w.w, hi.w, acc);
+  acc = dot2(w.x, lo.x, acc);
+  acc = dot2(w.y, lo.y, acc);
+  acc = dot2(w.z, lo.z, acc);
+  acc = dot2(w.w, lo.w, acc);
+  return acc;
+}
+
+// Sum over groups of G consecutive lanes (G a power of two up to 32); the total sits in
+// the group's last lane.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<kQuadXor1, 0xf>(0.f, v);
+  if constexpr (G >= 4) v += dpp<kQuadXor2, 0xf>(0.f, v);
+  if constexpr (G >= 8) v += dpp<kRowHalfMirror, 0xf>(0.f, v);
+  if constexpr (G >= 16) v += dpp<kRowMirror, 0xf>(0.f, v);
+  if constexpr (G >= 32) v += dpp<kRowBcast15, 0xa>(0.f, v);
+  return v;
+}
+
+// A GEMV tile of ROWS rows x COLS bf16 weights in LDS (chunk g at slot[g], row-major).
+// Worker wave w takes rows [w*RPW, w*RPW + RPW); the row loop has a fixed trip count and
+// no branches (rows past the tile re-read the last row and are not stored), so the rows'
+// loads, products and reductions interleave.  A row of CPR < 64 chunks (CPR dividing 64)
+// is one group of CPR lanes, 64/CPR rows per pass; a longer row takes ceil(CPR/64) passes
+// over the wave's lanes.
+template <int ROWS, int COLS>
+struct Gemv2 {
+  static constexpr int CPR = COLS / 8;
+  static constexpr int RPW = (ROWS + kWorkerWaves - 1) / kWorkerWaves;
+  static constexpr bool GROUPED = CPR < 64 && 64 % CPR == 0;
+  static constexpr int RPI = GROUPED ? 64 / CPR : 1;  // rows per pass
+  static constexpr int NPASS = (RPW + RPI - 1) / RPI;
+  static constexpr int NIT = GROUPED ? 1 : (CPR + 63) / 64;
+  static_assert(COLS % 8 == 0 && ROWS <= 64, "tile");
+};
+
+template <int ROWS, int COLS>
+__device__ __forceinline__ void tile_dot2(const u4* slot, const u4* ahi, const u4* alo, float* res, int wave, int lane) {
+  using G = Gemv2<ROWS, COLS>;
+  constexpr int CPR = G::CPR;
+  const int r0 = wave * G::RPW;
+  if (r0 >= ROWS) return;
+  if constexpr (G::GROUPED) {
+    const int lr = lane / CPR, c = lane % CPR;
+    const u4 hi = ahi[c], lo = alo[c];
+    float d[G::NPASS];
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) {
+      const int row = min(r0 + i * G::RPI + lr, ROWS - 1);
+      d[i] = dot8(slot[row * CPR + c], hi, lo, 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) d[i] = group_sum<CPR>(d[i]);
+#pragma unroll
+    for (int i = 0; i < G::NPASS; ++i) {
+      const int j = i * G::RPI + lr, row = r0 + j;
+      if (c == CPR - 1 && j < G::RPW && row < ROWS) res[row] = d[i];
+    }
+  } else {
+    u4 hi[G::NIT], lo[G::NIT];
+#pragma unroll
+    for (int i = 0; i < G::NIT; ++i) {
+      const int c = min(lane + 64 * i, CPR - 1);
+      hi[i] = ahi[c];
+      lo[i] = alo[c];
+    }
+    float d[G::RPW];
+#pragma unroll
+    for (int j = 0; j < G::RPW; ++j) {
+      const int row = min(r0 + j, ROWS - 1);
+      d[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < G::NIT; ++i) {
+        const int c = lane + 64 * i;
+        const u4 w = slot[row * CPR + min(c, CPR - 1)];
+        if (CPR % 64 == 0 || c < CPR) d[j] = dot8(w, hi[i], lo[i], d[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G::RPW; ++j) d[j] = wave_sum(d[j]);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < G::RPW; ++j)
+        if (r0 + j < ROWS) res[r0 + j] = d[j];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ the kernel
 template <class B>
 struct Lds {
-  float xs[B::H];            // residual stream (every workgroup holds all of it)
-  float an[B::H];            // normalised input of the next GEMV
-  float qkv[B::RQKV];        // raw q,k,v of this XCD's group, then q rotated and scaled
+  alignas(16) float xs[B::H];            // residual stream (every workgroup holds all of it)
+  alignas(16) float an[B::H];            // normalised input of the next GEMV
+  alignas(16) float qkv[B::RQKV];        // raw q,k,v of this XCD's group, then q rotated and scaled
   float kp[B::D], vp[B::D];  // K and V of the current position (cache precision)
-  float ov[B::OC];           // attention output of the group
-  float mv[B::IX];           // SwiGLU output slice
-  float res[64];             // row results of the current tile
-  float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
-  float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
+  alignas(16) float ov[B::OC];           // attention output of the group
+  alignas(16) float mv[B::IX];           // SwiGLU output slice
+  alignas(16) float res[64];             // row results of the current tile
+  // bf16 bodies: GEMV inputs as bf16 pairs, hi = bf16(v) and lo = bf16(v - hi), 8 values per u4
+  u4 an_hi[B::H / 8], an_lo[B::H / 8];
+  u4 ov_hi[B::OC / 8], ov_lo[B::OC / 8];
+  u4 mv_hi[B::IX / 8], mv_lo[B::IX / 8];
+  alignas(16) float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
+  alignas(16) float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
   float wbest_v[kWorkerWaves];
   int wbest_i[kWorkerWaves];
-  float g_in0[B::H];         // input norm of layer 0 (constant for the launch)
+  alignas(16) float g_in0[B::H];         // input norm of layer 0 (constant for the launch)
   // gains of layer j in G[j % 2] (j counted from the launch start), filled by the workers
   // ahead of use: [post-attention norm H][q norm D][k norm D][input norm of the next layer H],
   // each buffer padded to whole KB because an LDS copy instruction always writes 1 KB
-  float G[2][(2 * B::H + 2 * B::D + 255) / 256 * 256];
+  alignas(16) float G[2][(2 * B::H + 2 * B::D + 255) / 256 * 256];
   float rope_c[B::D / 2], rope_s[B::D / 2];  // cos/sin of every rotary pair at this position
   int abort_;
 };
@@ -393,6 +543,50 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 // of chunk_len positions; chunk r goes to rank r of the group's XCD.
 constexpr int kMinChunk = 32;
 __device__ __forceinline__ int n_chunks(int p) { return min(kPerXcd, max(1, (p + 1 + kMinChunk - 1) / kMinChunk)); }
+
+// RMSNorm of x with gains g into out (fp32) and, for the bf16 GEMVs, into split hi/lo
+// chunks; each lane works on whole 8-element chunks (16-byte LDS accesses).
+template <class B>
+__device__ __forceinline__ void norm_split(const float* x, const float* g, float* out, u4* hi, u4* lo, float eps, int lane) {
+  constexpr int NCH = B::H / 8, CPL = (NCH + 63) / 64;
+  f4 v[CPL][2];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = min(lane + 64 * i, NCH - 1);
+    v[i][0] = *reinterpret_cast<const f4*>(x + 8 * c);
+    v[i][1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+    if (NCH % 64 == 0 || lane + 64 * i < NCH) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        ss = fmaf(v[i][e].x, v[i][e].x, ss);
+        ss = fmaf(v[i][e].y, v[i][e].y, ss);
+        ss = fmaf(v[i][e].z, v[i][e].z, ss);
+        ss = fmaf(v[i][e].w, v[i][e].w, ss);
+      }
+    }
+  }
+  ss = wave_sum(ss);
+  const float rs = rsqrtf(ss / (float)B::H + eps);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (NCH % 64 == 0 || c < NCH) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const f4 gg = *reinterpret_cast<const f4*>(g + 8 * c + 4 * e);
+        y[4 * e + 0] = gg.x * (v[i][e].x * rs);
+        y[4 * e + 1] = gg.y * (v[i][e].y * rs);
+        y[4 * e + 2] = gg.z * (v[i][e].z * rs);
+        y[4 * e + 3] = gg.w * (v[i][e].w * rs);
+      }
+      *reinterpret_cast<f4*>(out + 8 * c) = f4{y[0], y[1], y[2], y[3]};
+      *reinterpret_cast<f4*>(out + 8 * c + 4) = f4{y[4], y[5], y[6], y[7]};
+      split8(y, hi[c], lo[c]);
+    }
+  }
+}
 
 template <class B>
 __device__ __forceinline__ void norm_to(const float* x, const float* g, float* out, float eps, int lane) {
@@ -608,6 +802,7 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
     const u4* vr = kb.v;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
+      if (jb + 4 * u >= w1) break;  // no position of the wave left in this load group
       const int j = jb + 4 * u + sub;
       float kf[DPC], vf[DPC];
       if (j == p) {
@@ -645,19 +840,20 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
       }
     }
   }
-  // merge the four position groups of the wave (lanes xor 16, xor 32)
+  // merge the four position groups of the wave (lanes xor 16, then xor 32; row swaps)
+  auto other = [&](float v, int o) { return o == 16 ? xor16(v, lane) : xor32(v, lane); };
 #pragma unroll
   for (int o = 16; o < 64; o <<= 1) {
 #pragma unroll
     for (int h = 0; h < B::QPG; ++h) {
-      const float mo = __shfl_xor(m[h], o), lo = __shfl_xor(ls[h], o);
+      const float mo = other(m[h], o), lo = other(ls[h], o);
       const float M = fmaxf(m[h], mo);
       const float fa = m[h] == -INFINITY ? 0.f : __expf(m[h] - M);
       const float fb = mo == -INFINITY ? 0.f : __expf(mo - M);
       ls[h] = ls[h] * fa + lo * fb;
 #pragma unroll
       for (int e = 0; e < DPC; ++e) {
-        const float ao = __shfl_xor(acc[h][e], o);
+        const float ao = other(acc[h][e], o);
         acc[h][e] = acc[h][e] * fa + ao * fb;
       }
       m[h] = M;
@@ -833,7 +1029,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   static_assert(slot_a_bytes<B>() % 1024 == 0 && slot_b_bytes<B>() % 1024 == 0, "slots in whole KB");
   static_assert(sizeof(S.G[0]) >= (size_t)((GCH + 63) / 64) * 1024, "gains buffer in whole KB");
   constexpr int NI_Q = (TQKV::TOTAL + 63) / 64, NI_O = (TO::TOTAL + 63) / 64, NI_D = (TD::TOTAL + 63) / 64;
-  constexpr int NI_GA = (GCH + 63) / 64;
+  constexpr int NI_GA = (GCH + 63) / 64, NI_GU = (TGU::TOTAL + 63) / 64;
   const TileAddr<B> A{P, x, r};
   const bool grp = B::NG == kXcds || x < B::NG;
   const int L = P.n_layers;
@@ -880,7 +1076,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       KvBatch<B> kb;
       if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // q, k, v rows (slot A)
-      if (grp) tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
+      if (grp) {
+        if constexpr (B::BF16) tile_dot2<B::T_QKV, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
+        else tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
+      }
       mark(1);
       wsync();
       wsync();  // q rotated, k/v of position p in LDS
@@ -888,14 +1087,19 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       // attention over the chunk
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
-      wait_vmem<0>();  // the O tile (and all earlier copies of this wave) has landed
+      // slot A is free since the q/k/v dot: the gate/up tile streams in while the chunk
+      // partials are combined (that wait is mostly for the slowest chunk anyway)
+      dma_copy<TGU::TOTAL>(A.gu(l), slotA, wave, lane);
+      mark(0);
+      wait_vmem_rt(dma_count(NI_GU, wave));  // the O tile (and every copy before the gate/up one) has landed
       wsync();
       wsync();  // attention output of the group in LDS
       if (S.abort_) return;
-      // O partial (slot B); slot A is free: copy the gate/up tile into it
-      dma_copy<TGU::TOTAL>(A.gu(l), slotA, wave, lane);
-      mark(0);
-      if (grp) tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
+      // O partial (slot B)
+      if (grp) {
+        if constexpr (B::BF16) tile_dot2<B::T_O, B::OC>(slotB, S.ov_hi, S.ov_lo, S.res, wave, lane);
+        else tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
+      }
       mark(1);
       wsync();
       dma_copy<TD::TOTAL>(A.down(l), slotB, wave, lane);
@@ -903,7 +1107,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();  // residual after attention, normalised
       if (S.abort_) return;
       // gate / up (slot A)
-      tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_GU, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
+      else tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
       dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
@@ -912,7 +1117,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return;
       // down partial (slot B)
-      tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_D, B::IX>(slotB, S.mv_hi, S.mv_lo, S.res, wave, lane);
+      else tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
       mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
       wsync();
@@ -1119,7 +1325,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           S.rope_c[i] = P.rope_cos[(size_t)ps * (B::D / 2) + i];
           S.rope_s[i] = P.rope_sin[(size_t)ps * (B::D / 2) + i];
         }
-        norm_to<B>(S.xs, S.g_in0, S.an, eps, lane);
+        if constexpr (B::BF16) norm_split<B>(S.xs, S.g_in0, S.an, S.an_hi, S.an_lo, eps, lane);
+        else norm_to<B>(S.xs, S.g_in0, S.an, eps, lane);
         if (P.dbg_hidden && b == 0)
           for (int k = 0; k < B::HPL; ++k)
             P.dbg_hidden[((size_t)t * (L + 1)) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
@@ -1140,7 +1347,38 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           // per-head RMSNorm of q and k, rotation, rounding of the cache entry
           const float* qn = S.G[gc & 1] + B::H;
           const float* kn = S.G[gc & 1] + B::H + B::D;
-          for (int h = 0; h <= B::QPG; ++h) {  // h == QPG is k
+          if constexpr (B::D == 128) {
+            // lane i holds elements i and i + 64 of every head, which are rotary pair i:
+            // norm and rotation stay in registers, the q heads and k side by side
+            const float c = S.rope_c[lane], sn = S.rope_s[lane];
+            float a0[B::QPG + 1], a1[B::QPG + 1], ss[B::QPG + 1];
+#pragma unroll
+            for (int h = 0; h <= B::QPG; ++h) {
+              a0[h] = S.qkv[h * B::D + lane];
+              a1[h] = S.qkv[h * B::D + lane + 64];
+              ss[h] = fmaf(a1[h], a1[h], a0[h] * a0[h]);
+            }
+#pragma unroll
+            for (int h = 0; h <= B::QPG; ++h) ss[h] = wave_sum(ss[h]);
+            const float vv0 = S.qkv[(B::QPG + 1) * B::D + lane], vv1 = S.qkv[(B::QPG + 1) * B::D + lane + 64];
+#pragma unroll
+            for (int h = 0; h <= B::QPG; ++h) {
+              const float* g = h < B::QPG ? qn : kn;
+              const float rs = rsqrtf(ss[h] / (float)B::D + eps);
+              const float n0 = g[lane] * (a0[h] * rs), n1 = g[lane + 64] * (a1[h] * rs);
+              float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
+              if (h < B::QPG) {
+                S.qkv[h * B::D + lane] = o0 * qscale;
+                S.qkv[h * B::D + lane + 64] = o1 * qscale;
+              } else {
+                if (P.kv_bf16) { o0 = bf16_round(o0); o1 = bf16_round(o1); }
+                S.kp[lane] = o0;
+                S.kp[lane + 64] = o1;
+              }
+            }
+            S.vp[lane] = P.kv_bf16 ? bf16_round(vv0) : vv0;
+            S.vp[lane + 64] = P.kv_bf16 ? bf16_round(vv1) : vv1;
+          } else for (int h = 0; h <= B::QPG; ++h) {  // h == QPG is k
             float* v = S.qkv + h * B::D;
             const float* g = h < B::QPG ? qn : kn;
             float ss = 0.f;
@@ -1167,11 +1405,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
               }
             }
           }
+          if constexpr (B::D != 128) {
 #pragma unroll
-          for (int k = 0; k < B::DPL; ++k) {
-            const int i = lane + 64 * k;
-            const float v = S.qkv[(B::QPG + 1) * B::D + i];
-            S.vp[i] = P.kv_bf16 ? bf16_round(v) : v;
+            for (int k = 0; k < B::DPL; ++k) {
+              const int i = lane + 64 * k;
+              const float v = S.qkv[(B::QPG + 1) * B::D + i];
+              S.vp[i] = P.kv_bf16 ? bf16_round(v) : v;
+            }
           }
           if (r == 0) {  // the group's cache entry at position p
             const size_t off = (((size_t)l * B::NKV + x) * P.max_seq + p) * B::D;
@@ -1264,6 +1504,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) S.ov[h * B::D + lane + 64 * k] = a[k] * inv;
           }
+          if constexpr (B::BF16) split_act<B::OC>(S.ov, S.ov_hi, S.ov_lo, lane);
         }
       }
       if (!sync()) return;
@@ -1289,7 +1530,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
                 st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
                 if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
               }))
-            norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
+          {
+            if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1], S.an, S.an_hi, S.an_lo, eps, lane);
+            else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
+          }
         }
       }
       if (!sync()) return;
@@ -1306,6 +1550,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm, tg0 + 4, lp);
           if (lane < HALF) S.mv[r * HALF + lane] = mm;
         });
+        if constexpr (B::BF16) split_act<B::IX>(S.mv, S.mv_hi, S.mv_lo, lane);
       }
       if (!sync()) return;
       // ------------------------------------------------------------ down partials -> residual
@@ -1328,7 +1573,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
                 st_local(lane < B::T_D ? P.xxb + (size_t)x * B::H + r * B::T_D + lane : sink, nv, tg0 + 6, lp);
                 if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
               })) {
-            norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
+            if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, S.an_hi, S.an_lo, eps, lane);
+            else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
             if (P.dbg_hidden && b == 0)
               for (int k = 0; k < B::HPL; ++k)
                 P.dbg_hidden[((size_t)t * (L + 1) + l + 1) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
