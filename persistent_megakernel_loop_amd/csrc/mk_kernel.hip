@@ -184,13 +184,13 @@ __device__ __forceinline__ void raise_timeout(const Params& P, const unsigned lo
 // carries `tag`, into dst[0..n) (LDS).  Words [own0, own1) are this workgroup's own: the
 // caller writes them to dst itself and they are not read back.
 //
-// Polling is pipelined: two rounds of KP loads per lane are in flight at a time, and a
-// round is consumed while the next one travels.  Every round loads all KP words of a
-// lane (indices clamped into the block), and `publish` (the caller's own stores, issued
-// after the first round) stores unconditionally, so the number of memory operations
-// between a round and its use is fixed and the wait before it covers that round only:
-// not the stores, and not the round behind it.  Returns false if the wait gave up
-// (spin limit, or another workgroup's abort).
+// Every round loads all KP words of a lane (indices clamped into the block), and
+// `publish` (the caller's own stores, issued after the first round) stores
+// unconditionally, so the number of memory operations between a round and its use is
+// fixed and the wait before the first round does not cover the stores.  A new round is
+// issued only after the previous one was consumed: a round still in flight when the
+// gather completes would make the next reuse of its registers wait for it.  Returns
+// false if the wait gave up (spin limit, or another workgroup's abort).
 // Loads per lane per poll round for an exchange of at most N words.
 template <int N>
 struct Kp : std::integral_constant<int, (N + 63) / 64 < 8 ? (N + 63) / 64 : 8> {};
@@ -210,7 +210,7 @@ __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, fl
     }
     const u64* s0 = src + base;
     const int last = cnt - 1;
-    u64 wa[KP], wb[KP];
+    u64 wa[KP];
     auto issue = [&](u64(&w)[KP]) {
 #pragma unroll
       for (int k = 0; k < KP; ++k) w[k] = ld_coh(s0 + min(lane + 64 * k, last));
@@ -239,18 +239,15 @@ __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, fl
       publish();
       published = true;
     }
-    issue(wb);
     uint32_t it = 0;
     while (true) {
       if (absorb(wa)) break;
-      issue(wa);
-      if (absorb(wb)) break;
       if (++it >= P.spin_limit) {
-        give_up(wb);
+        give_up(wa);
         return false;
       }
-      if ((it & 63) == 0 && ld_coh32(P.abort_flag)) return false;
-      issue(wb);
+      if ((it & 127) == 0 && ld_coh32(P.abort_flag)) return false;
+      issue(wa);
     }
   }
   if (!published) publish();
