@@ -712,14 +712,17 @@ __device__ __forceinline__ void lm_dot(const T& tl, const float* an, int rb, int
 // softmax over its positions; the four groups are merged at the end.  The current position
 // p is taken from LDS (K rotated and both rounded to cache precision by the control wave).
 // Attention over cache positions [c0, c1) of KV group x at layer l, for the group's
-// query heads: 16 lanes per 256-byte cache row (4 positions per load instruction), UNR
-// load instructions per batch; position p comes from LDS (k/v of this step).
-constexpr int kAttnUnroll = 4;
+// query heads.  A wave reads whole cache rows: lane i holds head dims
+// [i*DPL, i*DPL + DPL) of every row (one 4-byte load per lane and row), so a position's
+// score is one wave sum, uniform across the wave, and the wave's positions need no merge.
+// Position p comes from LDS (k/v of this step).  The positions of a wave are taken
+// kAttnBatch at a time, online softmax across batches.
+constexpr int kAttnBatch = 8;
 constexpr int kCoherent = 16;  // cache-policy bit of a buffer load: device-coherent
 
 template <class B>
 struct KvBatch {
-  u4 k[kAttnUnroll], v[kAttnUnroll];
+  uint32_t k[kAttnBatch], v[kAttnBatch];
 };
 
 template <class B>
@@ -743,18 +746,18 @@ __device__ __forceinline__ KvRange<B> kv_range(const Params& P, int x, int l, in
   return R;
 }
 
-// Issue the loads of one batch: positions jb + 4u + (lane / 16), clamped into the range
-// (rows past it are loaded again and ignored).  Rows at or past the current position
-// hold data of an earlier step or nothing yet: they are replaced or ignored by the caller.
+// Issue the loads of one batch: positions jb + u, clamped into the range (rows past it are
+// loaded again and ignored).  The row of the current position may hold data of an earlier
+// call: the caller takes that position from LDS.
 template <class B>
 __device__ __forceinline__ void kv_batch_load(const KvRange<B>& R, int jb, int lane, KvBatch<B>& kb) {
   constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
-  const int sub = lane >> 4, li = lane & 15;
+  static_assert(ROWB == 256, "a cache row is 64 lanes x 4 bytes");
 #pragma unroll
-  for (int u = 0; u < kAttnUnroll; ++u) {
-    const int jj = max(min(jb + 4 * u + sub, R.w1 - 1), 0);
-    kb.k[u] = __builtin_amdgcn_raw_buffer_load_b128(R.rk, jj * ROWB + li * 16, 0, kCoherent);
-    kb.v[u] = __builtin_amdgcn_raw_buffer_load_b128(R.rv, jj * ROWB + li * 16, 0, kCoherent);
+  for (int u = 0; u < kAttnBatch; ++u) {
+    const int jj = max(min(jb + u, R.w1 - 1), 0);
+    kb.k[u] = __builtin_amdgcn_raw_buffer_load_b32(R.rk, jj * ROWB + lane * 4, 0, kCoherent);
+    kb.v[u] = __builtin_amdgcn_raw_buffer_load_b32(R.rv, jj * ROWB + lane * 4, 0, kCoherent);
   }
 }
 
@@ -771,100 +774,93 @@ __device__ __forceinline__ void attention_prefetch(const Params& P, int x, int l
 template <class B, bool PREFETCHED>
 __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int x, int l, int p, int c0, int c1,
                                                 int wave, int lane, const KvBatch<B>& first) {
-  constexpr int ROWB = B::D * (B::BF16 ? 2 : 4);
-  static_assert(ROWB == 256, "a cache row is 16 lanes x 16 bytes");
-  constexpr int DPC = B::BF16 ? 8 : 4;  // head dims per 16-byte chunk
-  constexpr int UNR = kAttnUnroll;
-  const int sub = lane >> 4, li = lane & 15;
-  float q[B::QPG][DPC];
+  constexpr int DPL = B::D / 64;  // head dims per lane: 2 (bf16, d = 128) or 1 (f32, d = 64)
+  static_assert(DPL * (B::BF16 ? 2 : 4) == 4, "one 4-byte word per lane and row");
+  constexpr int PB = kAttnBatch;
+  float q[B::QPG][DPL];
 #pragma unroll
   for (int h = 0; h < B::QPG; ++h)
 #pragma unroll
-    for (int e = 0; e < DPC; ++e) q[h][e] = S.qkv[h * B::D + li * DPC + e];
-  float m[B::QPG], ls[B::QPG], acc[B::QPG][DPC];
+    for (int e = 0; e < DPL; ++e) q[h][e] = S.qkv[h * B::D + lane * DPL + e];
+  float m[B::QPG], ls[B::QPG], acc[B::QPG][DPL];
 #pragma unroll
   for (int h = 0; h < B::QPG; ++h) {
     m[h] = -INFINITY;
     ls[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < DPC; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   }
+  auto widen = [&](uint32_t w, float (&f)[DPL]) {
+    if constexpr (B::BF16) {
+      f[0] = bf16lo(w);
+      f[1] = bf16hi(w);
+    } else {
+      f[0] = __uint_as_float(w);
+    }
+  };
   const KvRange<B> R = kv_range<B>(P, x, l, c0, c1, wave);
   const int w0 = R.w0, w1 = R.w1;
-  for (int jb = w0; jb < w1; jb += 4 * UNR) {
+  for (int jb = w0; jb < w1; jb += PB) {
     KvBatch<B> kb;
     if (PREFETCHED && jb == w0) kb = first;
     else kv_batch_load<B>(R, jb, lane, kb);
-    const u4* kr = kb.k;
-    const u4* vr = kb.v;
+    const int nb = min(PB, w1 - jb);  // positions of this batch (uniform)
+    float sc[PB][B::QPG], vf[PB][DPL];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      if (jb + 4 * u >= w1) break;  // no position of the wave left in this load group
-      const int j = jb + 4 * u + sub;
-      float kf[DPC], vf[DPC];
-      if (j == p) {
+    for (int u = 0; u < PB; ++u) {
+      if (u < nb) {
+        float kf[DPL];
+        if (jb + u == p) {
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) { kf[e] = S.kp[li * DPC + e]; vf[e] = S.vp[li * DPC + e]; }
-      } else if constexpr (B::BF16) {
-        const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w}, vw[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = bf16lo(kw[e]); kf[2 * e + 1] = bf16hi(kw[e]);
-          vf[2 * e] = bf16lo(vw[e]); vf[2 * e + 1] = bf16hi(vw[e]);
+          for (int e = 0; e < DPL; ++e) { kf[e] = S.kp[lane * DPL + e]; vf[u][e] = S.vp[lane * DPL + e]; }
+        } else {
+          widen(kb.k[u], kf);
+          widen(kb.v[u], vf[u]);
         }
-      } else {
-        kf[0] = __uint_as_float(kr[u].x); kf[1] = __uint_as_float(kr[u].y);
-        kf[2] = __uint_as_float(kr[u].z); kf[3] = __uint_as_float(kr[u].w);
-        vf[0] = __uint_as_float(vr[u].x); vf[1] = __uint_as_float(vr[u].y);
-        vf[2] = __uint_as_float(vr[u].z); vf[3] = __uint_as_float(vr[u].w);
-      }
-      const bool valid = j < w1;
 #pragma unroll
-      for (int h = 0; h < B::QPG; ++h) {
-        float sc = 0.f;
+        for (int h = 0; h < B::QPG; ++h) {
+          float d = q[h][0] * kf[0];
 #pragma unroll
-        for (int e = 0; e < DPC; ++e) sc = fmaf(q[h][e], kf[e], sc);
-        sc = sum16(sc);  // within the 16-lane group of this position
-        if (valid) {
-          const float mn = fmaxf(m[h], sc);
-          const float corr = __expf(m[h] - mn);  // 0 while m is still -inf
-          const float ee = __expf(sc - mn);
-          ls[h] = ls[h] * corr + ee;
-#pragma unroll
-          for (int e = 0; e < DPC; ++e) acc[h][e] = fmaf(acc[h][e], corr, ee * vf[e]);
-          m[h] = mn;
+          for (int e = 1; e < DPL; ++e) d = fmaf(q[h][e], kf[e], d);
+          sc[u][h] = d;
         }
       }
     }
-  }
-  // merge the four position groups of the wave (lanes xor 16, then xor 32; row swaps)
-  auto other = [&](float v, int o) { return o == 16 ? xor16(v, lane) : xor32(v, lane); };
 #pragma unroll
-  for (int o = 16; o < 64; o <<= 1) {
+    for (int u = 0; u < PB; ++u)
+      if (u < nb)
+#pragma unroll
+        for (int h = 0; h < B::QPG; ++h) sc[u][h] = wave_sum(sc[u][h]);
 #pragma unroll
     for (int h = 0; h < B::QPG; ++h) {
-      const float mo = other(m[h], o), lo = other(ls[h], o);
-      const float M = fmaxf(m[h], mo);
-      const float fa = m[h] == -INFINITY ? 0.f : __expf(m[h] - M);
-      const float fb = mo == -INFINITY ? 0.f : __expf(mo - M);
-      ls[h] = ls[h] * fa + lo * fb;
+      float mb = sc[0][h];
 #pragma unroll
-      for (int e = 0; e < DPC; ++e) {
-        const float ao = other(acc[h][e], o);
-        acc[h][e] = acc[h][e] * fa + ao * fb;
+      for (int u = 1; u < PB; ++u)
+        if (u < nb) mb = fmaxf(mb, sc[u][h]);
+      const float mn = fmaxf(m[h], mb);
+      const float corr = __expf(m[h] - mn);  // 0 while m is still -inf
+      ls[h] *= corr;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[h][e] *= corr;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (u < nb) {
+          const float w = __expf(sc[u][h] - mn);
+          ls[h] += w;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(w, vf[u][e], acc[h][e]);
+        }
       }
-      m[h] = M;
+      m[h] = mn;
     }
   }
-  if (sub == 0) {
 #pragma unroll
-    for (int h = 0; h < B::QPG; ++h) {
+  for (int h = 0; h < B::QPG; ++h) {
 #pragma unroll
-      for (int e = 0; e < DPC; ++e) S.wpart[wave][h][2 + li * DPC + e] = acc[h][e];
-      if (li == 0) {
-        S.wpart[wave][h][0] = m[h];
-        S.wpart[wave][h][1] = ls[h];
-      }
+    for (int e = 0; e < DPL; ++e) S.wpart[wave][h][2 + lane * DPL + e] = acc[h][e];
+    if (lane == 0) {
+      S.wpart[wave][h][0] = m[h];
+      S.wpart[wave][h][1] = ls[h];
     }
   }
 }
