@@ -89,10 +89,8 @@ __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u &
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 // Round to bf16, nearest even (NaN kept quiet).
 __device__ __forceinline__ uint16_t f_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 b = (__bf16)f;  // the conversion instruction: round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
 }
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f(f_to_bf16(f)); }
 
@@ -564,7 +562,7 @@ __device__ __forceinline__ void norm_split(const float* x, const float* g, float
     }
   }
   ss = wave_sum(ss);
-  const float rs = rsqrtf(ss / (float)B::H + eps);
+  const float rs = __builtin_amdgcn_rsqf(ss / (float)B::H + eps);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
@@ -591,7 +589,7 @@ __device__ __forceinline__ void norm_to(const float* x, const float* g, float* o
 #pragma unroll
   for (int k = 0; k < B::HPL; ++k) { const float v = x[lane + 64 * k]; ss = fmaf(v, v, ss); }
   ss = wave_sum(ss);
-  const float rs = rsqrtf(ss / (float)B::H + eps);
+  const float rs = __builtin_amdgcn_rsqf(ss / (float)B::H + eps);
 #pragma unroll
   for (int k = 0; k < B::HPL; ++k) { const int i = lane + 64 * k; out[i] = g[i] * (x[i] * rs); }
 }
@@ -1357,7 +1355,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 #pragma unroll
             for (int h = 0; h <= B::QPG; ++h) {
               const float* g = h < B::QPG ? qn : kn;
-              const float rs = rsqrtf(ss[h] / (float)B::D + eps);
+              const float rs = __builtin_amdgcn_rsqf(ss[h] / (float)B::D + eps);
               const float n0 = g[lane] * (a0[h] * rs), n1 = g[lane + 64] * (a1[h] * rs);
               float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
               if (h < B::QPG) {
@@ -1378,7 +1376,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) { const float a = v[lane + 64 * k]; ss = fmaf(a, a, ss); }
             ss = wave_sum(ss);
-            const float rs = rsqrtf(ss / (float)B::D + eps);
+            const float rs = __builtin_amdgcn_rsqf(ss / (float)B::D + eps);
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) { const int i = lane + 64 * k; v[i] = g[i] * (v[i] * rs); }
             // LDS accesses of one wave are performed in order: the lane owning pair i
@@ -1441,19 +1439,29 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
         }
         if (r < nc) {
+          // every wave partial is read first (independent LDS loads), then combined
+          float mw[B::QPG][kWorkerWaves], lw[B::QPG][kWorkerWaves], aw[B::QPG][kWorkerWaves][B::DPL];
+#pragma unroll
+          for (int h = 0; h < B::QPG; ++h)
+#pragma unroll
+            for (int w = 0; w < kWorkerWaves; ++w) {
+              mw[h][w] = S.wpart[w][h][0];
+              lw[h][w] = S.wpart[w][h][1];
+#pragma unroll
+              for (int k = 0; k < B::DPL; ++k) aw[h][w][k] = S.wpart[w][h][2 + lane + 64 * k];
+            }
 #pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
             float M = -INFINITY;
-            for (int w = 0; w < kWorkerWaves; ++w) M = fmaxf(M, S.wpart[w][h][0]);
+#pragma unroll
+            for (int w = 0; w < kWorkerWaves; ++w) M = fmaxf(M, mw[h][w]);
             float Ls = 0.f;
 #pragma unroll
-            for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
             for (int w = 0; w < kWorkerWaves; ++w) {
-              const float mw = S.wpart[w][h][0];
-              const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
-              Ls = fmaf(S.wpart[w][h][1], f, Ls);
+              const float f = mw[h][w] == -INFINITY ? 0.f : __expf(mw[h][w] - M);
+              Ls = fmaf(lw[h][w], f, Ls);
 #pragma unroll
-              for (int k = 0; k < B::DPL; ++k) ca[h][k] = fmaf(S.wpart[w][h][2 + lane + 64 * k], f, ca[h][k]);
+              for (int k = 0; k < B::DPL; ++k) ca[h][k] = fmaf(aw[h][w][k], f, ca[h][k]);
             }
             cM[h] = M;
             cL[h] = Ls;
@@ -1480,20 +1488,29 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
         const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
         if (timed_exchange(Kp<kPerXcd * B::QPG * (B::D + 2)>{}, xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
                            own0, own1, publish_chunk)) {
+          // chunks four at a time: their loads are independent (chunks past nc weigh 0)
+#pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
             float M = -INFINITY;
-            for (int c = 0; c < nc; ++c) M = fmaxf(M, S.part[c][h][0]);
+            for (int c0 = 0; c0 < nc; c0 += 4) {
+#pragma unroll
+              for (int c = c0; c < c0 + 4; ++c) M = fmaxf(M, c < nc ? S.part[c][h][0] : -INFINITY);
+            }
             float Ls = 0.f, a[B::DPL];
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) a[k] = 0.f;
-            for (int c = 0; c < nc; ++c) {
-              const float mc = S.part[c][h][0];
-              const float f = mc == -INFINITY ? 0.f : __expf(mc - M);
-              Ls = fmaf(S.part[c][h][1], f, Ls);
+            for (int c0 = 0; c0 < nc; c0 += 4) {
 #pragma unroll
-              for (int k = 0; k < B::DPL; ++k) a[k] = fmaf(S.part[c][h][2 + lane + 64 * k], f, a[k]);
+              for (int c = c0; c < c0 + 4; ++c) {
+                const int cc = min(c, nc - 1);
+                const float mc = S.part[cc][h][0];
+                const float f = (c < nc && mc != -INFINITY) ? __expf(mc - M) : 0.f;
+                Ls = fmaf(S.part[cc][h][1], f, Ls);
+#pragma unroll
+                for (int k = 0; k < B::DPL; ++k) a[k] = fmaf(S.part[cc][h][2 + lane + 64 * k], f, a[k]);
+              }
             }
-            const float inv = 1.f / Ls;
+            const float inv = __builtin_amdgcn_rcpf(Ls);
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) S.ov[h * B::D + lane + 64 * k] = a[k] * inv;
           }
@@ -1537,7 +1554,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
         float mm = 0.f;
         if (lane < HALF) {
           const float gt = S.res[lane], up = S.res[HALF + lane];
-          mm = gt / (1.f + __expf(-gt)) * up;
+          mm = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
         }
         timed_exchange(Kp<B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF, (r + 1) * HALF, [&]() {
           st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm, tg0 + 4, lp);
