@@ -709,6 +709,29 @@ __device__ __forceinline__ void lm_dot(const T& tl, const float* an, int rb, int
 // flight together (device-coherent 128-bit buffer loads).  Every lane group keeps an online
 // softmax over its positions; the four groups are merged at the end.  The current position
 // p is taken from LDS (K rotated and both rounded to cache precision by the control wave).
+// The KV cache entry of group x at position p (layer l), from the rotated and rounded
+// k and v of this step in LDS.  Written by one worker wave of the group's last rank,
+// which waits for the stores to complete before it arrives at the next barrier: the
+// entry is visible to every reader of a later step.
+template <class B>
+__device__ __forceinline__ void write_kv_entry(const Params& P, const Lds<B>& S, int x, int l, int p, int lane) {
+  const size_t off = (((size_t)l * B::NKV + x) * P.max_seq + p) * B::D;
+#pragma unroll
+  for (int k = 0; k < B::DPL; ++k) {
+    const int i = lane + 64 * k;
+    if (P.kv_bf16) {
+      __hip_atomic_store(reinterpret_cast<uint16_t*>(P.kcache) + off + i, f_to_bf16(S.kp[i]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<uint16_t*>(P.vcache) + off + i, f_to_bf16(S.vp[i]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      __hip_atomic_store(reinterpret_cast<float*>(P.kcache) + off + i, S.kp[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<float*>(P.vcache) + off + i, S.vp[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every store of this wave acknowledged (and every copy landed)
+}
+
 // Attention over cache positions [c0, c1) of KV group x at layer l, for the group's
 // query heads.  A wave reads whole cache rows: lane i holds head dims
 // [i*DPL, i*DPL + DPL) of every row (one 4-byte load per lane and row), so a position's
@@ -929,6 +952,7 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       __syncthreads();
       __syncthreads();  // q rotated, k/v of position p in LDS
       if (S.abort_) return false;
+      if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over this rank's chunk of positions
       const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
@@ -1075,6 +1099,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
+      if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over the chunk
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
@@ -1402,24 +1427,6 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
               const int i = lane + 64 * k;
               const float v = S.qkv[(B::QPG + 1) * B::D + i];
               S.vp[i] = P.kv_bf16 ? bf16_round(v) : v;
-            }
-          }
-          if (r == 0) {  // the group's cache entry at position p
-            const size_t off = (((size_t)l * B::NKV + x) * P.max_seq + p) * B::D;
-#pragma unroll
-            for (int k = 0; k < B::DPL; ++k) {
-              const int i = lane + 64 * k;
-              if (P.kv_bf16) {
-                __hip_atomic_store(reinterpret_cast<uint16_t*>(P.kcache) + off + i, f_to_bf16(S.kp[i]),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<uint16_t*>(P.vcache) + off + i, f_to_bf16(S.vp[i]),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              } else {
-                __hip_atomic_store(reinterpret_cast<float*>(P.kcache) + off + i, S.kp[i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(reinterpret_cast<float*>(P.vcache) + off + i, S.vp[i], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-              }
             }
           }
         }
