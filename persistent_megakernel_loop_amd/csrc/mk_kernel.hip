@@ -536,7 +536,7 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 
 // Attention at position p covers positions 0..p, cut into n_chunks contiguous chunks
 // of chunk_len positions; chunk r goes to rank r of the group's XCD.
-constexpr int kMinChunk = 32;
+constexpr int kMinChunk = 56;  // one batch of 8 positions per worker wave
 __device__ __forceinline__ int n_chunks(int p) { return min(kPerXcd, max(1, (p + 1 + kMinChunk - 1) / kMinChunk)); }
 
 // RMSNorm of x with gains g into out (fp32) and, for the bf16 GEMVs, into split hi/lo

@@ -52,8 +52,8 @@ def test_q06_talker_two_layers():
 
 
 def test_q06_talker_long_chunks_two_layers():
-    """Positions past 1024 use all 32 attention chunks of an XCD."""
-    shape = wl.TALKER_0P6B.replace(name="talker-2l-kv1100", n_layers=2, kv_prefill=1100, prompt_len=0, steps=8)
+    """Positions past 32 x 56 use all 32 attention chunks of an XCD (the last one ragged)."""
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-kv1800", n_layers=2, kv_prefill=1800, prompt_len=0, steps=8)
     _case(shape)
 
 
