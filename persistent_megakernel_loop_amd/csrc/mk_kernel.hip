@@ -102,7 +102,7 @@ __device__ __forceinline__ float dpp(float old, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
 constexpr int kQuadXor1 = 0xb1, kQuadXor2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kRowRor8 = 0x128;
 
 // Sum over each group of 16 lanes, in every lane of the group.
 __device__ __forceinline__ float sum16(float v) {
@@ -112,6 +112,18 @@ __device__ __forceinline__ float sum16(float v) {
   v += dpp<kRowMirror, 0xf>(0.f, v);
   return v;
 }
+// Sum over groups of G consecutive lanes (G a power of two up to 32); the total sits in
+// the group's last lane.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp<kQuadXor1, 0xf>(0.f, v);
+  if constexpr (G >= 4) v += dpp<kQuadXor2, 0xf>(0.f, v);
+  if constexpr (G >= 8) v += dpp<kRowHalfMirror, 0xf>(0.f, v);
+  if constexpr (G >= 16) v += dpp<kRowMirror, 0xf>(0.f, v);
+  if constexpr (G >= 32) v += dpp<kRowBcast15, 0xa>(0.f, v);
+  return v;
+}
+
 // Sum over the wave, returned to every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v = sum16(v);
@@ -137,6 +149,62 @@ __device__ __forceinline__ float xor16(float v, int lane) {
 __device__ __forceinline__ float xor32(float v, int lane) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(lane >= 32 ? r[0] : r[1]);
+}
+
+// N wave sums at once (N = 2, 4, 8 or 16): lane L returns the sum over the wave of
+// v[L / (64 / N)] (for N = 2 only in the last lane of each half).  Each butterfly stage
+// pairs two values and keeps, in each half of the lanes, the partial sum of one of them:
+// lane-half swaps for the 32- and 16-lane steps, DPP for 8 and 4, then the sum within
+// the remaining 64 / N lanes.  Sixteen sums cost about as much as two single ones.
+template <int N>
+__device__ __forceinline__ float transpose_sum(const float (&v)[N], int lane) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "lane groups");
+  float a[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = v[i];
+  int n = N;
+  // lane bit 5: lanes < 32 keep a[i], the others a[i + n/2]
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a[i]), __float_as_uint(a[i + N / 2]), false, false);
+    a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  n = N / 2;
+  if constexpr (N >= 4) {  // lane bit 4: even rows keep a[i], odd rows a[i + n/2]
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + N / 4]), false, false);
+      a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+  }
+  if constexpr (N >= 8) {  // lane bit 3
+    const bool b3 = (lane & 8) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const float send = b3 ? a[i] : a[i + N / 8];
+      a[i] = (b3 ? a[i + N / 8] : a[i]) + dpp<kRowRor8, 0xf>(0.f, send);  // lane ^ 8 within the row
+    }
+  }
+  if constexpr (N >= 16) {  // lane bit 2: lanes 0-3 <-> 7-4 of each eight
+    const bool b2 = (lane & 4) != 0;
+    const float send = b2 ? a[0] : a[1];
+    a[0] = (b2 ? a[1] : a[0]) + dpp<kRowHalfMirror, 0xf>(0.f, send);
+  }
+  float z = a[0];
+  if constexpr (N == 16) {
+    z += dpp<kQuadXor1, 0xf>(0.f, z);
+    z += dpp<kQuadXor2, 0xf>(0.f, z);
+  } else if constexpr (N == 8) {
+    z += dpp<kRowHalfMirror, 0xf>(0.f, z);
+    z += dpp<kQuadXor1, 0xf>(0.f, z);
+    z += dpp<kQuadXor2, 0xf>(0.f, z);
+  } else if constexpr (N == 4) {
+    z = sum16(z);
+  } else {
+    z = group_sum<32>(z);
+  }
+  (void)n;
+  return z;
 }
 
 __device__ __forceinline__ u64 tagword(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
@@ -421,17 +489,6 @@ __device__ __forceinline__ float dot8(const u4& w, const u4& hi, const u4& lo, f
   return acc;
 }
 
-// Sum over groups of G consecutive lanes (G a power of two up to 32); the total sits in
-// the group's last lane.
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-  if constexpr (G >= 2) v += dpp<kQuadXor1, 0xf>(0.f, v);
-  if constexpr (G >= 4) v += dpp<kQuadXor2, 0xf>(0.f, v);
-  if constexpr (G >= 8) v += dpp<kRowHalfMirror, 0xf>(0.f, v);
-  if constexpr (G >= 16) v += dpp<kRowMirror, 0xf>(0.f, v);
-  if constexpr (G >= 32) v += dpp<kRowBcast15, 0xa>(0.f, v);
-  return v;
-}
 
 // A GEMV tile of ROWS rows x COLS bf16 weights in LDS (chunk g at slot[g], row-major).
 // Worker wave w takes rows [w*RPW, w*RPW + RPW); the row loop has a fixed trip count and
@@ -492,13 +549,16 @@ __device__ __forceinline__ void tile_dot2(const u4* slot, const u4* ahi, const u
         if (CPR % 64 == 0 || c < CPR) d[j] = dot8(w, hi[i], lo[i], d[j]);
       }
     }
+    // the wave's row sums together: lane L ends with row L / (64 / NS)
+    constexpr int NS = G::RPW <= 2 ? 2 : (G::RPW <= 4 ? 4 : (G::RPW <= 8 ? 8 : 16));
+    static_assert(G::RPW <= 16, "rows per wave");
+    float dv[NS];
 #pragma unroll
-    for (int j = 0; j < G::RPW; ++j) d[j] = wave_sum(d[j]);
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < G::RPW; ++j)
-        if (r0 + j < ROWS) res[r0 + j] = d[j];
-    }
+    for (int j = 0; j < NS; ++j) dv[j] = j < G::RPW ? d[j] : 0.f;
+    const float tot = transpose_sum<NS>(dv, lane);
+    constexpr int GL = 64 / NS;
+    const int j = lane / GL;
+    if (lane % GL == GL - 1 && j < G::RPW && r0 + j < ROWS) res[r0 + j] = tot;
   }
 }
 
@@ -518,6 +578,7 @@ struct Lds {
   u4 mv_hi[B::IX / 8], mv_lo[B::IX / 8];
   alignas(16) float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
   alignas(16) float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
+  alignas(16) float attw[kWorkerWaves][16];                 // per-wave softmax weights of a batch
   float wbest_v[kWorkerWaves];
   int wbest_i[kWorkerWaves];
   alignas(16) float g_in0[B::H];         // input norm of layer 0 (constant for the launch)
@@ -827,50 +888,70 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
     else kv_batch_load<B>(R, jb, lane, kb);
     const int nb = min(PB, w1 - jb);  // positions of this batch (uniform)
     float sc[PB][B::QPG], vf[PB][DPL];
+    // every slot of the batch is computed (branch-free, so the wave sums interleave);
+    // slots past the wave's range are ignored below
+    const int pu = p - jb;  // slot of the current position, if it is in this batch
+    float kp_[DPL], vp_[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) { kp_[e] = S.kp[lane * DPL + e]; vp_[e] = S.vp[lane * DPL + e]; }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
-      if (u < nb) {
-        float kf[DPL];
-        if (jb + u == p) {
+      float kf[DPL];
+      widen(kb.k[u], kf);
+      widen(kb.v[u], vf[u]);
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) { kf[e] = S.kp[lane * DPL + e]; vf[u][e] = S.vp[lane * DPL + e]; }
-        } else {
-          widen(kb.k[u], kf);
-          widen(kb.v[u], vf[u]);
-        }
+      for (int e = 0; e < DPL; ++e) {  // slots past the range may hold anything, NaN included: zeroed
+        kf[e] = u == pu ? kp_[e] : (u < nb ? kf[e] : 0.f);
+        vf[u][e] = u == pu ? vp_[e] : (u < nb ? vf[u][e] : 0.f);
+      }
 #pragma unroll
-        for (int h = 0; h < B::QPG; ++h) {
-          float d = q[h][0] * kf[0];
+      for (int h = 0; h < B::QPG; ++h) {
+        float d = q[h][0] * kf[0];
 #pragma unroll
-          for (int e = 1; e < DPL; ++e) d = fmaf(q[h][e], kf[e], d);
-          sc[u][h] = d;
-        }
+        for (int e = 1; e < DPL; ++e) d = fmaf(q[h][e], kf[e], d);
+        sc[u][h] = d;
       }
     }
+    // scores of the batch: lane L holds position u = L / 8 of head h = (L / 4) % 2
+    static_assert(PB * B::QPG == 16, "sixteen scores per batch");
+    float flat[16];
 #pragma unroll
     for (int u = 0; u < PB; ++u)
-      if (u < nb)
 #pragma unroll
-        for (int h = 0; h < B::QPG; ++h) sc[u][h] = wave_sum(sc[u][h]);
+      for (int h = 0; h < B::QPG; ++h) flat[u * B::QPG + h] = sc[u][h];
+    const float s_l = transpose_sum<16>(flat, lane);
+    const int u_l = lane >> 3, h_l = (lane >> 2) & 1;
+    const bool valid = u_l < nb;
+    const float sv = valid ? s_l : -INFINITY;
+    // batch maximum of the lane's head: over lane bits 3, 4, 5 (the positions)
+    float mx = fmaxf(sv, dpp<kRowRor8, 0xf>(sv, sv));
+    mx = fmaxf(mx, xor16(mx, lane));
+    mx = fmaxf(mx, xor32(mx, lane));
+    const float m_l = h_l ? m[1] : m[0];
+    const float mn_l = fmaxf(m_l, mx);
+    const float w_l = valid ? __expf(sv - mn_l) : 0.f;
+    float ws = w_l + dpp<kRowRor8, 0xf>(0.f, w_l);
+    ws += xor16(ws, lane);
+    ws += xor32(ws, lane);
+    if ((lane & 3) == 0) S.attw[wave][lane >> 2] = w_l;
+    float aw[16];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const f4 t = *reinterpret_cast<const f4*>(&S.attw[wave][i]);
+      aw[i] = t.x; aw[i + 1] = t.y; aw[i + 2] = t.z; aw[i + 3] = t.w;
+    }
 #pragma unroll
     for (int h = 0; h < B::QPG; ++h) {
-      float mb = sc[0][h];
-#pragma unroll
-      for (int u = 1; u < PB; ++u)
-        if (u < nb) mb = fmaxf(mb, sc[u][h]);
-      const float mn = fmaxf(m[h], mb);
+      const float mn = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mn_l), 4 * h));
+      const float wsum = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(ws), 4 * h));
       const float corr = __expf(m[h] - mn);  // 0 while m is still -inf
-      ls[h] *= corr;
+      ls[h] = fmaf(ls[h], corr, wsum);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] *= corr;
+      for (int e = 0; e < DPL; ++e) {
+        float a = acc[h][e] * corr;
 #pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        if (u < nb) {
-          const float w = __expf(sc[u][h] - mn);
-          ls[h] += w;
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(w, vf[u][e], acc[h][e]);
-        }
+        for (int u = 0; u < PB; ++u) a = fmaf(aw[u * B::QPG + h], vf[u][e], a);
+        acc[h][e] = a;
       }
       m[h] = mn;
     }
