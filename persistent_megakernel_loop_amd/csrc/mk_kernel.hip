@@ -723,6 +723,17 @@ __device__ __forceinline__ void dma_copy(const uint8_t* src, void* lds, int wave
     lds_dma16(src + (size_t)g * 16, reinterpret_cast<uint8_t*>(lds) + (size_t)i * 1024);
   }
 }
+// Part `part` of NPARTS of the same copy: its 1 KB instructions [part*NI/NPARTS,
+// (part+1)*NI/NPARTS), instruction i issued by worker wave i % 7 as in the whole copy.
+template <int CHUNKS, int NPARTS>
+__device__ __forceinline__ void dma_part(const uint8_t* src, void* lds, int part, int wave, int lane) {
+  constexpr int NI = (CHUNKS + 63) / 64;
+  const int a = part * NI / NPARTS, b = (part + 1) * NI / NPARTS;
+  for (int i = a + (wave - a % kWorkerWaves + kWorkerWaves) % kWorkerWaves; i < b; i += kWorkerWaves) {
+    const int g = min(i * 64 + lane, CHUNKS - 1);
+    lds_dma16(src + (size_t)g * 16, reinterpret_cast<uint8_t*>(lds) + (size_t)i * 1024);
+  }
+}
 
 // ------------------------------------------------------------------ worker waves
 // LM head rows of one pass: 2 per worker wave from rb, wave w holds rows rb + 2w, rb + 2w + 1.
@@ -1103,6 +1114,10 @@ __device__ __forceinline__ void wait_vmem_rt(int c) {
 }
 // Chunk-DMA instructions worker wave w issues for a copy of NI instructions.
 __device__ __forceinline__ constexpr int dma_count(int ni, int w) { return (ni - w + kWorkerWaves - 1) / kWorkerWaves; }
+// ... and for part `part` of NPARTS of it.
+__device__ __forceinline__ constexpr int dma_part_count(int ni, int nparts, int part, int w) {
+  return dma_count((part + 1) * ni / nparts, w) - dma_count(part * ni / nparts, w);
+}
 
 // Worker waves with the weight tiles in LDS.  Slot A holds the q/k/v tile, then gate/up;
 // slot B the O tile, then down.  Each tile is copied (LDS DMA, all seven worker waves)
@@ -1171,6 +1186,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
       KvBatch<B> kb;
       if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
+      // Weight copies are spread over the layer's phases, about 12 KB per phase, so that
+      // no exchange polls behind a large burst in this CU's memory queue: each tile is
+      // copied in parts as soon as its slot is free, and waited for before the barrier
+      // that precedes its dot product.
       // q, k, v rows (slot A)
       if (grp) {
         if constexpr (B::BF16) tile_dot2<B::T_QKV, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
@@ -1178,20 +1197,23 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       }
       mark(1);
       wsync();
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);  // slot A is free
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over the chunk
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
-      // slot A is free since the q/k/v dot: the gate/up tile streams in while the chunk
-      // partials are combined (that wait is mostly for the slowest chunk anyway)
-      dma_copy<TGU::TOTAL>(A.gu(l), slotA, wave, lane);
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 2, wave, lane);
       mark(0);
-      wait_vmem_rt(dma_count(NI_GU, wave));  // the O tile (and every copy before the gate/up one) has landed
       wsync();
+      // the O tile (and every copy before the gate/up parts) has landed
+      wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave) + dma_part_count(NI_GU, 4, 1, wave) +
+                   dma_part_count(NI_GU, 4, 2, wave));
       wsync();  // attention output of the group in LDS
       if (S.abort_) return;
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 3, wave, lane);
       // O partial (slot B)
       if (grp) {
         if constexpr (B::BF16) tile_dot2<B::T_O, B::OC>(slotB, S.ov_hi, S.ov_lo, S.res, wave, lane);
@@ -1199,31 +1221,35 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       }
       mark(1);
       wsync();
-      dma_copy<TD::TOTAL>(A.down(l), slotB, wave, lane);
-      wait_vmem_rt(dma_count(NI_D, wave));  // gate/up tile landed
+      dma_part<TD::TOTAL, 2>(A.down(l), slotB, 0, wave, lane);  // slot B is free
+      wait_vmem_rt(dma_part_count(NI_D, 2, 0, wave));        // gate/up tile landed
       wsync();  // residual after attention, normalised
       if (S.abort_) return;
+      dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
       // gate / up (slot A)
       if constexpr (B::BF16) tile_dot2<B::T_GU, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
       else tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
       dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
-      dma_copy<TQKV::TOTAL>(A.qkv(ln), slotA, wave, lane);
-      wait_vmem_rt(dma_count(NI_GA, wave) + dma_count(NI_Q, wave));  // down tile landed
+      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 0, wave, lane);  // slot A is free
+      wait_vmem_rt(dma_count(NI_GA, wave) + dma_part_count(NI_Q, 3, 0, wave));  // down tile landed
       wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return;
+      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 1, wave, lane);
       // down partial (slot B)
       if constexpr (B::BF16) tile_dot2<B::T_D, B::IX>(slotB, S.mv_hi, S.mv_lo, S.res, wave, lane);
       else tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
       mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
       wsync();
+      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 2, wave, lane);
       if (!lm_now) {
-        dma_copy<TO::TOTAL>(A.o(ln), slotB, wave, lane);
-        wait_vmem_rt(dma_count(NI_O, wave));  // next gains and q/k/v tile landed
+        dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 0, wave, lane);  // slot B is free
+        wait_vmem_rt(dma_part_count(NI_O, 2, 0, wave));       // next gains and q/k/v tile landed
       }
       wsync();  // residual after the MLP, normalised for the next layer or the head
+      if (!lm_now) dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 1, wave, lane);
       ++gc;
       if (S.abort_) return;
     }
