@@ -246,9 +246,17 @@ __device__ __forceinline__ void raise_timeout(const Params& P, const unsigned lo
   }
 }
 
-// Control wave: gather words src[0..n) that other workgroups publish, waiting until each
-// carries `tag`, into dst[0..n) (LDS).  Words [own0, own1) are this workgroup's own: the
-// caller writes them to dst itself and they are not read back.
+// Loads per lane per poll round for an exchange of at most N words polled by NP waves.
+template <int N, int NP = 1>
+struct Kp : std::integral_constant<int, (N + 64 * NP - 1) / (64 * NP) < 8 ? (N + 64 * NP - 1) / (64 * NP) : 8> {};
+// Waves that poll the gathers inside an XCD in the LDS-tile bodies: the control wave and
+// worker waves 4..6 (which have no weight copy in flight).
+constexpr int kPollWaves = 4;
+
+// Gather words src[0..n) that other workgroups publish, waiting until each carries `tag`,
+// into dst[0..n) (LDS).  Words [own0, own1) are this workgroup's own: the caller writes
+// them to dst itself and they are not read back.  The words go in blocks of 64*KP; NPART
+// waves may share a gather, wave `part` taking blocks part, part + NPART, ...
 //
 // Every round loads all KP words of a lane (indices clamped into the block), and
 // `publish` (the caller's own stores, issued after the first round) stores
@@ -257,22 +265,24 @@ __device__ __forceinline__ void raise_timeout(const Params& P, const unsigned lo
 // issued only after the previous one was consumed: a round still in flight when the
 // gather completes would make the next reuse of its registers wait for it.  Returns
 // false if the wait gave up (spin limit, or another workgroup's abort).
-// Loads per lane per poll round for an exchange of at most N words.
-template <int N>
-struct Kp : std::integral_constant<int, (N + 63) / 64 < 8 ? (N + 63) / 64 : 8> {};
-
-template <int KP, class F>
+template <int KP, int NPART, class F>
 __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, F&& publish,
-                                         int lane, const Params& P, uint32_t& rounds, unsigned long long& first_round) {
+                                         int lane, const Params& P, uint32_t& rounds, unsigned long long& first_round,
+                                         int part) {
   static_assert(KP >= 1 && KP <= 16, "words per lane per round");
   bool published = false;
-  for (int base = 0; base < n; base += 64 * KP) {
+  for (int base = part * 64 * KP; base < n; base += NPART * 64 * KP) {
     const int cnt = min(n - base, 64 * KP);
-    uint32_t pending = 0;
+    // need[k]: word base + lane + 64k is still awaited by this lane.  Each round only
+    // selects (no branch per word): a word whose tag matches keeps its value in a register
+    // and drops out of `need`; the values go to dst once the whole block has arrived.
+    bool need[KP], want[KP];
+    float val[KP];
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
       const int i = base + lane + 64 * k;
-      if (lane + 64 * k < cnt && (i < own0 || i >= own1)) pending |= 1u << k;
+      want[k] = need[k] = lane + 64 * k < cnt && (i < own0 || i >= own1);
+      val[k] = 0.f;
     }
     const u64* s0 = src + base;
     const int last = cnt - 1;
@@ -282,23 +292,24 @@ __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, fl
       for (int k = 0; k < KP; ++k) w[k] = ld_coh(s0 + min(lane + 64 * k, last));
     };
     auto absorb = [&](const u64(&w)[KP]) -> bool {
+      bool left = false;
 #pragma unroll
-      for (int k = 0; k < KP; ++k)
-        if (((pending >> k) & 1u) && (uint32_t)(w[k] >> 32) == tag) {
-          dst[base + lane + 64 * k] = __uint_as_float((uint32_t)w[k]);
-          pending &= ~(1u << k);
-        }
+      for (int k = 0; k < KP; ++k) {
+        const bool hit = (uint32_t)(w[k] >> 32) == tag;
+        val[k] = hit ? __uint_as_float((uint32_t)w[k]) : val[k];
+        need[k] = need[k] && !hit;
+        left = left || need[k];
+      }
       if (rounds++ == 0) first_round = wall_clock64();
-      return !__any(pending != 0);
+      return !__any(left);
     };
     auto give_up = [&](const u64(&w)[KP]) {
-      if (pending) {  // record the first word still behind (selected without indexing w at run time)
-        const int k0 = __builtin_ctz(pending);
-        uint32_t seen = 0;
+      int k0 = -1;  // the first word still behind (selected without indexing w at run time)
+      uint32_t seen = 0;
 #pragma unroll
-        for (int k = 0; k < KP; ++k) seen = k == k0 ? (uint32_t)(w[k] >> 32) : seen;
-        raise_timeout(P, s0 + lane + 64 * k0, tag, seen);
-      }
+      for (int k = KP - 1; k >= 0; --k)
+        if (need[k]) { k0 = k; seen = (uint32_t)(w[k] >> 32); }
+      if (k0 >= 0) raise_timeout(P, s0 + lane + 64 * k0, tag, seen);
     };
     issue(wa);
     if (!published) {
@@ -315,9 +326,22 @@ __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, fl
       if ((it & 127) == 0 && ld_coh32(P.abort_flag)) return false;
       issue(wa);
     }
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+      if (want[k]) dst[base + lane + 64 * k] = val[k];
   }
   if (!published) publish();
   return true;
+}
+
+// A worker wave's share (part 1..kPollWaves-1) of a gather the control wave publishes
+// into; false if the wait gave up.
+template <int KP>
+__device__ __forceinline__ bool help_gather(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, int part,
+                                            int lane, const Params& P) {
+  uint32_t rounds = 0;
+  unsigned long long r1 = 0;
+  return exchange<KP, kPollWaves>(src, n, tag, dst, own0, own1, [] {}, lane, P, rounds, r1, part);
 }
 
 // Phase trace: one workgroup (dbg_phase_wg >= 0, records [n][n_sync][8]) or every
@@ -701,35 +725,36 @@ __device__ __forceinline__ void lds_dma16(const void* g, const void* lds) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(g), "s"(l) : "memory");
 }
+// s_waitcnt vmcnt(0) as a builtin (expcnt and lgkmcnt fields at their maxima), so that the
+// compiler's own wait insertion knows no vector-memory load is outstanding after it.
+__device__ __forceinline__ void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// Wait until at most the last M chunk-DMA instructions of this wave may still be pending,
-// where M is what worker wave w issues of a copy of NI instructions dealt round-robin.
-template <int NI>
-__device__ __forceinline__ void wait_after(int w) {
-  if constexpr (NI % kWorkerWaves == 0) wait_vmem<NI / kWorkerWaves>();
-  else if (w < NI % kWorkerWaves) wait_vmem<NI / kWorkerWaves + 1>();
-  else wait_vmem<NI / kWorkerWaves>();
-}
-// Copy `chunks` 16-byte chunks src -> lds; instruction i (64 chunks) is issued by wave i % 7.
+// Worker waves 0..3 issue every weight copy of the LDS-tile bodies; waves 4..6 never have a
+// copy in flight, so they can take part in the gathers of other workgroups' words (a wave's
+// vector-memory counter is in order: a poll could not complete before an earlier copy).
+constexpr int kDmaWaves = 4;
+// Copy `chunks` 16-byte chunks src -> lds; instruction i (64 chunks) is issued by wave i % 4.
 template <int CHUNKS>
 __device__ __forceinline__ void dma_copy(const uint8_t* src, void* lds, int wave, int lane) {
   constexpr int NI = (CHUNKS + 63) / 64;
-  for (int i = wave; i < NI; i += kWorkerWaves) {
+  if (wave >= kDmaWaves) return;
+  for (int i = wave; i < NI; i += kDmaWaves) {
     const int g = min(i * 64 + lane, CHUNKS - 1);
     lds_dma16(src + (size_t)g * 16, reinterpret_cast<uint8_t*>(lds) + (size_t)i * 1024);
   }
 }
 // Part `part` of NPARTS of the same copy: its 1 KB instructions [part*NI/NPARTS,
-// (part+1)*NI/NPARTS), instruction i issued by worker wave i % 7 as in the whole copy.
+// (part+1)*NI/NPARTS), instruction i issued by wave i % 4 as in the whole copy.
 template <int CHUNKS, int NPARTS>
 __device__ __forceinline__ void dma_part(const uint8_t* src, void* lds, int part, int wave, int lane) {
   constexpr int NI = (CHUNKS + 63) / 64;
+  if (wave >= kDmaWaves) return;
   const int a = part * NI / NPARTS, b = (part + 1) * NI / NPARTS;
-  for (int i = a + (wave - a % kWorkerWaves + kWorkerWaves) % kWorkerWaves; i < b; i += kWorkerWaves) {
+  for (int i = a + (wave - a % kDmaWaves + kDmaWaves) % kDmaWaves; i < b; i += kDmaWaves) {
     const int g = min(i * 64 + lane, CHUNKS - 1);
     lds_dma16(src + (size_t)g * 16, reinterpret_cast<uint8_t*>(lds) + (size_t)i * 1024);
   }
@@ -1112,8 +1137,10 @@ __device__ __forceinline__ void wait_vmem_table(int c, std::integer_sequence<int
 __device__ __forceinline__ void wait_vmem_rt(int c) {
   wait_vmem_table(min(c, 63), std::make_integer_sequence<int, 64>{});
 }
-// Chunk-DMA instructions worker wave w issues for a copy of NI instructions.
-__device__ __forceinline__ constexpr int dma_count(int ni, int w) { return (ni - w + kWorkerWaves - 1) / kWorkerWaves; }
+// Chunk-DMA instructions wave w issues for a copy of NI instructions (none past the copy waves).
+__device__ __forceinline__ constexpr int dma_count(int ni, int w) {
+  return w < kDmaWaves ? (ni - w + kDmaWaves - 1) / kDmaWaves : 0;
+}
 // ... and for part `part` of NPARTS of it.
 __device__ __forceinline__ constexpr int dma_part_count(int ni, int nparts, int part, int w) {
   return dma_count((part + 1) * ni / nparts, w) - dma_count(part * ni / nparts, w);
@@ -1149,6 +1176,24 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   const int lm0 = b * rpb, lm1 = min(P.vocab, lm0 + rpb);
   __builtin_assume(wave >= 0 && wave < kWorkerWaves);
 
+  // waves 4..6 poll parts 1..3 of the gathers inside the XCD (the control wave polls part 0)
+  const bool poller = wave >= kWorkerWaves - (kPollWaves - 1);
+  const int part = wave - (kWorkerWaves - kPollWaves);
+  const uint32_t tpp = tags_per_position(L);
+  // this wave's share of a gather, then the barrier that joins the gather's waves
+  auto gather = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1) {
+    constexpr int NMAX = decltype(nmax)::value;
+    if (active && poller) {
+      if (!help_gather<Kp<NMAX, kPollWaves>::value>(src, n, tag, dst, own0, own1, part, lane, P) && lane == 0)
+        S.abort_ = 1;
+      // An exit of the poll loop may leave a round's loads in flight.  Waiting for them
+      // here, in a form the compiler sees, keeps it from waiting for them at a later merge
+      // point on every wave, where the copy waves would also wait for their weight copies.
+      vmem_drain();
+    }
+    __syncthreads();
+  };
+
   int gc = 0;  // layers entered since the launch started; gains of layer gc in G[gc % 2]
   // phase trace: worker wave 0 of the traced workgroup stamps, for the barrier it is about
   // to reach, when its copies were issued, when its dot product finished and when it arrived
@@ -1176,7 +1221,9 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
     ph = 0;
     wsync();  // input fetched
     if (S.abort_) return;
+    const uint32_t tbase = P.tag0 + 1 + (uint32_t)t * tpp;
     for (int l = 0; l < L; ++l) {
+      const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const bool lm_now = lm && l + 1 == L;
       // this rank's chunk of cache positions: its first batch is loaded now
@@ -1198,6 +1245,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       mark(1);
       wsync();
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);  // slot A is free
+      gather(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
+             r * B::T_QKV, (r + 1) * B::T_QKV);
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
@@ -1209,8 +1258,12 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       mark(0);
       wsync();
       // the O tile (and every copy before the gate/up parts) has landed
-      wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave) + dma_part_count(NI_GU, 4, 1, wave) +
-                   dma_part_count(NI_GU, 4, 2, wave));
+      if (wave < kDmaWaves)
+        wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave) + dma_part_count(NI_GU, 4, 1, wave) +
+                     dma_part_count(NI_GU, 4, 2, wave));
+      gather(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
+             P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+             r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0);
       wsync();  // attention output of the group in LDS
       if (S.abort_) return;
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 3, wave, lane);
@@ -1222,7 +1275,9 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       mark(1);
       wsync();
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 0, wave, lane);  // slot B is free
-      wait_vmem_rt(dma_part_count(NI_D, 2, 0, wave));        // gate/up tile landed
+      if (wave < kDmaWaves) wait_vmem_rt(dma_part_count(NI_D, 2, 0, wave));  // gate/up tile landed
+      gather(true, std::integral_constant<int, B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O,
+             (r + 1) * B::T_O);
       wsync();  // residual after attention, normalised
       if (S.abort_) return;
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
@@ -1233,7 +1288,9 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();
       dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
       dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 0, wave, lane);  // slot A is free
-      wait_vmem_rt(dma_count(NI_GA, wave) + dma_part_count(NI_Q, 3, 0, wave));  // down tile landed
+      if (wave < kDmaWaves) wait_vmem_rt(dma_count(NI_GA, wave) + dma_part_count(NI_Q, 3, 0, wave));  // down tile landed
+      gather(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv,
+             r * (B::T_GU / 2), (r + 1) * (B::T_GU / 2));
       wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return;
       dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 1, wave, lane);
@@ -1246,8 +1303,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 2, wave, lane);
       if (!lm_now) {
         dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 0, wave, lane);  // slot B is free
-        wait_vmem_rt(dma_part_count(NI_O, 2, 0, wave));       // next gains and q/k/v tile landed
+        if (wave < kDmaWaves) wait_vmem_rt(dma_part_count(NI_O, 2, 0, wave));  // next gains and q/k/v tile landed
       }
+      gather(true, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D,
+             (r + 1) * B::T_D);
       wsync();  // residual after the MLP, normalised for the next layer or the head
       if (!lm_now) dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 1, wave, lane);
       ++gc;
@@ -1292,11 +1351,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
   int n_marks = 0;  // gathers completed in the current segment (first two are traced)
   // a word every lane may store to when it has nothing to publish: publishing stays branch-free
   u64* const sink = P.xsink + (size_t)b * 64 + lane;
-  auto timed_exchange = [&](auto kp, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, auto&& publish) {
+  auto timed_exchange = [&](auto kp, auto np, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1,
+                            auto&& publish) {
     const unsigned long long a = wall_clock64();
     uint32_t rounds = 0;
     unsigned long long r1 = a;
-    const bool ok = exchange<decltype(kp)::value>(src, n, tag, dst, own0, own1, publish, lane, P, rounds, r1);
+    const bool ok = exchange<decltype(kp)::value, decltype(np)::value>(src, n, tag, dst, own0, own1, publish, lane, P,
+                                                                       rounds, r1, 0);
     const unsigned long long e = wall_clock64();
     wait_ticks += e - a;
     if (trace_phases && lane == 0 && n_marks < 2) {
@@ -1308,6 +1369,25 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
     ++n_marks;
     if (!ok) fail();
     return ok;
+  };
+  // A gather inside the XCD (at most NMAX words).  With the tiles in LDS, worker waves 4..6
+  // poll three of its four parts (this wave publishes and polls part 0) and a barrier joins
+  // them (not a traced phase); otherwise this wave polls all of it.  `active` is uniform
+  // over the workgroup; the barrier is passed either way.
+  constexpr bool kShare = lds_tiles<B>();
+  auto local_exchange = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1,
+                            auto&& publish) -> bool {
+    constexpr int NMAX = decltype(nmax)::value;
+    if constexpr (kShare) {
+      bool ok = true;
+      if (active)
+        ok = timed_exchange(Kp<NMAX, kPollWaves>{}, std::integral_constant<int, kPollWaves>{}, src, n, tag, dst, own0,
+                            own1, publish);
+      __syncthreads();
+      return active && ok && S.abort_ == 0;
+    } else {
+      return active && timed_exchange(Kp<NMAX>{}, std::integral_constant<int, 1>{}, src, n, tag, dst, own0, own1, publish);
+    }
   };
   // argmax over the grid's keys of the LM head that ran at position t
   auto argmax_of = [&](int t, int* out_id) -> bool {
@@ -1385,7 +1465,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     float* seen = &S.part[0][0][0];
-    if (timed_exchange(Kp<kGrid>{}, P.xplace, kGrid, P.tag0, seen, b, b + 1, [&]() {
+    if (timed_exchange(Kp<kGrid>{}, std::integral_constant<int, 1>{}, P.xplace, kGrid, P.tag0, seen, b, b + 1, [&]() {
           st_tag(lane == 0 ? P.xplace + b : sink, __uint_as_float(xcc & 0xfu), P.tag0);
           if (lane == 0) seen[b] = __uint_as_float(xcc & 0xfu);
         })) {
@@ -1461,9 +1541,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
       // ------------------------------------------------------------ q,k,v of the group
       if (!sync()) return;
-      if (grp) {
+      {
         u64* xq = P.xq + (size_t)x * B::RQKV;
-        if (timed_exchange(Kp<B::RQKV>{}, xq, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV, (r + 1) * B::T_QKV, [&]() {
+        if (local_exchange(grp, std::integral_constant<int, B::RQKV>{}, xq, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV,
+                           (r + 1) * B::T_QKV, [&]() {
               st_local(lane < B::T_QKV ? xq + r * B::T_QKV + lane : sink, S.res[lane], tg0 + 0, lp);
               if (lane < B::T_QKV) S.qkv[r * B::T_QKV + lane] = S.res[lane];
             })) {
@@ -1541,7 +1622,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
       if (!sync()) return;
       // ------------------------------------------------------------ attention combine
       if (!sync()) return;
-      if (grp) {
+      {
         const int nc = n_chunks(p);
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
         // this rank's chunk partial: the worker waves' partials merged in a fixed order
@@ -1552,7 +1633,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 #pragma unroll
           for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
         }
-        if (r < nc) {
+        if (grp && r < nc) {
           // every wave partial is read first (independent LDS loads), then combined
           float mw[B::QPG][kWorkerWaves], lw[B::QPG][kWorkerWaves], aw[B::QPG][kWorkerWaves][B::DPL];
 #pragma unroll
@@ -1600,8 +1681,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           }
         };
         const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
-        if (timed_exchange(Kp<kPerXcd * B::QPG * (B::D + 2)>{}, xa, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
-                           own0, own1, publish_chunk)) {
+        if (local_exchange(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{}, xa, nc * B::QPG * (B::D + 2),
+                           tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk)) {
           // chunks four at a time: their loads are independent (chunks past nc weigh 0)
 #pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
@@ -1638,26 +1719,29 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
         // group x's partial of rows [r*T_O, (r+1)*T_O) goes to slot [r][x]: the reader of
         // those rows finds every group's partial in one contiguous run
         float* pp = &S.part[0][0][0];
-        if (timed_exchange(Kp<B::NG * B::T_O>{}, P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, pp,
-                           grp ? x * B::T_O : 0, grp ? (x + 1) * B::T_O : 0, [&]() {
-                             const bool mine = grp && lane < B::T_O;
-                             st_tag(mine ? P.xop + ((size_t)r * B::NG + x) * B::T_O + lane : sink, S.res[lane], tg0 + 2);
-                             if (mine) pp[x * B::T_O + lane] = S.res[lane];
+        // this XCD's rows of the residual: every group's partial (across the XCDs)
+        const bool got = timed_exchange(Kp<B::NG * B::T_O>{}, std::integral_constant<int, 1>{},
+                                        P.xop + (size_t)r * B::NG * B::T_O, B::NG * B::T_O, tg0 + 2, pp,
+                                        grp ? x * B::T_O : 0, grp ? (x + 1) * B::T_O : 0, [&]() {
+                                          const bool mine = grp && lane < B::T_O;
+                                          st_tag(mine ? P.xop + ((size_t)r * B::NG + x) * B::T_O + lane : sink, S.res[lane],
+                                                 tg0 + 2);
+                                          if (mine) pp[x * B::T_O + lane] = S.res[lane];
+                                        });
+        float nv = 0.f;
+        if (got && lane < B::T_O) {
+          float d = 0.f;
+          for (int g = 0; g < B::NG; ++g) d += pp[g * B::T_O + lane];
+          nv = S.xs[r * B::T_O + lane] + d;
+        }
+        // then the whole residual inside the XCD
+        if (local_exchange(got, std::integral_constant<int, B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs,
+                           r * B::T_O, (r + 1) * B::T_O, [&]() {
+                             st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
+                             if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
                            })) {
-          float nv = 0.f;
-          if (lane < B::T_O) {
-            float d = 0.f;
-            for (int g = 0; g < B::NG; ++g) d += pp[g * B::T_O + lane];
-            nv = S.xs[r * B::T_O + lane] + d;
-          }
-          if (timed_exchange(Kp<B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O, (r + 1) * B::T_O, [&]() {
-                st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
-                if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
-              }))
-          {
-            if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1], S.an, S.an_hi, S.an_lo, eps, lane);
-            else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
-          }
+          if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1], S.an, S.an_hi, S.an_lo, eps, lane);
+          else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
         }
       }
       if (!sync()) return;
@@ -1670,39 +1754,42 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           const float gt = S.res[lane], up = S.res[HALF + lane];
           mm = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
         }
-        timed_exchange(Kp<B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF, (r + 1) * HALF, [&]() {
-          st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm, tg0 + 4, lp);
-          if (lane < HALF) S.mv[r * HALF + lane] = mm;
-        });
-        if constexpr (B::BF16) split_act<B::IX>(S.mv, S.mv_hi, S.mv_lo, lane);
+        const bool got = local_exchange(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4,
+                                        S.mv, r * HALF, (r + 1) * HALF, [&]() {
+                                          st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm,
+                                                   tg0 + 4, lp);
+                                          if (lane < HALF) S.mv[r * HALF + lane] = mm;
+                                        });
+        if constexpr (B::BF16) if (got) split_act<B::IX>(S.mv, S.mv_hi, S.mv_lo, lane);
       }
       if (!sync()) return;
       // ------------------------------------------------------------ down partials -> residual
       if (!sync()) return;
       {
         float* pp = &S.part[0][0][0];
-        if (timed_exchange(Kp<kXcds * B::T_D>{}, P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, pp,
-                           x * B::T_D, (x + 1) * B::T_D, [&]() {
-                             st_tag(lane < B::T_D ? P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane : sink, S.res[lane],
-                                    tg0 + 5);
-                             if (lane < B::T_D) pp[x * B::T_D + lane] = S.res[lane];
+        const bool got = timed_exchange(Kp<kXcds * B::T_D>{}, std::integral_constant<int, 1>{},
+                                        P.xdp + (size_t)r * kXcds * B::T_D, kXcds * B::T_D, tg0 + 5, pp, x * B::T_D,
+                                        (x + 1) * B::T_D, [&]() {
+                                          st_tag(lane < B::T_D ? P.xdp + ((size_t)r * kXcds + x) * B::T_D + lane : sink,
+                                                 S.res[lane], tg0 + 5);
+                                          if (lane < B::T_D) pp[x * B::T_D + lane] = S.res[lane];
+                                        });
+        float nv = 0.f;
+        if (got && lane < B::T_D) {
+          float d = 0.f;
+          for (int g = 0; g < kXcds; ++g) d += pp[g * B::T_D + lane];
+          nv = S.xs[r * B::T_D + lane] + d;
+        }
+        if (local_exchange(got, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs,
+                           r * B::T_D, (r + 1) * B::T_D, [&]() {
+                             st_local(lane < B::T_D ? P.xxb + (size_t)x * B::H + r * B::T_D + lane : sink, nv, tg0 + 6, lp);
+                             if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
                            })) {
-          float nv = 0.f;
-          if (lane < B::T_D) {
-            float d = 0.f;
-            for (int g = 0; g < kXcds; ++g) d += pp[g * B::T_D + lane];
-            nv = S.xs[r * B::T_D + lane] + d;
-          }
-          if (timed_exchange(Kp<B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D, (r + 1) * B::T_D, [&]() {
-                st_local(lane < B::T_D ? P.xxb + (size_t)x * B::H + r * B::T_D + lane : sink, nv, tg0 + 6, lp);
-                if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
-              })) {
-            if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, S.an_hi, S.an_lo, eps, lane);
-            else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
-            if (P.dbg_hidden && b == 0)
-              for (int k = 0; k < B::HPL; ++k)
-                P.dbg_hidden[((size_t)t * (L + 1) + l + 1) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
-          }
+          if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, S.an_hi, S.an_lo, eps, lane);
+          else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
+          if (P.dbg_hidden && b == 0)
+            for (int k = 0; k < B::HPL; ++k)
+              P.dbg_hidden[((size_t)t * (L + 1) + l + 1) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
         }
       }
       ++gc;
