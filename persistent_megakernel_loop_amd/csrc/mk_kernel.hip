@@ -481,16 +481,6 @@ __device__ __forceinline__ void split8(const float* v, u4& hi, u4& lo) {
   hi = u4{h[0], h[1], h[2], h[3]};
   lo = u4{l[0], l[1], l[2], l[3]};
 }
-// Control wave: split n inputs (n % 8 == 0) for the next GEMV.
-template <int N>
-__device__ __forceinline__ void split_act(const float* v, u4* hi, u4* lo, int lane) {
-  static_assert(N % 8 == 0, "whole chunks");
-#pragma unroll
-  for (int c0 = 0; c0 < N / 8; c0 += 64) {
-    const int c = c0 + lane;
-    if (c < N / 8) split8(v + 8 * c, hi[c], lo[c]);
-  }
-}
 // (through a copy: a bit cast applied directly to a vector element has been seen to read
 // element 0 instead)
 __device__ __forceinline__ bf16x2 as_bf2(uint32_t u) {
@@ -523,7 +513,9 @@ __device__ __forceinline__ float dot8(const u4& w, const u4& hi, const u4& lo, f
 template <int ROWS, int COLS>
 struct Gemv2 {
   static constexpr int CPR = COLS / 8;
-  static constexpr int RPW = (ROWS + kWorkerWaves - 1) / kWorkerWaves;
+  // the seven worker waves and the control wave (waves w and w + 4 share a SIMD, so equal
+  // shares over all eight balance the SIMDs)
+  static constexpr int RPW = (ROWS + kWorkerWaves) / (kWorkerWaves + 1);
   static constexpr bool GROUPED = CPR < 64 && 64 % CPR == 0;
   static constexpr int RPI = GROUPED ? 64 / CPR : 1;  // rows per pass
   static constexpr int NPASS = (RPW + RPI - 1) / RPI;
@@ -531,15 +523,44 @@ struct Gemv2 {
   static_assert(COLS % 8 == 0 && ROWS <= 64, "tile");
 };
 
-template <int ROWS, int COLS>
-__device__ __forceinline__ void tile_dot2(const u4* slot, const u4* ahi, const u4* alo, float* res, int wave, int lane) {
+// 8 fp32 inputs of chunk c as hi/lo bf16 chunks, times the gains g when GAIN.
+template <bool GAIN>
+__device__ __forceinline__ void split_chunk(const f4 (&v)[2], const float* g, int c, u4& hi, u4& lo) {
+  float y[8] = {v[0].x, v[0].y, v[0].z, v[0].w, v[1].x, v[1].y, v[1].z, v[1].w};
+  if constexpr (GAIN) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f4 gg = *reinterpret_cast<const f4*>(g + 8 * c + 4 * e);
+      y[4 * e + 0] *= gg.x;
+      y[4 * e + 1] *= gg.y;
+      y[4 * e + 2] *= gg.z;
+      y[4 * e + 3] *= gg.w;
+    }
+  }
+  split8(y, hi, lo);
+}
+
+// Rows [wave*RPW, ...) of a ROWS x COLS bf16 tile in LDS times the fp32 input x (LDS),
+// into res.  Every wave splits the input chunks it reads itself.  With NORM the input is
+// RMS-normalised with gains g: the products run on g * x, and each row sum is scaled by
+// 1/rms(x) at the end (one scalar per input vector), so the wave's sum of squares over all
+// COLS inputs overlaps the products instead of preceding them.  Every wave sums in the
+// same order (lane L's chunks are L, L + 64, ...), so all waves use the same scale.
+template <int ROWS, int COLS, bool NORM>
+__device__ __forceinline__ void tile_dot2(const u4* slot, const float* x, const float* g, float eps, float* res, int wave,
+                                          int lane) {
   using G = Gemv2<ROWS, COLS>;
   constexpr int CPR = G::CPR;
   const int r0 = wave * G::RPW;
   if (r0 >= ROWS) return;
   if constexpr (G::GROUPED) {
+    static_assert(!NORM, "normalised inputs use the chunk-per-lane layout");
     const int lr = lane / CPR, c = lane % CPR;
-    const u4 hi = ahi[c], lo = alo[c];
+    f4 v[2];
+    v[0] = *reinterpret_cast<const f4*>(x + 8 * c);
+    v[1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+    u4 hi, lo;
+    split_chunk<false>(v, g, c, hi, lo);
     float d[G::NPASS];
 #pragma unroll
     for (int i = 0; i < G::NPASS; ++i) {
@@ -554,12 +575,33 @@ __device__ __forceinline__ void tile_dot2(const u4* slot, const u4* ahi, const u
       if (c == CPR - 1 && j < G::RPW && row < ROWS) res[row] = d[i];
     }
   } else {
-    u4 hi[G::NIT], lo[G::NIT];
+    f4 v[G::NIT][2];
 #pragma unroll
     for (int i = 0; i < G::NIT; ++i) {
       const int c = min(lane + 64 * i, CPR - 1);
-      hi[i] = ahi[c];
-      lo[i] = alo[c];
+      v[i][0] = *reinterpret_cast<const f4*>(x + 8 * c);
+      v[i][1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+    }
+    u4 hi[G::NIT], lo[G::NIT];
+#pragma unroll
+    for (int i = 0; i < G::NIT; ++i) split_chunk<NORM>(v[i], g, min(lane + 64 * i, CPR - 1), hi[i], lo[i]);
+    float rs = 1.f;
+    if constexpr (NORM) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < G::NIT; ++i) {
+        if (CPR % 64 == 0 || lane + 64 * i < CPR) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            ss = fmaf(v[i][e].x, v[i][e].x, ss);
+            ss = fmaf(v[i][e].y, v[i][e].y, ss);
+            ss = fmaf(v[i][e].z, v[i][e].z, ss);
+            ss = fmaf(v[i][e].w, v[i][e].w, ss);
+          }
+        }
+      }
+      ss = wave_sum(ss);
+      rs = __builtin_amdgcn_rsqf(ss / (float)COLS + eps);
     }
     float d[G::RPW];
 #pragma unroll
@@ -582,7 +624,7 @@ __device__ __forceinline__ void tile_dot2(const u4* slot, const u4* ahi, const u
     const float tot = transpose_sum<NS>(dv, lane);
     constexpr int GL = 64 / NS;
     const int j = lane / GL;
-    if (lane % GL == GL - 1 && j < G::RPW && r0 + j < ROWS) res[r0 + j] = tot;
+    if (lane % GL == GL - 1 && j < G::RPW && r0 + j < ROWS) res[r0 + j] = NORM ? tot * rs : tot;
   }
 }
 
@@ -596,10 +638,6 @@ struct Lds {
   alignas(16) float ov[B::OC];           // attention output of the group
   alignas(16) float mv[B::IX];           // SwiGLU output slice
   alignas(16) float res[64];             // row results of the current tile
-  // bf16 bodies: GEMV inputs as bf16 pairs, hi = bf16(v) and lo = bf16(v - hi), 8 values per u4
-  u4 an_hi[B::H / 8], an_lo[B::H / 8];
-  u4 ov_hi[B::OC / 8], ov_lo[B::OC / 8];
-  u4 mv_hi[B::IX / 8], mv_lo[B::IX / 8];
   alignas(16) float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
   alignas(16) float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
   alignas(16) float attw[kWorkerWaves][16];                 // per-wave softmax weights of a batch
@@ -624,10 +662,11 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 constexpr int kMinChunk = 56;  // one batch of 8 positions per worker wave
 __device__ __forceinline__ int n_chunks(int p) { return min(kPerXcd, max(1, (p + 1 + kMinChunk - 1) / kMinChunk)); }
 
-// RMSNorm of x with gains g into out (fp32) and, for the bf16 GEMVs, into split hi/lo
-// chunks; each lane works on whole 8-element chunks (16-byte LDS accesses).
+// RMSNorm of x with gains g into out (fp32), lane L working on 8-element chunks L,
+// L + 64, ... (16-byte LDS accesses; the order of the sum of squares is the one the bf16
+// GEMVs that normalise their own inputs use).
 template <class B>
-__device__ __forceinline__ void norm_split(const float* x, const float* g, float* out, u4* hi, u4* lo, float eps, int lane) {
+__device__ __forceinline__ void norm_out(const float* x, const float* g, float* out, float eps, int lane) {
   constexpr int NCH = B::H / 8, CPL = (NCH + 63) / 64;
   f4 v[CPL][2];
   float ss = 0.f;
@@ -652,18 +691,12 @@ __device__ __forceinline__ void norm_split(const float* x, const float* g, float
   for (int i = 0; i < CPL; ++i) {
     const int c = lane + 64 * i;
     if (NCH % 64 == 0 || c < NCH) {
-      float y[8];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const f4 gg = *reinterpret_cast<const f4*>(g + 8 * c + 4 * e);
-        y[4 * e + 0] = gg.x * (v[i][e].x * rs);
-        y[4 * e + 1] = gg.y * (v[i][e].y * rs);
-        y[4 * e + 2] = gg.z * (v[i][e].z * rs);
-        y[4 * e + 3] = gg.w * (v[i][e].w * rs);
+        *reinterpret_cast<f4*>(out + 8 * c + 4 * e) =
+            f4{gg.x * (v[i][e].x * rs), gg.y * (v[i][e].y * rs), gg.z * (v[i][e].z * rs), gg.w * (v[i][e].w * rs)};
       }
-      *reinterpret_cast<f4*>(out + 8 * c) = f4{y[0], y[1], y[2], y[3]};
-      *reinterpret_cast<f4*>(out + 8 * c + 4) = f4{y[4], y[5], y[6], y[7]};
-      split8(y, hi[c], lo[c]);
     }
   }
 }
@@ -1239,7 +1272,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       // that precedes its dot product.
       // q, k, v rows (slot A)
       if (grp) {
-        if constexpr (B::BF16) tile_dot2<B::T_QKV, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
+        // input norm: layer 0's own gains, else the block of the layer before
+        if constexpr (B::BF16)
+          tile_dot2<B::T_QKV, B::H, true>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D,
+                                          P.rms_eps, S.res, wave, lane);
         else tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
       }
       mark(1);
@@ -1269,7 +1305,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 3, wave, lane);
       // O partial (slot B)
       if (grp) {
-        if constexpr (B::BF16) tile_dot2<B::T_O, B::OC>(slotB, S.ov_hi, S.ov_lo, S.res, wave, lane);
+        if constexpr (B::BF16) tile_dot2<B::T_O, B::OC, false>(slotB, S.ov, nullptr, 0.f, S.res, wave, lane);
         else tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
       }
       mark(1);
@@ -1282,7 +1318,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (S.abort_) return;
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
       // gate / up (slot A)
-      if constexpr (B::BF16) tile_dot2<B::T_GU, B::H>(slotA, S.an_hi, S.an_lo, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_GU, B::H, true>(slotA, S.xs, S.G[gc & 1], P.rms_eps, S.res, wave, lane);
       else tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
@@ -1295,7 +1331,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (S.abort_) return;
       dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 1, wave, lane);
       // down partial (slot B)
-      if constexpr (B::BF16) tile_dot2<B::T_D, B::IX>(slotB, S.mv_hi, S.mv_lo, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_D, B::IX, false>(slotB, S.mv, nullptr, 0.f, S.res, wave, lane);
       else tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
       mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
@@ -1334,7 +1370,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
 
 // ------------------------------------------------------------------ control wave
 template <class B>
-__device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, int r, int lane) {
+__device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u4* slotA, const u4* slotB, int x, int r,
+                                             int lane) {
   const TileAddr<B> A{P, x, r};
   const bool grp = B::NG == kXcds || x < B::NG;
   const int L = P.n_layers;
@@ -1375,6 +1412,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
   // them (not a traced phase); otherwise this wave polls all of it.  `active` is uniform
   // over the workgroup; the barrier is passed either way.
   constexpr bool kShare = lds_tiles<B>();
+  // the bf16 GEMVs with LDS tiles normalise their own inputs: only the LM head needs S.an
+  constexpr bool kNormHere = !(lds_tiles<B>() && B::BF16);
   auto local_exchange = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1,
                             auto&& publish) -> bool {
     constexpr int NMAX = decltype(nmax)::value;
@@ -1528,8 +1567,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           S.rope_c[i] = P.rope_cos[(size_t)ps * (B::D / 2) + i];
           S.rope_s[i] = P.rope_sin[(size_t)ps * (B::D / 2) + i];
         }
-        if constexpr (B::BF16) norm_split<B>(S.xs, S.g_in0, S.an, S.an_hi, S.an_lo, eps, lane);
-        else norm_to<B>(S.xs, S.g_in0, S.an, eps, lane);
+        if constexpr (kNormHere) {
+          if constexpr (B::BF16) norm_out<B>(S.xs, S.g_in0, S.an, eps, lane);
+          else norm_to<B>(S.xs, S.g_in0, S.an, eps, lane);
+        }
         if (P.dbg_hidden && b == 0)
           for (int k = 0; k < B::HPL; ++k)
             P.dbg_hidden[((size_t)t * (L + 1)) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
@@ -1539,6 +1580,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 
     for (int l = 0; l < L; ++l) {
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
+      // this wave's share of the bf16 GEMVs with tiles in LDS (the eighth row block)
+      constexpr bool kDots = lds_tiles<B>() && B::BF16;
+      if constexpr (kDots) {
+        if (grp)
+          tile_dot2<B::T_QKV, B::H, true>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D, eps, S.res,
+                                          kWorkerWaves, lane);
+      }
       // ------------------------------------------------------------ q,k,v of the group
       if (!sync()) return;
       {
@@ -1709,11 +1757,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
 #pragma unroll
             for (int k = 0; k < B::DPL; ++k) S.ov[h * B::D + lane + 64 * k] = a[k] * inv;
           }
-          if constexpr (B::BF16) split_act<B::OC>(S.ov, S.ov_hi, S.ov_lo, lane);
         }
       }
       if (!sync()) return;
       // ------------------------------------------------------------ O partials -> residual
+      if constexpr (kDots) {
+        if (grp) tile_dot2<B::T_O, B::OC, false>(slotB, S.ov, nullptr, 0.f, S.res, kWorkerWaves, lane);
+      }
       if (!sync()) return;
       {
         // group x's partial of rows [r*T_O, (r+1)*T_O) goes to slot [r][x]: the reader of
@@ -1740,12 +1790,15 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
                              st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
                              if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
                            })) {
-          if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1], S.an, S.an_hi, S.an_lo, eps, lane);
-          else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
+          if constexpr (kNormHere) {
+            if constexpr (B::BF16) norm_out<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
+            else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
+          }
         }
       }
       if (!sync()) return;
       // ------------------------------------------------------------ SwiGLU slice
+      if constexpr (kDots) tile_dot2<B::T_GU, B::H, true>(slotA, S.xs, S.G[gc & 1], eps, S.res, kWorkerWaves, lane);
       if (!sync()) return;
       {
         constexpr int HALF = B::T_GU / 2;
@@ -1754,16 +1807,15 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
           const float gt = S.res[lane], up = S.res[HALF + lane];
           mm = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
         }
-        const bool got = local_exchange(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4,
-                                        S.mv, r * HALF, (r + 1) * HALF, [&]() {
-                                          st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm,
-                                                   tg0 + 4, lp);
-                                          if (lane < HALF) S.mv[r * HALF + lane] = mm;
-                                        });
-        if constexpr (B::BF16) if (got) split_act<B::IX>(S.mv, S.mv_hi, S.mv_lo, lane);
+        local_exchange(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv, r * HALF,
+                       (r + 1) * HALF, [&]() {
+                         st_local(lane < HALF ? P.xm + (size_t)x * B::IX + r * HALF + lane : sink, mm, tg0 + 4, lp);
+                         if (lane < HALF) S.mv[r * HALF + lane] = mm;
+                       });
       }
       if (!sync()) return;
       // ------------------------------------------------------------ down partials -> residual
+      if constexpr (kDots) tile_dot2<B::T_D, B::IX, false>(slotB, S.mv, nullptr, 0.f, S.res, kWorkerWaves, lane);
       if (!sync()) return;
       {
         float* pp = &S.part[0][0][0];
@@ -1785,8 +1837,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, int x, 
                              st_local(lane < B::T_D ? P.xxb + (size_t)x * B::H + r * B::T_D + lane : sink, nv, tg0 + 6, lp);
                              if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
                            })) {
-          if constexpr (B::BF16) norm_split<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, S.an_hi, S.an_lo, eps, lane);
-          else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
+          // the next layer's input norm, or the final norm ahead of the LM head
+          if (kNormHere || l + 1 == L) {
+            if constexpr (B::BF16) norm_out<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
+            else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
+          }
           if (P.dbg_hidden && b == 0)
             for (int k = 0; k < B::HPL; ++k)
               P.dbg_hidden[((size_t)t * (L + 1) + l + 1) * B::H + lane + 64 * k] = S.xs[lane + 64 * k];
@@ -1836,7 +1891,7 @@ __device__ __forceinline__ void persistent_body(const Params& P) {
   const int b = blockIdx.x, x = b % kXcds, r = b / kXcds;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x == 0) S.abort_ = 0;
-  if (wave == kWorkerWaves) control_loop<B>(P, S, x, r, lane);
+  if (wave == kWorkerWaves) control_loop<B>(P, S, slotA, slotB, x, r, lane);
   else if constexpr (lds_tiles<B>()) worker_loop_lds<B>(P, S, slotA, slotB, x, r, wave, lane);
   else worker_loop_regs<B>(P, S, x, r, wave, lane);
 }
