@@ -540,15 +540,21 @@ __device__ __forceinline__ void split_chunk(const f4 (&v)[2], const float* g, in
   split8(y, hi, lo);
 }
 
-// Rows [wave*RPW, ...) of a ROWS x COLS bf16 tile in LDS times the fp32 input x (LDS),
-// into res.  Every wave splits the input chunks it reads itself.  With NORM the input is
+// Input of a bf16 GEMV with LDS tiles: fp32 in LDS (each wave splits the chunks it reads),
+// fp32 RMS-normalised on the way, or already split into hi/lo chunks in LDS.
+enum class In { kF32, kF32Norm, kSplit };
+
+// Rows [wave*RPW, ...) of a ROWS x COLS bf16 tile in LDS times the input x, into res.  For
+// In::kSplit, x points at the hi chunks and g at the lo chunks.  Every wave splits the
+// fp32 input chunks it reads itself.  With In::kF32Norm the input is
 // RMS-normalised with gains g: the products run on g * x, and each row sum is scaled by
 // 1/rms(x) at the end (one scalar per input vector), so the wave's sum of squares over all
 // COLS inputs overlaps the products instead of preceding them.  Every wave sums in the
 // same order (lane L's chunks are L, L + 64, ...), so all waves use the same scale.
-template <int ROWS, int COLS, bool NORM>
+template <int ROWS, int COLS, In IN>
 __device__ __forceinline__ void tile_dot2(const u4* slot, const float* x, const float* g, float eps, float* res, int wave,
                                           int lane) {
+  constexpr bool NORM = IN == In::kF32Norm;
   using G = Gemv2<ROWS, COLS>;
   constexpr int CPR = G::CPR;
   const int r0 = wave * G::RPW;
@@ -556,11 +562,16 @@ __device__ __forceinline__ void tile_dot2(const u4* slot, const float* x, const 
   if constexpr (G::GROUPED) {
     static_assert(!NORM, "normalised inputs use the chunk-per-lane layout");
     const int lr = lane / CPR, c = lane % CPR;
-    f4 v[2];
-    v[0] = *reinterpret_cast<const f4*>(x + 8 * c);
-    v[1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
     u4 hi, lo;
-    split_chunk<false>(v, g, c, hi, lo);
+    if constexpr (IN == In::kSplit) {
+      hi = reinterpret_cast<const u4*>(x)[c];
+      lo = reinterpret_cast<const u4*>(g)[c];
+    } else {
+      f4 v[2];
+      v[0] = *reinterpret_cast<const f4*>(x + 8 * c);
+      v[1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+      split_chunk<false>(v, g, c, hi, lo);
+    }
     float d[G::NPASS];
 #pragma unroll
     for (int i = 0; i < G::NPASS; ++i) {
@@ -576,15 +587,19 @@ __device__ __forceinline__ void tile_dot2(const u4* slot, const float* x, const 
     }
   } else {
     f4 v[G::NIT][2];
+    u4 hi[G::NIT], lo[G::NIT];
 #pragma unroll
     for (int i = 0; i < G::NIT; ++i) {
       const int c = min(lane + 64 * i, CPR - 1);
-      v[i][0] = *reinterpret_cast<const f4*>(x + 8 * c);
-      v[i][1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+      if constexpr (IN == In::kSplit) {
+        hi[i] = reinterpret_cast<const u4*>(x)[c];
+        lo[i] = reinterpret_cast<const u4*>(g)[c];
+      } else {
+        v[i][0] = *reinterpret_cast<const f4*>(x + 8 * c);
+        v[i][1] = *reinterpret_cast<const f4*>(x + 8 * c + 4);
+        split_chunk<NORM>(v[i], g, c, hi[i], lo[i]);
+      }
     }
-    u4 hi[G::NIT], lo[G::NIT];
-#pragma unroll
-    for (int i = 0; i < G::NIT; ++i) split_chunk<NORM>(v[i], g, min(lane + 64 * i, CPR - 1), hi[i], lo[i]);
     float rs = 1.f;
     if constexpr (NORM) {
       float ss = 0.f;
@@ -638,6 +653,7 @@ struct Lds {
   alignas(16) float ov[B::OC];           // attention output of the group
   alignas(16) float mv[B::IX];           // SwiGLU output slice
   alignas(16) float res[64];             // row results of the current tile
+  u4 ov_hi[B::OC / 8], ov_lo[B::OC / 8];  // attention output split for the O GEMV (bf16 hi, lo)
   alignas(16) float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
   alignas(16) float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
   alignas(16) float attw[kWorkerWaves][16];                 // per-wave softmax weights of a batch
@@ -710,6 +726,73 @@ __device__ __forceinline__ void norm_to(const float* x, const float* g, float* o
   const float rs = __builtin_amdgcn_rsqf(ss / (float)B::H + eps);
 #pragma unroll
   for (int k = 0; k < B::HPL; ++k) { const int i = lane + 64 * k; out[i] = g[i] * (x[i] * rs); }
+}
+
+// ---------------------------------------------------------------- shared steps after a gather
+// With the tiles in LDS, all eight waves of a workgroup take part in the steps that follow
+// the q/k/v gather and the attention gather, wave pw doing share pw of 8 (the control
+// wave is pw 7).
+
+// Per-head RMSNorm of q and k and their rotation (head dim 128: lane i holds elements i and
+// i + 64 of a head, rotary pair i), the cache rounding of k and v: q head pw (pw < QPG),
+// k (pw == QPG), v (pw == QPG + 1).
+template <class B>
+__device__ __forceinline__ void qk_part(Lds<B>& S, const float* qn, const float* kn, float eps, bool kv_bf16, int pw,
+                                        int lane) {
+  static_assert(B::D == 128, "two elements per lane");
+  if (pw <= B::QPG) {
+    const float a0 = S.qkv[pw * B::D + lane], a1 = S.qkv[pw * B::D + lane + 64];
+    const float ss = wave_sum(fmaf(a1, a1, a0 * a0));
+    const float* g = pw < B::QPG ? qn : kn;
+    const float rs = __builtin_amdgcn_rsqf(ss / (float)B::D + eps);
+    const float c = S.rope_c[lane], sn = S.rope_s[lane];
+    const float n0 = g[lane] * (a0 * rs), n1 = g[lane + 64] * (a1 * rs);
+    float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
+    if (pw < B::QPG) {
+      const float qscale = rsqrtf((float)B::D);
+      S.qkv[pw * B::D + lane] = o0 * qscale;
+      S.qkv[pw * B::D + lane + 64] = o1 * qscale;
+    } else {
+      if (kv_bf16) { o0 = bf16_round(o0); o1 = bf16_round(o1); }
+      S.kp[lane] = o0;
+      S.kp[lane + 64] = o1;
+    }
+  } else if (pw == B::QPG + 1) {
+    const float v0 = S.qkv[(B::QPG + 1) * B::D + lane], v1 = S.qkv[(B::QPG + 1) * B::D + lane + 64];
+    S.vp[lane] = kv_bf16 ? bf16_round(v0) : v0;
+    S.vp[lane + 64] = kv_bf16 ? bf16_round(v1) : v1;
+  }
+}
+
+// The group's attention output from the nc chunk partials in S.part, split for the O
+// GEMV: wave pw takes output columns [pw*QPG*D/8, ...) (lane = column), combined in chunk
+// order; then four of its lanes split the columns 8 at a time.
+template <class B>
+__device__ __forceinline__ void combine_part(Lds<B>& S, int nc, int pw, int lane) {
+  constexpr int CW = B::OC / 8;  // columns per wave
+  static_assert(CW <= 64 && CW % 8 == 0 && B::D % CW == 0, "columns per wave");
+  const int col = pw * CW + lane, h = (pw * CW) / B::D, d = col - h * B::D;
+  if (lane < CW) {
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < nc; c0 += 4) {
+#pragma unroll
+      for (int c = c0; c < c0 + 4; ++c) M = fmaxf(M, c < nc ? S.part[c][h][0] : -INFINITY);
+    }
+    float Ls = 0.f, a = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += 4) {
+#pragma unroll
+      for (int c = c0; c < c0 + 4; ++c) {
+        const int cc = min(c, nc - 1);
+        const float mc = S.part[cc][h][0];
+        const float f = (c < nc && mc != -INFINITY) ? __expf(mc - M) : 0.f;
+        Ls = fmaf(S.part[cc][h][1], f, Ls);
+        a = fmaf(S.part[cc][h][2 + d], f, a);
+      }
+    }
+    S.ov[col] = a * __builtin_amdgcn_rcpf(Ls);
+  }
+  // this wave's own LDS writes are seen by its later reads
+  if (lane < CW / 8) split8(S.ov + pw * CW + 8 * lane, S.ov_hi[pw * (CW / 8) + lane], S.ov_lo[pw * (CW / 8) + lane]);
 }
 
 // Addresses of this workgroup's tiles in layer l.
@@ -1214,7 +1297,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
   const int part = wave - (kWorkerWaves - kPollWaves);
   const uint32_t tpp = tags_per_position(L);
   // this wave's share of a gather, then the barrier that joins the gather's waves
-  auto gather = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1) {
+  // (true if the gather completed everywhere: the steps after it may run)
+  auto gather = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1) -> bool {
     constexpr int NMAX = decltype(nmax)::value;
     if (active && poller) {
       if (!help_gather<Kp<NMAX, kPollWaves>::value>(src, n, tag, dst, own0, own1, part, lane, P) && lane == 0)
@@ -1225,6 +1309,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       vmem_drain();
     }
     __syncthreads();
+    return active && S.abort_ == 0;
   };
 
   int gc = 0;  // layers entered since the launch started; gains of layer gc in G[gc % 2]
@@ -1274,15 +1359,17 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (grp) {
         // input norm: layer 0's own gains, else the block of the layer before
         if constexpr (B::BF16)
-          tile_dot2<B::T_QKV, B::H, true>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D,
+          tile_dot2<B::T_QKV, B::H, In::kF32Norm>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D,
                                           P.rms_eps, S.res, wave, lane);
         else tile_dot_lds<B, TQKV>(slotA, S.an, S.res, wave, lane);
       }
       mark(1);
       wsync();
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);  // slot A is free
-      gather(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
-             r * B::T_QKV, (r + 1) * B::T_QKV);
+      if (gather(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
+                 r * B::T_QKV, (r + 1) * B::T_QKV)) {
+        if constexpr (B::BF16) qk_part<B>(S, S.G[gc & 1] + B::H, S.G[gc & 1] + B::H + B::D, P.rms_eps, P.kv_bf16, wave, lane);
+      }
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
@@ -1297,15 +1384,18 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (wave < kDmaWaves)
         wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave) + dma_part_count(NI_GU, 4, 1, wave) +
                      dma_part_count(NI_GU, 4, 2, wave));
-      gather(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
-             P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
-             r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0);
+      if (gather(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
+                 P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+                 r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0)) {
+        if constexpr (B::BF16) combine_part<B>(S, nc, wave, lane);
+      }
       wsync();  // attention output of the group in LDS
       if (S.abort_) return;
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 3, wave, lane);
       // O partial (slot B)
       if (grp) {
-        if constexpr (B::BF16) tile_dot2<B::T_O, B::OC, false>(slotB, S.ov, nullptr, 0.f, S.res, wave, lane);
+        if constexpr (B::BF16) tile_dot2<B::T_O, B::OC, In::kSplit>(slotB, reinterpret_cast<const float*>(S.ov_hi),
+                                                              reinterpret_cast<const float*>(S.ov_lo), 0.f, S.res, wave, lane);
         else tile_dot_lds<B, TO>(slotB, S.ov, S.res, wave, lane);
       }
       mark(1);
@@ -1318,7 +1408,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (S.abort_) return;
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
       // gate / up (slot A)
-      if constexpr (B::BF16) tile_dot2<B::T_GU, B::H, true>(slotA, S.xs, S.G[gc & 1], P.rms_eps, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_GU, B::H, In::kF32Norm>(slotA, S.xs, S.G[gc & 1], P.rms_eps, S.res, wave, lane);
       else tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
@@ -1331,7 +1421,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (S.abort_) return;
       dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 1, wave, lane);
       // down partial (slot B)
-      if constexpr (B::BF16) tile_dot2<B::T_D, B::IX, false>(slotB, S.mv, nullptr, 0.f, S.res, wave, lane);
+      if constexpr (B::BF16) tile_dot2<B::T_D, B::IX, In::kF32>(slotB, S.mv, nullptr, 0.f, S.res, wave, lane);
       else tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
       mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
@@ -1412,8 +1502,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
   // them (not a traced phase); otherwise this wave polls all of it.  `active` is uniform
   // over the workgroup; the barrier is passed either way.
   constexpr bool kShare = lds_tiles<B>();
-  // the bf16 GEMVs with LDS tiles normalise their own inputs: only the LM head needs S.an
-  constexpr bool kNormHere = !(lds_tiles<B>() && B::BF16);
+  // bf16 GEMVs with LDS tiles: this wave takes an eighth of every GEMV and of the steps after
+  // the q/k/v and attention gathers; the GEMVs normalise their own inputs, so only the LM
+  // head reads S.an
+  constexpr bool kDots = lds_tiles<B>() && B::BF16;
+  constexpr bool kNormHere = !kDots;
   auto local_exchange = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1,
                             auto&& publish) -> bool {
     constexpr int NMAX = decltype(nmax)::value;
@@ -1581,10 +1674,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
     for (int l = 0; l < L; ++l) {
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
       // this wave's share of the bf16 GEMVs with tiles in LDS (the eighth row block)
-      constexpr bool kDots = lds_tiles<B>() && B::BF16;
       if constexpr (kDots) {
         if (grp)
-          tile_dot2<B::T_QKV, B::H, true>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D, eps, S.res,
+          tile_dot2<B::T_QKV, B::H, In::kF32Norm>(slotA, S.xs, l == 0 ? S.g_in0 : S.G[(gc - 1) & 1] + B::H + 2 * B::D, eps, S.res,
                                           kWorkerWaves, lane);
       }
       // ------------------------------------------------------------ q,k,v of the group
@@ -1599,7 +1691,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
           // per-head RMSNorm of q and k, rotation, rounding of the cache entry
           const float* qn = S.G[gc & 1] + B::H;
           const float* kn = S.G[gc & 1] + B::H + B::D;
-          if constexpr (B::D == 128) {
+          if constexpr (kDots) {
+            qk_part<B>(S, qn, kn, eps, P.kv_bf16, kWorkerWaves, lane);  // waves 0..3 take the heads
+          } else if constexpr (B::D == 128) {
             // lane i holds elements i and i + 64 of every head, which are rotary pair i:
             // norm and rotation stay in registers, the q heads and k side by side
             const float c = S.rope_c[lane], sn = S.rope_s[lane];
@@ -1729,8 +1823,11 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
           }
         };
         const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
-        if (local_exchange(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{}, xa, nc * B::QPG * (B::D + 2),
-                           tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk)) {
+        const bool got = local_exchange(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{}, xa,
+                                        nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk);
+        if constexpr (kDots) {
+          if (got) combine_part<B>(S, nc, kWorkerWaves, lane);
+        } else if (got) {
           // chunks four at a time: their loads are independent (chunks past nc weigh 0)
 #pragma unroll
           for (int h = 0; h < B::QPG; ++h) {
@@ -1762,7 +1859,8 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       if (!sync()) return;
       // ------------------------------------------------------------ O partials -> residual
       if constexpr (kDots) {
-        if (grp) tile_dot2<B::T_O, B::OC, false>(slotB, S.ov, nullptr, 0.f, S.res, kWorkerWaves, lane);
+        if (grp) tile_dot2<B::T_O, B::OC, In::kSplit>(slotB, reinterpret_cast<const float*>(S.ov_hi),
+                                                       reinterpret_cast<const float*>(S.ov_lo), 0.f, S.res, kWorkerWaves, lane);
       }
       if (!sync()) return;
       {
@@ -1798,7 +1896,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       }
       if (!sync()) return;
       // ------------------------------------------------------------ SwiGLU slice
-      if constexpr (kDots) tile_dot2<B::T_GU, B::H, true>(slotA, S.xs, S.G[gc & 1], eps, S.res, kWorkerWaves, lane);
+      if constexpr (kDots) tile_dot2<B::T_GU, B::H, In::kF32Norm>(slotA, S.xs, S.G[gc & 1], eps, S.res, kWorkerWaves, lane);
       if (!sync()) return;
       {
         constexpr int HALF = B::T_GU / 2;
@@ -1815,7 +1913,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       }
       if (!sync()) return;
       // ------------------------------------------------------------ down partials -> residual
-      if constexpr (kDots) tile_dot2<B::T_D, B::IX, false>(slotB, S.mv, nullptr, 0.f, S.res, kWorkerWaves, lane);
+      if constexpr (kDots) tile_dot2<B::T_D, B::IX, In::kF32>(slotB, S.mv, nullptr, 0.f, S.res, kWorkerWaves, lane);
       if (!sync()) return;
       {
         float* pp = &S.part[0][0][0];
