@@ -1372,11 +1372,12 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       }
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
-      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
-      // attention over the chunk
+      // attention over the chunk (its cache rows were loaded at the start of the layer; a
+      // copy issued before it would be waited for with them)
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
       dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 2, wave, lane);
       mark(0);
       wsync();
@@ -1407,34 +1408,31 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();  // residual after attention, normalised
       if (S.abort_) return;
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
+      // the next layer's gains: their buffer held those of the layer before this one, last
+      // read by this layer's q/k/v GEMV
+      dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
       // gate / up (slot A)
       if constexpr (B::BF16) tile_dot2<B::T_GU, B::H, In::kF32Norm>(slotA, S.xs, S.G[gc & 1], P.rms_eps, S.res, wave, lane);
       else tile_dot_lds<B, TGU>(slotA, S.an, S.res, wave, lane);
       mark(1);
       wsync();
-      dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
-      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 0, wave, lane);  // slot A is free
-      if (wave < kDmaWaves) wait_vmem_rt(dma_count(NI_GA, wave) + dma_part_count(NI_Q, 3, 0, wave));  // down tile landed
+      if (wave < kDmaWaves) wait_vmem_rt(dma_count(NI_GA, wave));  // down tile landed
       gather(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv,
              r * (B::T_GU / 2), (r + 1) * (B::T_GU / 2));
       wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return;
-      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 1, wave, lane);
+      dma_copy<TQKV::TOTAL>(A.qkv(ln), slotA, wave, lane);  // the next q/k/v tile: slot A is free
       // down partial (slot B)
       if constexpr (B::BF16) tile_dot2<B::T_D, B::IX, In::kF32>(slotB, S.mv, nullptr, 0.f, S.res, wave, lane);
       else tile_dot_lds<B, TD>(slotB, S.mv, S.res, wave, lane);
       mark(1);
       if (lm_now) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
       wsync();
-      dma_part<TQKV::TOTAL, 3>(A.qkv(ln), slotA, 2, wave, lane);
-      if (!lm_now) {
-        dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 0, wave, lane);  // slot B is free
-        if (wave < kDmaWaves) wait_vmem_rt(dma_part_count(NI_O, 2, 0, wave));  // next gains and q/k/v tile landed
-      }
+      if (!lm_now && wave < kDmaWaves) wait_vmem<0>();  // next gains and q/k/v tile landed
       gather(true, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D,
              (r + 1) * B::T_D);
       wsync();  // residual after the MLP, normalised for the next layer or the head
-      if (!lm_now) dma_part<TO::TOTAL, 2>(A.o(ln), slotB, 1, wave, lane);
+      if (!lm_now) dma_copy<TO::TOTAL>(A.o(ln), slotB, wave, lane);  // slot B is free
       ++gc;
       if (S.abort_) return;
     }
