@@ -426,6 +426,72 @@ __device__ __forceinline__ void tile_dot(const T& t, const float* act, float* re
   }
 }
 
+// A tile streamed from HBM through a ring of kRing chunks per lane: the first kRing
+// 1 KB loads of the wave's rows are issued ahead (stream_begin, one exchange before the
+// dot product), and the dot product issues load j + kRing as it consumes chunk j, so a
+// wave keeps kRing KB in flight instead of holding its whole share of the tile.  The
+// loads are buffer loads over the wave's rows (one lane offset, the chunk in the
+// constant offset, so no address registers per chunk; past the tile they read 0).
+constexpr int kRing = 8;
+constexpr int kNonTemporal = 2;  // cache-policy bit of a buffer load: streamed
+struct Ring {
+  u4 v[kRing];
+  __amdgpu_buffer_rsrc_t src;
+  int last;  // byte offset of the wave's last 1 KB instruction: later chunks re-read it
+};
+// Chunk j of the wave's rows (instructions past its rows re-read its last one: every load
+// stays inside the tile, and the dot product ignores them).
+template <class T>
+__device__ __forceinline__ u4 stream_load(const Ring& q, int j, int lane) {
+  return __builtin_amdgcn_raw_buffer_load_b128(q.src, lane * 16, min(j * 1024, q.last), kNonTemporal);
+}
+template <class T>
+__device__ __forceinline__ void stream_begin(Ring& q, const uint8_t* base, int wave, int lane) {
+  static_assert(T::CPW % 64 == 0 && T::TOTAL % 64 == 0 && T::TOTAL >= 64, "whole 1 KB instructions");
+  // the wave's rows; a wave past the last row reads the tile's last instruction (ignored)
+  const int start = min(min(wave, T::NWA - 1) * T::CPW, T::TOTAL - 64);
+  const int chunks = min(T::CPW, T::TOTAL - start);
+  q.src = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base) + (size_t)start * 16, (short)0, chunks * 16,
+                                            0x00020000);
+  q.last = (chunks / 64 - 1) * 1024;
+#pragma unroll
+  for (int j = 0; j < kRing; ++j)
+    if (j < T::LPL) q.v[j] = stream_load<T>(q, j, lane);
+}
+// Row results of the wave's rows go to res[wave*RPW + r] (LDS), as tile_dot.
+template <class B, class T>
+__device__ __forceinline__ void stream_dot(Ring& q, const float* act, float* res, int wave, int lane) {
+  if (wave >= T::NWA) return;  // (its ring loads are in bounds and simply not used)
+  float acc[T::RPW];
+#pragma unroll
+  for (int r = 0; r < T::RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < T::LPL; ++j) {
+    const u4 w = q.v[j % kRing];
+    if (j + kRing < T::LPL) q.v[j % kRing] = stream_load<T>(q, j + kRing, lane);
+    const int k = j * 64 + lane;
+    if (T::EXACT || (k < T::CPW && wave * T::CPW + k < T::TOTAL)) {
+      const int row = k / T::CPR;
+      const int col = (k - row * T::CPR) * B::E;
+      const float d = dot_chunk<B>(w, act + col);
+      if constexpr (T::CPR % 64 == 0) {
+        acc[(j * 64) / T::CPR] += d;
+      } else {
+#pragma unroll
+        for (int r = 0; r < T::RPW; ++r) acc[r] += (row == r) ? d : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < T::RPW; ++r) acc[r] = wave_sum(acc[r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < T::RPW; ++r)
+      if (wave * T::RPW + r < T::TOTAL / T::CPR)
+        res[wave * T::RPW + r] = acc[r];
+  }
+}
+
 // tile_dot with the tile in LDS: chunk g of the tile at slot[g].
 template <class B, class T>
 __device__ __forceinline__ void tile_dot_lds(const u4* slot, const float* act, float* res, int wave, int lane) {
@@ -1133,15 +1199,12 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
   const int b = blockIdx.x;
   const int rpb = (P.vocab + kGrid - 1) / kGrid;
   const int lm0 = b * rpb, lm1 = min(P.vocab, lm0 + rpb);
-  constexpr bool LA = false;  // tiles one phase ahead (the whole layer does not fit)
   __builtin_assume(wave >= 0 && wave < kWorkerWaves);
 
   // Every load below is unconditional (addresses clamped in bounds): a conditional
-  // load would make the compiler copy the tile registers and wait for them.
-  TQKV tq;
-  TO to;
-  TGU tg;
-  TD td;
+  // load would make the compiler copy the registers and wait for them.  One ring streams
+  // every tile: its head is loaded right after the dot product before, one exchange ahead.
+  Ring q;
   TLM tl;
   // Gains block of the layer entered next, held in registers one layer ahead and
   // written to LDS (G[layer count % 2]) at that layer's first phase.
@@ -1156,6 +1219,19 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
     for (int k = 0; k < GPT; ++k) r_g[k] = g[min(tid + NT * k, NGF - 1)];
   };
   int gc = 0;  // layers entered since the launch started
+  // phase trace: worker wave 0 of the traced workgroup stamps, for the barrier it is about
+  // to reach, when its dot product finished and when it arrived
+  const bool trace = phase_traced(P, b) && wave == 0 && lane == 0;
+  const int n_sync = 2 + 10 * L;
+  int cur_t = 0, ph = 0;
+  auto mark = [&](int k) {
+    if (trace) phase_record(P, b, cur_t, n_sync, ph)[4 + k] = wall_clock64();
+  };
+  auto wsync = [&]() {
+    mark(2);
+    __syncthreads();
+    ++ph;
+  };
   auto gstore = [&]() {
     float* G = S.G[gc & 1];
 #pragma unroll
@@ -1163,63 +1239,57 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       if (tid + NT * k < NGF) G[tid + NT * k] = r_g[k];
   };
   gload(0);
-  tile_load(tq, A.qkv(0), wave, lane);
-  if constexpr (LA) {
-    tile_load(to, A.o(0), wave, lane);
-    tile_load(tg, A.gu(0), wave, lane);
-    tile_load(td, A.down(0), wave, lane);
-  }
+  stream_begin<TQKV>(q, A.qkv(0), wave, lane);
 
   for (int t = 0; t < P.n_pos; ++t) {
     const int p = P.pos0 + t;
     const bool lm = t >= P.logits_from;
-    __syncthreads();  // input fetched
+    cur_t = t;
+    ph = 0;
+    wsync();  // input fetched
     if (S.abort_) return;
     auto layer = [&](int l, auto last) -> bool {
       const int ln = (l + 1 < L) ? l + 1 : 0;
       // q, k, v rows
       gstore();
-      if (grp) tile_dot<B>(tq, S.an, S.res, wave, lane);
+      if (grp) stream_dot<B, TQKV>(q, S.an, S.res, wave, lane);
+      mark(1);
       gload(ln);
-      if constexpr (!LA) tile_load(to, A.o(l), wave, lane);
-      __syncthreads();
-      __syncthreads();  // q rotated, k/v of position p in LDS
+      stream_begin<TO>(q, A.o(l), wave, lane);
+      wsync();
+      wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return false;
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over this rank's chunk of positions
       const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
       if (grp && r < nc) attention_chunk<B, false>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane, KvBatch<B>{});
-      __syncthreads();
-      __syncthreads();  // attention output of the group in LDS
+      wsync();
+      wsync();  // attention output of the group in LDS
       if (S.abort_) return false;
       // O partial
-      if (grp) tile_dot<B>(to, S.ov, S.res, wave, lane);
-      if constexpr (LA) {
-        tile_load(tq, A.qkv(ln), wave, lane);
-        tile_load(to, A.o(ln), wave, lane);
-      } else {
-        tile_load(tg, A.gu(l), wave, lane);
-      }
-      __syncthreads();
-      __syncthreads();  // residual after attention, normalised
+      if (grp) stream_dot<B, TO>(q, S.ov, S.res, wave, lane);
+      mark(1);
+      stream_begin<TGU>(q, A.gu(l), wave, lane);
+      wsync();
+      wsync();  // residual after attention, normalised
       if (S.abort_) return false;
       // gate / up
-      tile_dot<B>(tg, S.an, S.res, wave, lane);
-      if constexpr (LA) tile_load(tg, A.gu(ln), wave, lane);
-      else tile_load(td, A.down(l), wave, lane);
-      __syncthreads();
-      __syncthreads();  // SwiGLU slice of the XCD
+      stream_dot<B, TGU>(q, S.an, S.res, wave, lane);
+      mark(1);
+      stream_begin<TD>(q, A.down(l), wave, lane);
+      wsync();
+      wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return false;
       // down partial
-      tile_dot<B>(td, S.mv, S.res, wave, lane);
-      if constexpr (LA) tile_load(td, A.down(ln), wave, lane);
-      else tile_load(tq, A.qkv(ln), wave, lane);
+      stream_dot<B, TD>(q, S.mv, S.res, wave, lane);
+      mark(1);
+      stream_begin<TQKV>(q, A.qkv(ln), wave, lane);
       if constexpr (decltype(last)::value) {
         if (lm) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
       }
-      __syncthreads();
-      __syncthreads();  // residual after the MLP, normalised for the next layer or the head
+      wsync();
+      wsync();  // residual after the MLP, normalised for the next layer or the head
       ++gc;
       return S.abort_ == 0;
     };
@@ -1240,7 +1310,7 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
         lm_dot<B>(t2, S.an, rb + LMR, lm1, wave, lane, bv, bi);
       }
       if (lane == 0) { S.wbest_v[wave] = bv; S.wbest_i[wave] = bi; }
-      __syncthreads();
+      wsync();
     }
   }
 }
