@@ -1232,6 +1232,21 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
     __syncthreads();
     ++ph;
   };
+  // Waves 4..6 poll parts 1..3 of the gathers inside the XCD (the control wave polls part
+  // 0); a barrier joins them.  They have no load in flight when they poll (a wave's
+  // vector-memory counter is in order): they start their next tile's ring, and any other
+  // load of the segment, after their part of the gather.
+  const bool poller = wave >= kWorkerWaves - (kPollWaves - 1);
+  const int part = wave - (kWorkerWaves - kPollWaves);
+  const uint32_t tpp = tags_per_position(L);
+  auto poll = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1) {
+    constexpr int NMAX = decltype(nmax)::value;
+    if (active && poller) {
+      if (!help_gather<Kp<NMAX, kPollWaves>::value>(src, n, tag, dst, own0, own1, part, lane, P) && lane == 0)
+        S.abort_ = 1;
+      vmem_drain();
+    }
+  };
   auto gstore = [&]() {
     float* G = S.G[gc & 1];
 #pragma unroll
@@ -1246,49 +1261,79 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
     const bool lm = t >= P.logits_from;
     cur_t = t;
     ph = 0;
+    const uint32_t tbase = P.tag0 + 1 + (uint32_t)t * tpp;
     wsync();  // input fetched
     if (S.abort_) return;
     auto layer = [&](int l, auto last) -> bool {
       const int ln = (l + 1 < L) ? l + 1 : 0;
+      const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
+      const int nc = n_chunks(p);
       // q, k, v rows
       gstore();
       if (grp) stream_dot<B, TQKV>(q, S.an, S.res, wave, lane);
       mark(1);
-      gload(ln);
-      stream_begin<TO>(q, A.o(l), wave, lane);
+      if (!poller) {
+        gload(ln);
+        stream_begin<TO>(q, A.o(l), wave, lane);
+      }
       wsync();
+      poll(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
+           r * B::T_QKV, (r + 1) * B::T_QKV);
+      if (poller) {
+        gload(ln);
+        stream_begin<TO>(q, A.o(l), wave, lane);
+      }
+      __syncthreads();
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return false;
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over this rank's chunk of positions
-      const int nc = n_chunks(p);
       const int csz = (p + 1 + nc - 1) / nc;
       if (grp && r < nc) attention_chunk<B, false>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane, KvBatch<B>{});
       wsync();
+      poll(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
+           P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+           r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0);
+      __syncthreads();
       wsync();  // attention output of the group in LDS
       if (S.abort_) return false;
       // O partial
       if (grp) stream_dot<B, TO>(q, S.ov, S.res, wave, lane);
       mark(1);
-      stream_begin<TGU>(q, A.gu(l), wave, lane);
+      if (!poller) stream_begin<TGU>(q, A.gu(l), wave, lane);
       wsync();
+      poll(true, std::integral_constant<int, B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O,
+           (r + 1) * B::T_O);
+      if (poller) stream_begin<TGU>(q, A.gu(l), wave, lane);
+      __syncthreads();
       wsync();  // residual after attention, normalised
       if (S.abort_) return false;
       // gate / up
       stream_dot<B, TGU>(q, S.an, S.res, wave, lane);
       mark(1);
-      stream_begin<TD>(q, A.down(l), wave, lane);
+      if (!poller) stream_begin<TD>(q, A.down(l), wave, lane);
       wsync();
+      poll(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv,
+           r * (B::T_GU / 2), (r + 1) * (B::T_GU / 2));
+      if (poller) stream_begin<TD>(q, A.down(l), wave, lane);
+      __syncthreads();
       wsync();  // SwiGLU slice of the XCD
       if (S.abort_) return false;
       // down partial
       stream_dot<B, TD>(q, S.mv, S.res, wave, lane);
       mark(1);
-      stream_begin<TQKV>(q, A.qkv(ln), wave, lane);
-      if constexpr (decltype(last)::value) {
-        if (lm) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
-      }
+      auto ahead = [&]() {
+        stream_begin<TQKV>(q, A.qkv(ln), wave, lane);
+        if constexpr (decltype(last)::value) {
+          if (lm) lm_load<B>(tl, P, lm0, lm1, wave, lane);  // first LM head pass, ahead of the last exchange
+        }
+      };
+      if (!poller) ahead();
       wsync();
+      poll(true, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D,
+           (r + 1) * B::T_D);
+      if (poller) ahead();
+      __syncthreads();
       wsync();  // residual after the MLP, normalised for the next layer or the head
       ++gc;
       return S.abort_ == 0;
@@ -1565,11 +1610,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
     if (!ok) fail();
     return ok;
   };
-  // A gather inside the XCD (at most NMAX words).  With the tiles in LDS, worker waves 4..6
-  // poll three of its four parts (this wave publishes and polls part 0) and a barrier joins
-  // them (not a traced phase); otherwise this wave polls all of it.  `active` is uniform
-  // over the workgroup; the barrier is passed either way.
-  constexpr bool kShare = lds_tiles<B>();
+  // A gather inside the XCD (at most NMAX words): worker waves 4..6 poll three of its four
+  // parts (this wave publishes and polls part 0) and a barrier joins them (not a traced
+  // phase).  `active` is uniform over the workgroup; the barrier is passed either way.
+  constexpr bool kShare = true;
   // bf16 GEMVs with LDS tiles: this wave takes an eighth of every GEMV and of the steps after
   // the q/k/v and attention gathers; the GEMVs normalise their own inputs, so only the LM
   // head reads S.an
