@@ -830,6 +830,38 @@ __device__ __forceinline__ void qk_part(Lds<B>& S, const float* qn, const float*
   }
 }
 
+// RMSNorm of x with gains g into out (fp32), wave pw writing chunks [pw*H/64, ...): every
+// wave sums the squares of all of x in norm_out's order, so all use one scale.
+template <class B>
+__device__ __forceinline__ void norm_out_part(const float* x, const float* g, float* out, float eps, int pw, int lane) {
+  constexpr int NCH = B::H / 8, CPL = NCH / 64, CPW = NCH / 8;
+  static_assert(NCH % 64 == 0 && CPW <= 64, "whole chunks per lane and per wave");
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f4 v = *reinterpret_cast<const f4*>(x + 8 * c + 4 * e);
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  const float rs = __builtin_amdgcn_rsqf(ss / (float)B::H + eps);
+  if (lane < CPW) {
+    const int c = pw * CPW + lane;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f4 v = *reinterpret_cast<const f4*>(x + 8 * c + 4 * e);
+      const f4 gg = *reinterpret_cast<const f4*>(g + 8 * c + 4 * e);
+      *reinterpret_cast<f4*>(out + 8 * c + 4 * e) = f4{gg.x * (v.x * rs), gg.y * (v.y * rs), gg.z * (v.z * rs), gg.w * (v.w * rs)};
+    }
+  }
+}
+
 // The group's attention output from the nc chunk partials in S.part, split for the O
 // GEMV: wave pw takes output columns [pw*QPG*D/8, ...) (lane = column), combined in chunk
 // order; then four of its lanes split the columns 8 at a time.
@@ -1237,6 +1269,8 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
   // vector-memory counter is in order): they start their next tile's ring, and any other
   // load of the segment, after their part of the gather.
   const bool poller = wave >= kWorkerWaves - (kPollWaves - 1);
+  // the steps after the q/k/v, attention and residual gathers, shared by the eight waves
+  constexpr bool kSteps = B::BF16 && B::D == 128;
   const int part = wave - (kWorkerWaves - kPollWaves);
   const uint32_t tpp = tags_per_position(L);
   auto poll = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1) {
@@ -1284,6 +1318,9 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
         stream_begin<TO>(q, A.o(l), wave, lane);
       }
       __syncthreads();
+      if constexpr (kSteps) {
+        if (grp && S.abort_ == 0) qk_part<B>(S, S.G[gc & 1] + B::H, S.G[gc & 1] + B::H + B::D, P.rms_eps, P.kv_bf16, wave, lane);
+      }
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return false;
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
@@ -1295,6 +1332,9 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
            P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
            r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0);
       __syncthreads();
+      if constexpr (kSteps) {
+        if (grp && S.abort_ == 0) combine_part<B>(S, nc, wave, lane);
+      }
       wsync();  // attention output of the group in LDS
       if (S.abort_) return false;
       // O partial
@@ -1306,6 +1346,9 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
            (r + 1) * B::T_O);
       if (poller) stream_begin<TGU>(q, A.gu(l), wave, lane);
       __syncthreads();
+      if constexpr (kSteps) {
+        if (S.abort_ == 0) norm_out_part<B>(S.xs, S.G[gc & 1], S.an, P.rms_eps, wave, lane);
+      }
       wsync();  // residual after attention, normalised
       if (S.abort_) return false;
       // gate / up
@@ -1334,6 +1377,9 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
            (r + 1) * B::T_D);
       if (poller) ahead();
       __syncthreads();
+      if constexpr (kSteps) {
+        if (S.abort_ == 0) norm_out_part<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, P.rms_eps, wave, lane);
+      }
       wsync();  // residual after the MLP, normalised for the next layer or the head
       ++gc;
       return S.abort_ == 0;
@@ -1619,6 +1665,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
   // head reads S.an
   constexpr bool kDots = lds_tiles<B>() && B::BF16;
   constexpr bool kNormHere = !kDots;
+  // the steps after the q/k/v, attention and (register tiles) residual gathers are shared by
+  // the eight waves, this one taking share 7
+  constexpr bool kSteps = B::BF16 && B::D == 128;
   auto local_exchange = [&](bool active, auto nmax, const u64* src, int n, uint32_t tag, float* dst, int own0, int own1,
                             auto&& publish) -> bool {
     constexpr int NMAX = decltype(nmax)::value;
@@ -1803,7 +1852,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
           // per-head RMSNorm of q and k, rotation, rounding of the cache entry
           const float* qn = S.G[gc & 1] + B::H;
           const float* kn = S.G[gc & 1] + B::H + B::D;
-          if constexpr (kDots) {
+          if constexpr (kSteps) {
             qk_part<B>(S, qn, kn, eps, P.kv_bf16, kWorkerWaves, lane);  // waves 0..3 take the heads
           } else if constexpr (B::D == 128) {
             // lane i holds elements i and i + 64 of every head, which are rotary pair i:
@@ -1937,7 +1986,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
         const int own0 = r < nc ? r * B::QPG * (B::D + 2) : 0, own1 = r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0;
         const bool got = local_exchange(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{}, xa,
                                         nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0], own0, own1, publish_chunk);
-        if constexpr (kDots) {
+        if constexpr (kSteps) {
           if (got) combine_part<B>(S, nc, kWorkerWaves, lane);
         } else if (got) {
           // chunks four at a time: their loads are independent (chunks past nc weigh 0)
@@ -2000,7 +2049,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
                              st_local(lane < B::T_O ? P.xxa + (size_t)x * B::H + r * B::T_O + lane : sink, nv, tg0 + 3, lp);
                              if (lane < B::T_O) S.xs[r * B::T_O + lane] = nv;
                            })) {
-          if constexpr (kNormHere) {
+          if constexpr (kSteps && kNormHere) {
+            norm_out_part<B>(S.xs, S.G[gc & 1], S.an, eps, kWorkerWaves, lane);
+          } else if constexpr (kNormHere) {
             if constexpr (B::BF16) norm_out<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
             else norm_to<B>(S.xs, S.G[gc & 1], S.an, eps, lane);
           }
@@ -2048,7 +2099,9 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
                              if (lane < B::T_D) S.xs[r * B::T_D + lane] = nv;
                            })) {
           // the next layer's input norm, or the final norm ahead of the LM head
-          if (kNormHere || l + 1 == L) {
+          if constexpr (kSteps && kNormHere) {
+            norm_out_part<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, kWorkerWaves, lane);
+          } else if (kNormHere || l + 1 == L) {
             if constexpr (B::BF16) norm_out<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
             else norm_to<B>(S.xs, S.G[gc & 1] + B::H + 2 * B::D, S.an, eps, lane);
           }
