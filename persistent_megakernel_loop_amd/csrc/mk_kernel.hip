@@ -246,9 +246,10 @@ __device__ __forceinline__ void raise_timeout(const Params& P, const unsigned lo
   }
 }
 
-// Loads per lane per poll round for an exchange of at most N words polled by NP waves.
-template <int N, int NP = 1>
-struct Kp : std::integral_constant<int, (N + 64 * NP - 1) / (64 * NP) < 8 ? (N + 64 * NP - 1) / (64 * NP) : 8> {};
+// Loads per lane per poll round for an exchange of at most N words polled by NP waves: at
+// most 8.
+template <int N, int NP = 1, int CAP = 8>
+struct Kp : std::integral_constant<int, (N + 64 * NP - 1) / (64 * NP) < CAP ? (N + 64 * NP - 1) / (64 * NP) : CAP> {};
 // Waves that poll the gathers inside an XCD in the LDS-tile bodies: the control wave and
 // worker waves 4..6 (which have no weight copy in flight).
 constexpr int kPollWaves = 4;
@@ -723,6 +724,7 @@ struct Lds {
   alignas(16) float part[kPerXcd][B::QPG][B::D + 2];        // chunk partials read back for the combine
   alignas(16) float wpart[kWorkerWaves][B::QPG][B::D + 2];  // per-wave attention partials
   alignas(16) float attw[kWorkerWaves][16];                 // per-wave softmax weights of a batch
+  alignas(16) float chw[kWorkerWaves + 1][64];              // per-wave chunk weights of the combine
   float wbest_v[kWorkerWaves];
   int wbest_i[kWorkerWaves];
   alignas(16) float g_in0[B::H];         // input norm of layer 0 (constant for the launch)
@@ -863,33 +865,32 @@ __device__ __forceinline__ void norm_out_part(const float* x, const float* g, fl
 }
 
 // The group's attention output from the nc chunk partials in S.part, split for the O
-// GEMV: wave pw takes output columns [pw*QPG*D/8, ...) (lane = column), combined in chunk
-// order; then four of its lanes split the columns 8 at a time.
+// GEMV: wave pw takes output columns [pw*QPG*D/8, ...) of one head.  Lane c first works
+// out chunk c's weight exp(m_c - M) (M the largest chunk maximum) and the weights go
+// through LDS; then lane = column sums the chunks' vectors in chunk order, and four lanes
+// split the wave's columns 8 at a time.
 template <class B>
 __device__ __forceinline__ void combine_part(Lds<B>& S, int nc, int pw, int lane) {
   constexpr int CW = B::OC / 8;  // columns per wave
-  static_assert(CW <= 64 && CW % 8 == 0 && B::D % CW == 0, "columns per wave");
+  static_assert(CW <= 64 && CW % 8 == 0 && B::D % CW == 0 && kPerXcd <= 64, "columns per wave, a chunk per lane");
   const int col = pw * CW + lane, h = (pw * CW) / B::D, d = col - h * B::D;
+  const int cl = min(lane, nc - 1);
+  const float mc = lane < nc ? S.part[cl][h][0] : -INFINITY;
+  const float M = wave_max(mc);
+  const float f = (lane < nc && mc != -INFINITY) ? __expf(mc - M) : 0.f;
+  const float Ls = wave_sum(S.part[cl][h][1] * f);
+  S.chw[pw][lane] = f;  // this wave's own LDS writes are seen by its later reads
   if (lane < CW) {
-    float M = -INFINITY;
+    float a = 0.f;
     for (int c0 = 0; c0 < nc; c0 += 4) {
-#pragma unroll
-      for (int c = c0; c < c0 + 4; ++c) M = fmaxf(M, c < nc ? S.part[c][h][0] : -INFINITY);
-    }
-    float Ls = 0.f, a = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 4) {
-#pragma unroll
-      for (int c = c0; c < c0 + 4; ++c) {
-        const int cc = min(c, nc - 1);
-        const float mc = S.part[cc][h][0];
-        const float f = (c < nc && mc != -INFINITY) ? __expf(mc - M) : 0.f;
-        Ls = fmaf(S.part[cc][h][1], f, Ls);
-        a = fmaf(S.part[cc][h][2 + d], f, a);
-      }
+      const f4 w = *reinterpret_cast<const f4*>(&S.chw[pw][c0]);  // zero past nc
+      a = fmaf(S.part[min(c0 + 0, nc - 1)][h][2 + d], w.x, a);
+      a = fmaf(S.part[min(c0 + 1, nc - 1)][h][2 + d], w.y, a);
+      a = fmaf(S.part[min(c0 + 2, nc - 1)][h][2 + d], w.z, a);
+      a = fmaf(S.part[min(c0 + 3, nc - 1)][h][2 + d], w.w, a);
     }
     S.ov[col] = a * __builtin_amdgcn_rcpf(Ls);
   }
-  // this wave's own LDS writes are seen by its later reads
   if (lane < CW / 8) split8(S.ov + pw * CW + 8 * lane, S.ov_hi[pw * (CW / 8) + lane], S.ov_lo[pw * (CW / 8) + lane]);
 }
 
@@ -1132,10 +1133,7 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
   };
   const KvRange<B> R = kv_range<B>(P, x, l, c0, c1, wave);
   const int w0 = R.w0, w1 = R.w1;
-  for (int jb = w0; jb < w1; jb += PB) {
-    KvBatch<B> kb;
-    if (PREFETCHED && jb == w0) kb = first;
-    else kv_batch_load<B>(R, jb, lane, kb);
+  auto batch = [&](const KvBatch<B>& kb, int jb) {
     const int nb = min(PB, w1 - jb);  // positions of this batch (uniform)
     float sc[PB][B::QPG], vf[PB][DPL];
     // every slot of the batch is computed (branch-free, so the wave sums interleave);
@@ -1205,7 +1203,26 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
       }
       m[h] = mn;
     }
+  };
+  // The loads of the next batch, if there is one, are issued before this one is computed;
+  // it moves into place after (that copy waits for it, when it is needed anyway), so no
+  // load is left in flight past the loop.
+  if (w0 < w1) {
+    KvBatch<B> cur, nxt;
+    if constexpr (PREFETCHED) cur = first;
+    else kv_batch_load<B>(R, w0, lane, cur);
+    for (int jb = w0;; jb += PB) {
+      const bool more = jb + PB < w1;
+      if (more) kv_batch_load<B>(R, jb + PB, lane, nxt);
+      batch(cur, jb);
+      if (!more) break;
+      cur = nxt;
+    }
   }
+  // Nothing of the wave's is in flight now but copies issued an exchange ago.  A wait the
+  // compiler sees keeps it from assuming a batch load is still pending further on, where it
+  // would wait for it (and for every later copy) before the next GEMV.
+  vmem_drain();
 #pragma unroll
   for (int h = 0; h < B::QPG; ++h) {
 #pragma unroll
