@@ -335,15 +335,20 @@ __device__ __forceinline__ bool exchange(const u64* src, int n, uint32_t tag, fl
   return true;
 }
 
-// A worker wave's share (part 1..kPollWaves-1) of a gather the control wave publishes
-// into; false if the wait gave up.
-template <int KP>
+// A worker wave's share (part 1..NP-1) of a gather the control wave publishes into;
+// false if the wait gave up.
+template <int KP, int NP = kPollWaves>
 __device__ __forceinline__ bool help_gather(const u64* src, int n, uint32_t tag, float* dst, int own0, int own1, int part,
                                             int lane, const Params& P) {
   uint32_t rounds = 0;
   unsigned long long r1 = 0;
-  return exchange<KP, kPollWaves>(src, n, tag, dst, own0, own1, [] {}, lane, P, rounds, r1, part);
+  return exchange<KP, NP>(src, n, tag, dst, own0, own1, [] {}, lane, P, rounds, r1, part);
 }
+// The attention-chunk gather of the LDS-tile bodies is polled by all eight waves (the
+// control wave part 0, worker wave w part w + 1): the copy waves issue that segment's
+// copies after their part.  Long contexts gather 32 chunks there.
+template <class B>
+constexpr int comb_parts() { return B::H <= 1024 ? kWorkerWaves + 1 : kPollWaves; }
 
 // Phase trace: one workgroup (dbg_phase_wg >= 0, records [n][n_sync][8]) or every
 // workgroup (dbg_phase_wg < 0, records [n][grid][n_sync][8]).
@@ -1555,18 +1560,27 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       // copy issued before it would be waited for with them)
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
-      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
-      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 2, wave, lane);
-      mark(0);
       wsync();
-      // the O tile (and every copy before the gate/up parts) has landed
-      if (wave < kDmaWaves)
-        wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave) + dma_part_count(NI_GU, 4, 1, wave) +
-                     dma_part_count(NI_GU, 4, 2, wave));
-      if (gather(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
-                 P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
-                 r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0)) {
-        if constexpr (B::BF16) combine_part<B>(S, nc, wave, lane);
+      // the attention chunks, polled by every wave: no copy in flight (the O tile and gate/up
+      // part 0 have landed), then the copy waves issue gate/up parts 1 and 2
+      {
+        constexpr int NC = kPerXcd * B::QPG * (B::D + 2);
+        static_assert(comb_parts<B>() == kWorkerWaves + 1, "every wave polls the chunks");
+        if (wave < kDmaWaves) wait_vmem<0>();
+        if (grp && !help_gather<Kp<NC, kWorkerWaves + 1>::value, kWorkerWaves + 1>(
+                       P.xatt + (size_t)x * NC, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+                       r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0, wave + 1, lane,
+                       P) &&
+            lane == 0)
+          S.abort_ = 1;
+        vmem_drain();
+        mark(0);
+        dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
+        dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 2, wave, lane);
+        __syncthreads();
+        if constexpr (B::BF16) {
+          if (grp && S.abort_ == 0) combine_part<B>(S, nc, wave, lane);
+        }
       }
       wsync();  // attention output of the group in LDS
       if (S.abort_) return;
@@ -1677,6 +1691,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
   // parts (this wave publishes and polls part 0) and a barrier joins them (not a traced
   // phase).  `active` is uniform over the workgroup; the barrier is passed either way.
   constexpr bool kShare = true;
+  constexpr int kCombParts = comb_parts<B>();
   // bf16 GEMVs with LDS tiles: this wave takes an eighth of every GEMV and of the steps after
   // the q/k/v and attention gathers; the GEMVs normalise their own inputs, so only the LM
   // head reads S.an
@@ -1689,10 +1704,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
                             auto&& publish) -> bool {
     constexpr int NMAX = decltype(nmax)::value;
     if constexpr (kShare) {
+      constexpr int NP = NMAX == kPerXcd * B::QPG * (B::D + 2) ? kCombParts : kPollWaves;
       bool ok = true;
       if (active)
-        ok = timed_exchange(Kp<NMAX, kPollWaves>{}, std::integral_constant<int, kPollWaves>{}, src, n, tag, dst, own0,
-                            own1, publish);
+        ok = timed_exchange(Kp<NMAX, NP>{}, std::integral_constant<int, NP>{}, src, n, tag, dst, own0, own1, publish);
       __syncthreads();
       return active && ok && S.abort_ == 0;
     } else {
