@@ -1534,6 +1534,9 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
       KvBatch<B> kb;
       if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
+      // this layer's O tile, behind the cache rows (slot B has been free since the last
+      // down GEMV; layer 0's tile was copied before the position)
+      if (l > 0) dma_copy<TO::TOTAL>(A.o(l), slotB, wave, lane);
       // Weight copies are spread over the layer's phases, about 12 KB per phase, so that
       // no exchange polls behind a large burst in this CU's memory queue: each tile is
       // copied in parts as soon as its slot is free, and waited for before the barrier
@@ -1624,7 +1627,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       gather(true, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D,
              (r + 1) * B::T_D);
       wsync();  // residual after the MLP, normalised for the next layer or the head
-      if (!lm_now) dma_copy<TO::TOTAL>(A.o(ln), slotB, wave, lane);  // slot B is free
+      if (!lm && l + 1 == L) dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);  // the next position's layer 0
       ++gc;
       if (S.abort_) return;
     }
