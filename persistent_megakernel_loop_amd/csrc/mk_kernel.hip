@@ -344,11 +344,12 @@ __device__ __forceinline__ bool help_gather(const u64* src, int n, uint32_t tag,
   unsigned long long r1 = 0;
   return exchange<KP, NP>(src, n, tag, dst, own0, own1, [] {}, lane, P, rounds, r1, part);
 }
-// The attention-chunk gather of the LDS-tile bodies is polled by all eight waves (the
-// control wave part 0, worker wave w part w + 1): the copy waves issue that segment's
-// copies after their part.  Long contexts gather 32 chunks there.
+// The attention-chunk gather is polled by all eight waves (the control wave part 0, worker
+// wave w part w + 1): in the LDS-tile bodies the copy waves issue that segment's copies
+// after their part; in the register-tile body the ring heads in flight then were issued
+// an exchange and the attention earlier.  Long contexts gather 32 chunks there.
 template <class B>
-constexpr int comb_parts() { return B::H <= 1024 ? kWorkerWaves + 1 : kPollWaves; }
+constexpr int comb_parts() { return kWorkerWaves + 1; }
 
 // Phase trace: one workgroup (dbg_phase_wg >= 0, records [n][n_sync][8]) or every
 // workgroup (dbg_phase_wg < 0, records [n][grid][n_sync][8]).
@@ -1324,6 +1325,13 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
       const int nc = n_chunks(p);
+      const int csz = (p + 1 + nc - 1) / nc;
+      const bool attn = grp && r < nc;
+      const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
+      // the first batch of this rank's cache rows (waves 4..6: after their part of the
+      // q/k/v gather)
+      KvBatch<B> kb;
+      if (attn && !poller) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // q, k, v rows
       gstore();
       if (grp) stream_dot<B, TQKV>(q, S.an, S.res, wave, lane);
@@ -1336,6 +1344,7 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       poll(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
            r * B::T_QKV, (r + 1) * B::T_QKV);
       if (poller) {
+        if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
         gload(ln);
         stream_begin<TO>(q, A.o(l), wave, lane);
       }
@@ -1347,12 +1356,19 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
       if (S.abort_) return false;
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // attention over this rank's chunk of positions
-      const int csz = (p + 1 + nc - 1) / nc;
-      if (grp && r < nc) attention_chunk<B, false>(P, S, x, l, p, r * csz, min(p + 1, r * csz + csz), wave, lane, KvBatch<B>{});
+      if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       wsync();
-      poll(grp, std::integral_constant<int, kPerXcd * B::QPG * (B::D + 2)>{},
-           P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2), nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
-           r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0);
+      {  // the attention chunks, polled by every wave
+        constexpr int NC = kPerXcd * B::QPG * (B::D + 2);
+        static_assert(comb_parts<B>() == kWorkerWaves + 1, "every wave polls the chunks");
+        if (grp && !help_gather<Kp<NC, kWorkerWaves + 1>::value, kWorkerWaves + 1>(
+                       P.xatt + (size_t)x * NC, nc * B::QPG * (B::D + 2), tg0 + 1, &S.part[0][0][0],
+                       r < nc ? r * B::QPG * (B::D + 2) : 0, r < nc ? (r + 1) * B::QPG * (B::D + 2) : 0, wave + 1, lane,
+                       P) &&
+            lane == 0)
+          S.abort_ = 1;
+        vmem_drain();
+      }
       __syncthreads();
       if constexpr (kSteps) {
         if (grp && S.abort_ == 0) combine_part<B>(S, nc, wave, lane);
