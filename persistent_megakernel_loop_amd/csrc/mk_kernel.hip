@@ -484,8 +484,16 @@ __device__ __forceinline__ void stream_dot(Ring& q, const float* act, float* res
       if constexpr (T::CPR % 64 == 0) {
         acc[(j * 64) / T::CPR] += d;
       } else {
+        // the 64 chunks of load j span rows r0 and at most r0 + 1; once the loops are
+        // unrolled r0 is a constant and only those two accumulators are touched
+        static_assert(T::CPR >= 64 || (64 % T::CPR == 0 && T::CPR >= 32), "two rows per load at most");
+        const int r0 = (j * 64) / T::CPR;
+        const bool next = row > r0;
 #pragma unroll
-        for (int r = 0; r < T::RPW; ++r) acc[r] += (row == r) ? d : 0.f;
+        for (int r = 0; r < T::RPW; ++r) {
+          if (r == r0) acc[r] += next ? 0.f : d;
+          else if (r == r0 + 1) acc[r] += next ? d : 0.f;
+        }
       }
     }
   }
