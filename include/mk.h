@@ -150,6 +150,15 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
  * MK_ERR_ARG if wg is not in [-1, grid). */
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
 
+/* Poll rounds after which a wait for other workgroups' words gives up, for the following
+ * prefill/decode calls (polls == 0 restores the default, 2^22, about a second).  A wait
+ * that gives up latches MK_ERR_TIMEOUT in the device error word and raises the abort
+ * flag; every other wait sees the flag within 128 rounds, so every wave of the launch
+ * leaves and the call completes; mk_status then returns MK_ERR_TIMEOUT, mk_error_info
+ * says where, and the handle needs mk_reset before it decodes again.  A small limit is
+ * how a host forces that path.  MK_ERR_ARG for a NULL handle. */
+int mk_set_spin_limit(mk_handle* h, uint32_t polls);
+
 /* Ids published so far by the most recently enqueued prefill/decode call (0 until
  * its first id), read from pinned host memory without synchronizing: the basis of
  * time-to-first-chunk.  A prefill publishes one id. */

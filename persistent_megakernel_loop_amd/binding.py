@@ -18,7 +18,7 @@ _LIB_NAME = "libmk.so"
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_set_phase_trace", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_grid_size",
+           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
@@ -71,6 +71,7 @@ def lib():
     L.mk_position.argtypes = [vp, pi32]
     L.mk_set_debug.argtypes = [vp, vp, vp]
     L.mk_set_phase_trace.argtypes = [vp, vp, i32]
+    L.mk_set_spin_limit.argtypes = [vp, ctypes.c_uint32]
     L.mk_progress.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
     L.mk_status.argtypes = [vp]
     L.mk_error_info.argtypes = [vp, pi32]
@@ -201,6 +202,9 @@ class Decoder:
 
     def set_phase_trace(self, phase=None, wg: int = 0):
         _check(lib().mk_set_phase_trace(self.handle, _ptr(phase), wg), "mk_set_phase_trace")
+
+    def set_spin_limit(self, polls: int = 0):
+        _check(lib().mk_set_spin_limit(self.handle, polls), "mk_set_spin_limit")
 
     def progress(self) -> int:
         v = ctypes.c_int64()

@@ -15,6 +15,10 @@
 using mk::LayerLayout;
 using mk::Params;
 
+// Poll rounds before a cross-workgroup wait gives up (about a second at the round times
+// measured on MI355X).
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+
 struct mk_handle {
   int body = -1;
   mk_cfg cfg{};
@@ -52,6 +56,7 @@ struct mk_handle {
   unsigned long long* dbg_trace = nullptr;
   unsigned long long* dbg_phase = nullptr;
   int32_t dbg_phase_wg = 0;
+  uint32_t spin_limit = kDefaultSpinLimit;
 };
 
 namespace {
@@ -267,7 +272,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   }
   P.tag0 = h->tag;
   P.lm_seq0 = h->lm_seq;
-  P.spin_limit = 1u << 22;
+  P.spin_limit = h->spin_limit;
   if (mk::launch_decode(h->body, P, prompt, h->stream)) return MK_ERR_HIP;
   h->tag += need;
   h->lm_seq = (h->lm_seq + (uint32_t)(n - logits_from)) & 0x3fffu;
@@ -436,6 +441,12 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace) {
   if (!h) return MK_ERR_ARG;
   h->dbg_hidden = d_hidden;
   h->dbg_trace = (unsigned long long*)d_trace;
+  return MK_OK;
+}
+
+int mk_set_spin_limit(mk_handle* h, uint32_t polls) {
+  if (!h) return MK_ERR_ARG;
+  h->spin_limit = polls ? polls : kDefaultSpinLimit;
   return MK_OK;
 }
 

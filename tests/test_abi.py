@@ -166,6 +166,7 @@ def test_null_handle_calls(lib):
     assert lib.mk_position(None, ctypes.byref(i32)) == -1
     assert lib.mk_set_debug(None, None, None) == -1
     assert lib.mk_set_phase_trace(None, None, 0) == -1
+    assert lib.mk_set_spin_limit(None, 1) == -1
     assert lib.mk_progress(None, ctypes.byref(i64)) == -1
     assert lib.mk_status(None) == -1
     assert lib.mk_error_info(None, info) == -1

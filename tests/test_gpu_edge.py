@@ -7,8 +7,12 @@
   word (mk_status returns MK_ERR_DEVICE) and read as id 0: the run equals, bit for bit,
   the run with 0 in its place;
 * a position stream outside the rotary table is flagged the same way and read as
-  position 0.
+  position 0;
+* a wait that gives up (a spin limit of one poll round, set from the host) ends the
+  launch cleanly, is reported as MK_ERR_TIMEOUT, and the handle recovers after mk_reset.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -18,6 +22,7 @@ from tests.parity import compare, make_inputs, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 MK_ERR_DEVICE = -7
+MK_ERR_TIMEOUT = -8
 
 
 def _decoder(shape):
@@ -104,3 +109,49 @@ def test_position_outside_rotary_table_flagged_and_read_as_zero():
     assert code_b == MK_ERR_DEVICE and code_f == 0
     assert np.array_equal(ids_b, ids_f)
     assert np.array_equal(hid_b.view(np.uint32), hid_f.view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [
+    wl.TINY,
+    wl.TALKER_0P6B.replace(name="talker-2l-timeout", n_layers=2, prompt_len=4, steps=8),
+    wl.TALKER_1P7B.replace(name="talker-1.7b-2l-timeout", n_layers=2, kv_prefill=0, prompt_len=4, steps=8),
+], ids=lambda s: s.name)
+def test_forced_timeout_reported_and_recovered(shape):
+    """A spin limit of one poll round makes the first wait for another workgroup give up:
+    the launch still completes (every wave leaves at the same barrier), mk_status reports
+    MK_ERR_TIMEOUT with the place recorded, and after mk_reset with the default limit the
+    handle decodes exactly as before (each body: fp32 LDS tiles, bf16 LDS tiles, register
+    rings)."""
+    import torch
+    from persistent_megakernel_loop_amd.binding import lib
+
+    print(f"[case] {shape.name}: spin limit 1 (forced timeout), then recovery", flush=True)
+    dec = _decoder(shape)
+    inp = make_inputs(shape)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    prompt = (t(inp.prompt_ids), t(inp.prompt_rows), t(inp.prompt_pos3))
+    steps = (t(inp.step_ids), t(inp.step_rows), t(inp.step_pos3))
+    dec.prefill(*prompt)
+    ref = dec.decode(inp.n_steps, *steps)
+    torch.cuda.synchronize()
+    dec.check()
+    ref = ref.cpu().numpy()
+
+    dec.reset()
+    dec.set_spin_limit(1)
+    dec.prefill(*prompt)
+    dec.decode(inp.n_steps, *steps)
+    torch.cuda.synchronize()
+    assert dec.status() == MK_ERR_TIMEOUT
+    info = (ctypes.c_int32 * 5)()
+    assert lib().mk_error_info(dec.handle, info) == 0
+    assert info[0] == 1 and 0 <= info[1] < 256  # recorded, by a workgroup of the grid
+
+    dec.set_spin_limit(0)
+    dec.reset()
+    dec.prefill(*prompt)
+    again = dec.decode(inp.n_steps, *steps)
+    torch.cuda.synchronize()
+    dec.check()
+    dec.close()
+    assert np.array_equal(again.cpu().numpy(), ref)
