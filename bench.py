@@ -131,13 +131,17 @@ CSRC = os.path.join(ROOT, "persistent_megakernel_loop_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+# The decode kernel's sources: its code and the parameter block the host fills in.
+DECODE_SOURCES = ("mk_internal.h", "mk_kernel.hip")
+
+
 def csrc_digest() -> str:
-    """sha256 over the code of the library's HIP/C++ sources (line comments and blank lines
+    """sha256 over the code of the decode kernel's sources (line comments and blank lines
     dropped): names the kernel build HBM counters were taken on."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for n in sorted(os.listdir(CSRC)):
+    for n in DECODE_SOURCES:
         with open(os.path.join(CSRC, n)) as f:
             code = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
         h.update(n.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
@@ -289,16 +293,17 @@ def main():
     algo = step_bytes(shape, first_pos, K)
     gbps = algo / (launch_ms * 1e-3) / 1e9
 
-    # time to first chunk: host clock from the prefill enqueue until the host sees k ids
-    ttfc = {}
-    if P:
+    # time to first chunk: host clock from the prefill enqueue until the host sees k ids;
+    # the prompt through the batched prefill (the default) and position by position
+    def ttfc_run(batched):
+        res = {}
         for kf in (1, 2, 4, 8):
             trials = []
             for _ in range(args.ttfc_trials):
                 dec.reset()
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
-                dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first)
+                dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first, batched=batched)
                 if kf == 1:
                     while dec.progress() < 1:
                         pass
@@ -308,8 +313,31 @@ def main():
                         pass
                 trials.append((time.perf_counter() - t0) * 1e3)
                 torch.cuda.synchronize()
-            ttfc[str(kf)] = round(float(np.median(trials)), 3)
+            res[str(kf)] = round(float(np.median(trials)), 3)
         dec.check()
+        return res
+
+    def prefill_ms(batched):
+        """Median device time of the prompt call alone (events on the launch stream)."""
+        trials = []
+        for _ in range(args.ttfc_trials):
+            dec.reset()
+            if kv is not None:
+                dec.load_kv(kv, shape.kv_prefill)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first, batched=batched)
+            b.record(stream)
+            torch.cuda.synchronize()
+            trials.append(a.elapsed_time(b))
+        dec.check()
+        return round(float(np.median(trials)), 3)
+
+    ttfc, ttfc_pp, pf_ms = {}, {}, {}
+    if P and args.ttfc_trials > 0:
+        ttfc = ttfc_run(True)
+        ttfc_pp = ttfc_run(False)
+        pf_ms = {"batched": prefill_ms(True), "per_position": prefill_ms(False)}
 
     # barrier share: in-kernel wait ticks over position ticks, one separate traced run
     prepare()
@@ -341,6 +369,8 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "ttfc_ms": ttfc,
+        "ttfc_ms_per_position_prefill": ttfc_pp,
+        "prefill_ms": pf_ms,
         "rtf_talker_only": round(ms_step / FRAME_MS, 5),
         "barrier_share": round(share, 4),
         "wall_ms_timed_launch": round(wall_ms, 3),

@@ -107,6 +107,24 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
 int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
                int32_t n, int32_t* d_out_first);
 
+/* Same contract and arguments as mk_prefill, with the prompt run as a batch: the
+ * positions before the last go through ordinary per-layer kernels, up to 64 positions
+ * per pass over the weights (matrix-core products over the packed weight tiles, causal
+ * attention over the cache, the cache written as mk_prefill writes it), and only the
+ * last position runs through the persistent kernel, which produces d_out_first[0] and
+ * the feedback id.  The time to the first id is where per-position work costs most
+ * (the dev.to article "Porting a 1200-line persistent CUDA megakernel to Qwen3-TTS",
+ * "Making it talk end-to-end"), and a batch is the case a one-position-per-pass
+ * persistent loop does not serve well (same article, "What I took away").  Results
+ * equal mk_prefill's up to rounding order (the debug hidden states too).
+ * Allocates its scratch (about 40 MB at hidden 2048) on the first call with n > 1.
+ * MK_ERR_UNSUPPORTED for float32 weights or a head layout other than head_dim 128 with
+ * two query heads per KV head (use mk_prefill there); other errors as mk_prefill.
+ * Stream-ordered on the handle's stream like mk_prefill; an id or position outside its
+ * table is flagged in the device error word and read as 0, as in mk_prefill. */
+int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
+                       int32_t n, int32_t* d_out_first);
+
 /* The hot path: n_steps decode steps in ONE launch.  Step s runs at position
  * position+s and reads
  *   d_ids == NULL : the id picked by the previous step (step 0: by the last prefill
@@ -178,6 +196,14 @@ int mk_error_info(mk_handle* h, int32_t* info /* [5] */);
  * n_chunks 16-byte chunks of d_src into LDS at byte offset offset_bytes, then back out to
  * d_dst (device buffers of n_chunks * 16 bytes).  offset_bytes + 16 n_chunks <= 147456. */
 int mk_selftest_lds_dma(const void* d_src, void* d_dst, int32_t n_chunks, int32_t offset_bytes, void* stream);
+
+/* Self-test of the batched prefill's matrix product: d_y[t][r] = sum over k of
+ * d_w[r][k] * d_x[t][k], d_w [rows][k] bf16, d_x [n][k] float32, d_y [n][rows] float32,
+ * through the same activation split and MFMA product kernels.  rows % 32 == 0,
+ * k % 64 == 0, 1 <= n <= 64, else MK_ERR_ARG.  Allocates and frees its scratch;
+ * synchronizes `stream`. */
+int mk_selftest_gemm(const void* d_w, int32_t rows, int32_t k, const float* d_x, int32_t n, float* d_y,
+                     void* stream);
 
 /* Number of workgroups of the persistent grid (one per CU). */
 int mk_grid_size(mk_handle* h, int32_t* n);

@@ -17,8 +17,8 @@ _LIB_NAME = "libmk.so"
 
 MK_F32, MK_BF16 = 0, 1
 
-EXPORTS = ("mk_create", "mk_prefill", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_grid_size",
+EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
+           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
@@ -65,6 +65,7 @@ def lib():
     vp, i32, pi32 = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
     L.mk_create.argtypes = [ctypes.POINTER(MkWeights), ctypes.POINTER(MkCfg), vp, ctypes.POINTER(vp)]
     L.mk_prefill.argtypes = [vp, vp, vp, vp, i32, vp]
+    L.mk_prefill_batched.argtypes = [vp, vp, vp, vp, i32, vp]
     L.mk_decode.argtypes = [vp, i32, vp, vp, vp, vp]
     L.mk_load_kv.argtypes = [vp, vp, i32]
     L.mk_reset.argtypes = [vp]
@@ -76,6 +77,7 @@ def lib():
     L.mk_status.argtypes = [vp]
     L.mk_error_info.argtypes = [vp, pi32]
     L.mk_selftest_lds_dma.argtypes = [vp, vp, i32, i32, vp]
+    L.mk_selftest_gemm.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     L.mk_grid_size.argtypes = [vp, pi32]
     L.mk_embed_sum.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     L.mk_strerror.argtypes = [ctypes.c_int]
@@ -170,12 +172,15 @@ class Decoder:
             raise RuntimeError("decoder destroyed")
         return self._h
 
-    def prefill(self, ids, rows=None, pos3=None, out=None):
+    def prefill(self, ids, rows=None, pos3=None, out=None, batched: bool = False):
+        """Run the prompt; batched=True takes mk_prefill_batched (all positions but the
+        last as a batch, the last through the persistent kernel)."""
         import torch
         n = ids.numel()
         if out is None:
             out = torch.empty(1, dtype=torch.int32, device=ids.device)
-        _check(lib().mk_prefill(self.handle, _ptr(ids), _ptr(rows), _ptr(pos3), n, _ptr(out)), "mk_prefill")
+        fn, name = (lib().mk_prefill_batched, "mk_prefill_batched") if batched else (lib().mk_prefill, "mk_prefill")
+        _check(fn(self.handle, _ptr(ids), _ptr(rows), _ptr(pos3), n, _ptr(out)), name)
         return out
 
     def decode(self, n_steps: int, ids=None, rows=None, pos3=None, out=None, device="cuda"):
@@ -243,6 +248,18 @@ def selftest_lds_dma(src, dst, offset_bytes: int = 0, stream=None):
     """Copy src -> LDS (at offset_bytes) -> dst through the kernel's LDS DMA path (both int32/uint8 device tensors)."""
     n = src.numel() * src.element_size() // 16
     _check(lib().mk_selftest_lds_dma(_ptr(src), _ptr(dst), n, offset_bytes, _stream_handle(stream)), "mk_selftest_lds_dma")
+
+
+def selftest_gemm(w, x, y=None, stream=None):
+    """y[t][r] = sum_k w[r][k] x[t][k] through the batched prefill's product kernels
+    (w: [rows][k] bf16 device tensor, x: [n][k] float32 device tensor)."""
+    import torch
+    rows, k = w.shape
+    n = x.shape[0]
+    if y is None:
+        y = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    _check(lib().mk_selftest_gemm(_ptr(w), rows, k, _ptr(x), n, _ptr(y), _stream_handle(stream)), "mk_selftest_gemm")
+    return y
 
 
 def embed_sum(codebooks, text, ids, rows=None, bad=None, stream=None):

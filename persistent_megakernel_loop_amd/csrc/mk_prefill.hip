@@ -1,0 +1,554 @@
+// Batched prompt prefill.
+//
+// The persistent decode kernel runs one position per pass over the weights, so a
+// prompt of P positions costs P passes.  Every prompt position but the last is
+// known up front, which makes the prompt a batch: each layer's projections become
+// matrix products with P columns, and the weights stream once per chunk of up to 64
+// positions instead of once per position.  The causal mask keeps the result the same
+// as the position-by-position run (up to rounding order): position p attends to
+// cache entries 0..p, all of which are written before the chunk's attention runs.
+//
+// One chunk, per layer, as a short sequence of ordinary kernels on the handle's
+// stream:
+//   input rows and RMSNorm (layer 0) or residual + RMSNorm (later layers)
+//   QKV product -> per-head q/k RMSNorm, rotary embedding, cache write
+//   causal attention, one workgroup per (position, KV group)
+//   O product -> residual + post-attention RMSNorm
+//   gate/up product -> SwiGLU
+//   down product -> residual + next input RMSNorm
+// The products read the weight tiles of the persistent kernel's arena as they are
+// (no second copy of the weights) and run on the matrix cores: 16x16x32 bf16 MFMA
+// with the activations split into a bf16 high and low part (two products per tile),
+// so the activations keep about 16 significant bits, as the fp32 dot products of the
+// decode path do up to rounding.  The last prompt position still runs through the
+// persistent kernel, which reads the filled cache and produces the first id.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+#include "mk_prefill.h"
+
+namespace mk {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ float from_bf16(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ float wsum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over the 256 threads of a workgroup (every thread gets the total).
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wsum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Split-activation layout of a K-column input for npp positions: element k of
+// position n at [(k/8)*npp + n][k%8] (the high parts), the low parts K*npp elements
+// further.  Eight consecutive columns of one position are one 16-byte chunk, and
+// the 16 positions of a tile are 16 consecutive chunks.
+__device__ __forceinline__ void store_split8(uint16_t* xs, int K, int npp, int n, int c, const float v[8]) {
+  uint32_t hi[4], lo[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = to_bf16(v[2 * e]), h1 = to_bf16(v[2 * e + 1]);
+    const uint16_t l0 = to_bf16(v[2 * e] - from_bf16(h0)), l1 = to_bf16(v[2 * e + 1] - from_bf16(h1));
+    hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  const size_t off = ((size_t)c * npp + n) * 8;
+  *reinterpret_cast<uint4*>(xs + off) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *reinterpret_cast<uint4*>(xs + (size_t)K * npp + off) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+}
+
+__device__ __forceinline__ void zero_split(uint16_t* xs, int K, int npp, int n) {
+  for (int c = threadIdx.x; c < K / 8; c += blockDim.x) {
+    const size_t off = ((size_t)c * npp + n) * 8;
+    *reinterpret_cast<uint4*>(xs + off) = make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(xs + (size_t)K * npp + off) = make_uint4(0, 0, 0, 0);
+  }
+}
+
+// RMSNorm of row x (H floats) with gains g, written split into xs for position n.
+__device__ void norm_split(const float* x, const float* g, int H, float eps, uint16_t* xs, int npp, int n, float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
+  ss = block_sum(ss, red);
+  const float rs = rsqrtf(ss / (float)H + eps);
+  for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = g[8 * c + e] * (x[8 * c + e] * rs);
+    store_split8(xs, H, npp, n, c, v);
+  }
+}
+
+// ------------------------------------------------------------------ input rows
+__global__ __launch_bounds__(256) void pf_input_kernel(PfArgs A) {
+  __shared__ float red[4];
+  const int n = blockIdx.x, H = A.H;
+  if (n >= A.m) { zero_split(A.xs, H, A.npp, n); return; }
+  const int p = A.pos0 + n;
+  int id = A.ids[n];
+  if (id >= A.vocab || (id < 0 && A.rows == nullptr)) {  // flagged and read as id 0
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(A.err, DEV_ERR_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    id = 0;
+  }
+  if ((int)threadIdx.x < A.n_sections) {
+    const int v = A.pos3 ? A.pos3[n * 3 + threadIdx.x] : p;
+    if (v < 0 || v >= A.rope_positions)
+      __hip_atomic_fetch_or(A.err, DEV_ERR_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  float* x = A.x + (size_t)n * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    const float v = id >= 0 ? from_bf16(A.embed[(size_t)id * H + i]) : A.rows[(size_t)n * H + i];
+    x[i] = v;
+    if (A.dbg_hidden) A.dbg_hidden[(size_t)n * (A.L + 1) * H + i] = v;
+  }
+  __syncthreads();
+  norm_split(x, A.in_norm0, H, A.eps, A.xs, A.npp, n, red);
+}
+
+// ------------------------------------------------------------------ products
+// part[ks][n][r] = sum over the ks-th run of KC columns of W[r][k] * X[n][k].
+// Weight element (r, k) sits at w[(k/KB)*R*KB + r*KB + k%KB] (KB = K for a plain
+// row-major matrix; the O and down tiles are K-blocked per KV group and per MLP
+// slice).  One wave computes 32 rows x 16*NT positions over KC = 64*S columns: per 64
+// columns, lane group q (lanes 16q..16q+15) holds columns 16q..16q+15 of 16 rows as
+// two 8-column halves, and the activations of 16 positions over the same columns, so
+// that each 16x16x32 MFMA pairs operands over the same 32 columns whatever order the
+// hardware gives them inside the instruction.  The result tile has 4 consecutive rows
+// per lane (rows 4q..4q+3 of the tile, position lane%16).
+template <int NT, int S>
+__global__ __launch_bounds__(256) void pf_gemm_kernel(const uint16_t* __restrict__ w, int R, int KB, int K,
+                                                      const uint16_t* __restrict__ xs, float* __restrict__ part,
+                                                      int n_waves) {
+  constexpr int NPP = 16 * NT, KC = 64 * S;
+  const int lane = threadIdx.x & 63;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= n_waves) return;
+  const int groups = R / 32;
+  const int rg = wid % groups, ks = wid / groups;
+  const int k0 = ks * KC, blk = k0 / KB, kk0 = k0 % KB;
+  const int q = lane >> 4, i16 = lane & 15;
+  const uint16_t* w0 = w + (size_t)blk * R * KB + (size_t)(rg * 32 + i16) * KB + kk0 + 16 * q;
+  const uint16_t* w1 = w0 + (size_t)16 * KB;
+  const uint16_t* xh = xs + ((size_t)(k0 / 8 + 2 * q) * NPP + i16) * 8;
+  const uint16_t* xl = xh + (size_t)K * NPP;
+  bf16x8 a[S][2][2];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      a[s][0][hf] = *reinterpret_cast<const bf16x8*>(w0 + s * 64 + hf * 8);
+      a[s][1][hf] = *reinterpret_cast<const bf16x8*>(w1 + s * 64 + hf * 8);
+    }
+  // every weight load of the wave is in flight before the first product waits on one
+  __builtin_amdgcn_sched_barrier(0);
+  f4 acc[2][NT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    bf16x8 bh[NT][2], bl[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const size_t off = ((size_t)(s * 8 + hf) * NPP + nt * 16) * 8;
+        bh[nt][hf] = *reinterpret_cast<const bf16x8*>(xh + off);
+        bl[nt][hf] = *reinterpret_cast<const bf16x8*>(xl + off);
+      }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bh[nt][hf], acc[rt][nt], 0, 0, 0);
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bl[nt][hf], acc[rt][nt], 0, 0, 0);
+        }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f4*>(part + ((size_t)ks * NPP + nt * 16 + i16) * R + rg * 32 + rt * 16 + 4 * q) = acc[rt][nt];
+}
+
+// ------------------------------------------------------------------ q, k, v
+// One workgroup per (KV group g, position n); wave h < QPG takes q head h, wave QPG
+// the key, wave QPG+1 the value.  Lane i holds elements i and i + 64 of its head,
+// which are rotary pair i (head dim 128).
+__global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const float* G, int ks) {
+  constexpr int D = 128, QPG = 2;
+  const int g = blockIdx.x, n = blockIdx.y, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int p = A.pos0 + n;
+  const int R = A.NKV * (QPG + 2) * D;
+  const int row = g * (QPG + 2) * D + h * D + lane;
+  float a0 = 0.f, a1 = 0.f;
+  for (int s = 0; s < ks; ++s) {
+    const float* pp = A.part + ((size_t)s * A.npp + n) * R + row;
+    a0 += pp[0];
+    a1 += pp[64];
+  }
+  const size_t crow = (((size_t)l * A.NKV + g) * A.max_seq + p) * D;
+  if (h <= QPG) {
+    const float* gn = G + A.H + (h < QPG ? 0 : D);
+    const float ss = wsum(fmaf(a1, a1, a0 * a0));
+    const float rs = rsqrtf(ss / (float)D + A.eps);
+    const float n0 = gn[lane] * (a0 * rs), n1 = gn[lane + 64] * (a1 * rs);
+    const int sct = lane < A.sec_end0 ? 0 : (lane < A.sec_end1 ? 1 : 2);
+    int ps = A.pos3 ? A.pos3[n * 3 + sct] : p;
+    ps = (ps < 0 || ps >= A.rope_positions) ? 0 : ps;
+    const float c = A.rope_cos[(size_t)ps * (D / 2) + lane], sn = A.rope_sin[(size_t)ps * (D / 2) + lane];
+    const float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
+    if (h < QPG) {
+      const float qscale = rsqrtf((float)D);
+      float* qo = A.q + ((size_t)n * A.NQ + g * QPG + h) * D;
+      qo[lane] = o0 * qscale;
+      qo[lane + 64] = o1 * qscale;
+    } else if (A.kv_bf16) {
+      uint16_t* kc = reinterpret_cast<uint16_t*>(A.kcache) + crow;
+      kc[lane] = to_bf16(o0);
+      kc[lane + 64] = to_bf16(o1);
+    } else {
+      float* kc = reinterpret_cast<float*>(A.kcache) + crow;
+      kc[lane] = o0;
+      kc[lane + 64] = o1;
+    }
+  } else if (A.kv_bf16) {
+    uint16_t* vc = reinterpret_cast<uint16_t*>(A.vcache) + crow;
+    vc[lane] = to_bf16(a0);
+    vc[lane + 64] = to_bf16(a1);
+  } else {
+    float* vc = reinterpret_cast<float*>(A.vcache) + crow;
+    vc[lane] = a0;
+    vc[lane + 64] = a1;
+  }
+}
+
+// ------------------------------------------------------------------ attention
+// One workgroup per (KV group g, position n) over cache positions 0..p: wave w takes
+// the 64-key blocks w, w+4, ...; lane j of a block scores key j against the group's
+// QPG query heads, the block's softmax weights go through LDS, and the values are
+// read as whole rows (lane i holds dims 2i, 2i+1).  The four waves' running maxima,
+// sums and outputs merge in LDS; the result goes out split for the O product.
+__device__ __forceinline__ void load_row8(const void* cache, int bf, size_t idx, float v[8]) {
+  if (bf) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cache) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void load_pair(const void* cache, int bf, size_t idx, float& v0, float& v1) {
+  if (bf) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(cache) + idx);
+    v0 = __uint_as_float(u << 16);
+    v1 = __uint_as_float(u & 0xffff0000u);
+  } else {
+    const float2 a = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(cache) + idx);
+    v0 = a.x;
+    v1 = a.y;
+  }
+}
+
+__global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
+  constexpr int D = 128, QPG = 2, NW = 4;
+  __shared__ float qs[QPG][D];
+  __shared__ float pw[NW][QPG][64];
+  __shared__ float mw[NW][QPG], lw[NW][QPG];
+  __shared__ float aw[NW][QPG][D];
+  const int g = blockIdx.x, n = blockIdx.y, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int K = A.NQ * D;
+  if (n >= A.m) {  // padding columns of the O product
+    if (w < QPG) {
+      const int e = (g * QPG + w) * D + 2 * lane;
+      const size_t off = ((size_t)(e / 8) * A.npp + n) * 8 + e % 8;
+      *reinterpret_cast<uint32_t*>(A.xs + off) = 0u;
+      *reinterpret_cast<uint32_t*>(A.xs + (size_t)K * A.npp + off) = 0u;
+    }
+    return;
+  }
+  const int p = A.pos0 + n, nkeys = p + 1;
+  for (int i = threadIdx.x; i < QPG * D; i += blockDim.x)
+    qs[i / D][i % D] = A.q[((size_t)n * A.NQ + g * QPG) * D + i];
+  __syncthreads();
+  const size_t cbase = ((size_t)l * A.NKV + g) * A.max_seq * D;
+  float M[QPG], Ls[QPG], acc[QPG][2];
+#pragma unroll
+  for (int h = 0; h < QPG; ++h) { M[h] = -INFINITY; Ls[h] = 0.f; acc[h][0] = acc[h][1] = 0.f; }
+  for (int kb = w; kb * 64 < nkeys; kb += NW) {
+    const int j = kb * 64 + lane;
+    const bool valid = j < nkeys;
+    const size_t krow = cbase + (size_t)(valid ? j : p) * D;
+    float s[QPG];
+#pragma unroll
+    for (int h = 0; h < QPG; ++h) s[h] = 0.f;
+#pragma unroll 4
+    for (int d = 0; d < D; d += 8) {
+      float kv[8];
+      load_row8(A.kcache, A.kv_bf16, krow + d, kv);
+#pragma unroll
+      for (int h = 0; h < QPG; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[h] = fmaf(qs[h][d + e], kv[e], s[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < QPG; ++h) {
+      const float sv = valid ? s[h] : -INFINITY;
+      const float mn = fmaxf(M[h], wmax(sv));  // finite: key kb*64 is valid
+      const float corr = __expf(M[h] - mn);    // 0 while M is still -inf
+      const float pr = valid ? __expf(sv - mn) : 0.f;
+      Ls[h] = Ls[h] * corr + wsum(pr);
+      acc[h][0] *= corr;
+      acc[h][1] *= corr;
+      M[h] = mn;
+      pw[w][h][lane] = pr;
+    }
+    // the block's weights are read back by every lane of this wave (LDS accesses of
+    // one wave complete in order)
+    __builtin_amdgcn_wave_barrier();
+    const int nb = min(64, nkeys - kb * 64);
+    for (int u0 = 0; u0 < nb; u0 += 8) {
+      float v0[8], v1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int u = min(u0 + e, nb - 1);  // past the block's last key: weight 0, row in range
+        load_pair(A.vcache, A.kv_bf16, cbase + (size_t)(kb * 64 + u) * D + 2 * lane, v0[e], v1[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int h = 0; h < QPG; ++h) {
+          const float pu = u0 + e < nb ? pw[w][h][u0 + e] : 0.f;
+          acc[h][0] = fmaf(pu, v0[e], acc[h][0]);
+          acc[h][1] = fmaf(pu, v1[e], acc[h][1]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+#pragma unroll
+  for (int h = 0; h < QPG; ++h) {
+    if (lane == 0) { mw[w][h] = M[h]; lw[w][h] = Ls[h]; }
+    aw[w][h][2 * lane] = acc[h][0];
+    aw[w][h][2 * lane + 1] = acc[h][1];
+  }
+  __syncthreads();
+  if (w < QPG) {
+    const int h = w;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) mx = fmaxf(mx, mw[v][h]);
+    float f[NW], lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      f[v] = mw[v][h] == -INFINITY ? 0.f : __expf(mw[v][h] - mx);
+      lsum = fmaf(f[v], lw[v][h], lsum);
+    }
+    const float inv = 1.f / lsum;
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      o0 = fmaf(f[v], aw[v][h][2 * lane], o0);
+      o1 = fmaf(f[v], aw[v][h][2 * lane + 1], o1);
+    }
+    o0 *= inv;
+    o1 *= inv;
+    const uint16_t h0 = to_bf16(o0), h1 = to_bf16(o1);
+    const uint16_t l0 = to_bf16(o0 - from_bf16(h0)), l1 = to_bf16(o1 - from_bf16(h1));
+    const int e = (g * QPG + h) * D + 2 * lane;
+    const size_t off = ((size_t)(e / 8) * A.npp + n) * 8 + e % 8;
+    *reinterpret_cast<uint32_t*>(A.xs + off) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    *reinterpret_cast<uint32_t*>(A.xs + (size_t)K * A.npp + off) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+}
+
+// ------------------------------------------------------------------ residual + norm
+// x[n] += sum of the ks partials (in order); the layer output is recorded when slot
+// >= 0; then RMSNorm with gains g, split for the next product.
+__global__ __launch_bounds__(256) void pf_resid_kernel(PfArgs A, const float* g, int ks, int slot) {
+  __shared__ float red[4];
+  const int n = blockIdx.x, H = A.H;
+  if (n >= A.m) { zero_split(A.xs, H, A.npp, n); return; }
+  float* x = A.x + (size_t)n * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    float y = 0.f;
+    for (int s = 0; s < ks; ++s) y += A.part[((size_t)s * A.npp + n) * H + i];
+    const float v = x[i] + y;
+    x[i] = v;
+    if (slot >= 0 && A.dbg_hidden) A.dbg_hidden[((size_t)n * (A.L + 1) + slot) * H + i] = v;
+  }
+  __syncthreads();
+  norm_split(x, g, H, A.eps, A.xs, A.npp, n, red);
+}
+
+// ------------------------------------------------------------------ SwiGLU
+// Gate/up rows come in the arena's order: slice x of I/8 columns, 32 runs of HALF gate
+// rows then HALF up rows; column c of the intermediate is gate row x*2IX + r*2HALF + i
+// with x = c / IX, r = (c % IX) / HALF, i = c % HALF.  The output is split in natural
+// column order, which is the down tiles' column order.
+__global__ __launch_bounds__(256) void pf_swiglu_kernel(PfArgs A, int ks) {
+  const int n = blockIdx.x, I = A.I;
+  if (n >= A.m) { zero_split(A.xs, I, A.npp, n); return; }
+  const int IX = I / kXcds, HALF = IX / kPerXcd, R = 2 * I;
+  for (int c = threadIdx.x; c < I / 8; c += blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ci = 8 * c + e;
+      const int mg = (ci / IX) * 2 * IX + ((ci % IX) / HALF) * 2 * HALF + ci % HALF;
+      float gt = 0.f, up = 0.f;
+      for (int s = 0; s < ks; ++s) {
+        const float* pp = A.part + ((size_t)s * A.npp + n) * R;
+        gt += pp[mg];
+        up += pp[mg + HALF];
+      }
+      v[e] = gt / (1.f + __expf(-gt)) * up;
+    }
+    store_split8(A.xs, I, A.npp, n, c, v);
+  }
+}
+
+// ------------------------------------------------------------------ self-test helpers
+__global__ __launch_bounds__(256) void pf_split_kernel(const float* x, int K, int m, int npp, uint16_t* xs) {
+  const int n = blockIdx.x;
+  if (n >= m) { zero_split(xs, K, npp, n); return; }
+  for (int c = threadIdx.x; c < K / 8; c += blockDim.x) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = x[(size_t)n * K + 8 * c + e];
+    store_split8(xs, K, npp, n, c, v);
+  }
+}
+
+__global__ __launch_bounds__(256) void pf_reduce_kernel(const float* part, int ks, int npp, int R, int m, float* y) {
+  const int n = blockIdx.x;
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < ks; ++s) v += part[((size_t)s * npp + n) * R + r];
+    y[(size_t)n * R + r] = v;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+template <int NT>
+int launch_gemm_nt(const uint16_t* w, int R, int KB, int K, int kc, const uint16_t* xs, float* part, hipStream_t st) {
+  const int waves = (R / 32) * (K / kc);
+  const dim3 grid((waves + 3) / 4), block(256);
+  switch (kc) {
+    case 64: hipLaunchKernelGGL((pf_gemm_kernel<NT, 1>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
+    case 128: hipLaunchKernelGGL((pf_gemm_kernel<NT, 2>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
+    case 256: hipLaunchKernelGGL((pf_gemm_kernel<NT, 4>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
+    default: return -1;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// Columns per wave of a product: the widest of 256/128/64 that divides the K block,
+// narrowed while the product has fewer than 1024 waves (a wave streams 32 rows x KC
+// columns, so narrower runs put more weight bytes in flight at once).
+int pick_kc(int R, int KB, int K) {
+  int kc = 256;
+  while (kc > 64 && KB % kc) kc /= 2;
+  if (KB % kc || K % kc || R % 32) return -1;
+  while (kc > 64 && (R / 32) * (K / kc) < 1024) kc /= 2;
+  return kc;
+}
+
+int launch_gemm(const uint16_t* w, int R, int KB, int K, int npp, const uint16_t* xs, float* part, hipStream_t st,
+                int* ks) {
+  const int kc = pick_kc(R, KB, K);
+  if (kc < 0) return -1;
+  *ks = K / kc;
+  switch (npp) {
+    case 16: return launch_gemm_nt<1>(w, R, KB, K, kc, xs, part, st);
+    case 32: return launch_gemm_nt<2>(w, R, KB, K, kc, xs, part, st);
+    case 48: return launch_gemm_nt<3>(w, R, KB, K, kc, xs, part, st);
+    case 64: return launch_gemm_nt<4>(w, R, KB, K, kc, xs, part, st);
+  }
+  return -1;
+}
+
+}  // namespace
+
+size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I) {
+  const int QPG = NQ / NKV;
+  const int dims[4][3] = {{NKV * (QPG + 2) * D, H, H}, {H, QPG * D, NQ * D}, {2 * I, H, H}, {H, I / kXcds, I}};
+  size_t best = 0;
+  for (const auto& d : dims) {
+    const int kc = pick_kc(d[0], d[1], d[2]);
+    if (kc < 0) return 0;
+    const size_t need = (size_t)(d[2] / kc) * kPrefillChunk * d[0];
+    if (need > best) best = need;
+  }
+  return best;
+}
+
+int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayout& lay, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int H = A.H, D = A.D, NQ = A.NQ, NKV = A.NKV, I = A.I, QPG = NQ / NKV;
+  if (D != 128 || QPG != 2 || A.npp % 16 || A.npp > kPrefillChunk || A.m <= 0 || A.m > A.npp) return -1;
+  const dim3 b256(256);
+  hipLaunchKernelGGL(pf_input_kernel, dim3(A.npp), b256, 0, st, A);
+  for (int l = 0; l < A.L; ++l) {
+    const uint8_t* base = layers + (size_t)l * lay.stride;
+    const float* G = reinterpret_cast<const float*>(base + lay.gains);
+    int ks = 0;
+    if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.qkv), NKV * (QPG + 2) * D, H, H, A.npp, A.xs, A.part,
+                    st, &ks))
+      return -1;
+    hipLaunchKernelGGL(pf_qkv_kernel, dim3(NKV, A.m), b256, 0, st, A, l, G, ks);
+    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), b256, 0, st, A, l);
+    if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
+      return -1;
+    hipLaunchKernelGGL(pf_resid_kernel, dim3(A.npp), b256, 0, st, A, G, ks, -1);
+    if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.gu), 2 * I, H, H, A.npp, A.xs, A.part, st, &ks))
+      return -1;
+    hipLaunchKernelGGL(pf_swiglu_kernel, dim3(A.npp), b256, 0, st, A, ks);
+    if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.down), H, I / kXcds, I, A.npp, A.xs, A.part, st, &ks))
+      return -1;
+    hipLaunchKernelGGL(pf_resid_kernel, dim3(A.npp), b256, 0, st, A, G + H + 2 * D, ks, l + 1);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_selftest(const uint16_t* w, int R, int K, const float* x, int m, float* y, uint16_t* xs, float* part,
+                         void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  const int npp = (m + 15) / 16 * 16;
+  hipLaunchKernelGGL(pf_split_kernel, dim3(npp), dim3(256), 0, st, x, K, m, npp, xs);
+  int ks = 0;
+  if (launch_gemm(w, R, K, K, npp, xs, part, st, &ks)) return -1;
+  hipLaunchKernelGGL(pf_reduce_kernel, dim3(m), dim3(256), 0, st, part, ks, npp, R, m, y);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace mk

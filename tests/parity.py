@@ -59,7 +59,7 @@ class GpuRun:
     trace: Optional[np.ndarray] = None
 
 
-def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None) -> GpuRun:
+def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batched: bool = False) -> GpuRun:
     import torch
     from persistent_megakernel_loop_amd.binding import Decoder, to_device
 
@@ -78,7 +78,7 @@ def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None) -> G
     t = lambda a, dt=None: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     if P:
         dec.set_debug(hid[:P], None)
-        out = dec.prefill(t(inp.prompt_ids), t(inp.prompt_rows), t(inp.prompt_pos3))
+        out = dec.prefill(t(inp.prompt_ids), t(inp.prompt_rows), t(inp.prompt_pos3), batched=batched)
         dec.check()
         first = int(out.cpu()[0])
     dec.set_debug(hid[P:], tr)

@@ -160,6 +160,7 @@ def test_null_handle_calls(lib):
     i32, i64 = ctypes.c_int32(), ctypes.c_int64()
     info = (ctypes.c_int32 * 5)()
     assert lib.mk_prefill(None, 0x10, None, None, 4, 0x20) == -1
+    assert lib.mk_prefill_batched(None, 0x10, None, None, 4, 0x20) == -1
     assert lib.mk_decode(None, 4, None, None, None, 0x20) == -1
     assert lib.mk_load_kv(None, 0x10, 4) == -1
     assert lib.mk_reset(None) == -1
@@ -181,6 +182,12 @@ def test_selftest_and_embed_sum_argument_checks(lib):
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 4, 8, None) == -1
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 9217, 0, None) == -1
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 1, 144 * 1024 - 8, None) == -1
+    # product self-test: rows % 32, k % 64, 1 <= n <= 64, non-null buffers
+    assert lib.mk_selftest_gemm(None, 32, 64, 0x10, 1, 0x20, None) == -1
+    assert lib.mk_selftest_gemm(0x10, 33, 64, 0x20, 1, 0x30, None) == -1
+    assert lib.mk_selftest_gemm(0x10, 32, 96, 0x20, 1, 0x30, None) == -1
+    assert lib.mk_selftest_gemm(0x10, 32, 64, 0x20, 0, 0x30, None) == -1
+    assert lib.mk_selftest_gemm(0x10, 32, 64, 0x20, 65, 0x30, None) == -1
     # embed_sum: null tables, bad sizes, bad dtype
     args = dict(cb=0x10, ncb=16, cbs=2048, tx=0x20, tv=151936, h=1024, dt=1, ids=0x30, n=4, rows=0x40)
 
