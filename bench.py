@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (known bytes for scaling HBM counters) and exit")
     ap.add_argument("--hbm-summary", metavar="DIR", help="only print the HBM counter summary of the passes under DIR")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
+                    help="only run the workload's prompt N times through the batched prefill (for profiling) and exit")
     args = ap.parse_args()
     if args.hbm_summary:
         sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024))
@@ -259,6 +261,21 @@ def main():
     kv = to_device(wl.make_kv_prefill(shape)) if shape.kv_prefill else None
     out = torch.empty(K, dtype=torch.int32, device="cuda")
     first = torch.empty(1, dtype=torch.int32, device="cuda")
+    if args.prefill_only:
+        times = []
+        for _ in range(args.prefill_only):
+            dec.reset()
+            if kv is not None:
+                dec.load_kv(kv, shape.kv_prefill)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            dec.prefill(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"], out=first, batched=True)
+            torch.cuda.synchronize()
+            times.append((time.perf_counter() - t0) * 1e3)
+        dec.check()
+        print(json.dumps({"workload": shape.name, "prompt_positions": P, "batched_prefill_ms": times}), flush=True)
+        dec.close()
+        return
 
     def prepare():
         dec.reset()

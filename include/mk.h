@@ -107,21 +107,24 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
 int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
                int32_t n, int32_t* d_out_first);
 
-/* Same contract and arguments as mk_prefill, with the prompt run as a batch: the
- * positions before the last go through ordinary per-layer kernels, up to 64 positions
- * per pass over the weights (matrix-core products over the packed weight tiles, causal
- * attention over the cache, the cache written as mk_prefill writes it), and only the
- * last position runs through the persistent kernel, which produces d_out_first[0] and
- * the feedback id.  The time to the first id is where per-position work costs most
+/* Same contract and arguments as mk_prefill, with the prompt run as a batch through
+ * ordinary per-layer kernels instead of the persistent kernel: up to 64 positions per
+ * pass over the weights (matrix-core products over the packed weight tiles, causal
+ * attention over the cache, the cache written as mk_prefill writes it), then the LM
+ * head over the last position and its greedy id (ties: lowest index), published as
+ * mk_prefill publishes it (d_out_first[0], the feedback id, the pinned mirror and the
+ * progress word).  The time to the first id is where per-position work costs most
  * (the dev.to article "Porting a 1200-line persistent CUDA megakernel to Qwen3-TTS",
  * "Making it talk end-to-end"), and a batch is the case a one-position-per-pass
  * persistent loop does not serve well (same article, "What I took away").  Results
- * equal mk_prefill's up to rounding order (the debug hidden states too).
- * Allocates its scratch (about 40 MB at hidden 2048) on the first call with n > 1.
- * MK_ERR_UNSUPPORTED for float32 weights or a head layout other than head_dim 128 with
+ * equal mk_prefill's up to rounding order, the debug hidden states too; the barrier
+ * trace and phase timeline are not written for these positions.
+ * Allocates its scratch (about 40 MB at hidden 2048) on the first call.
+ * MK_ERR_UNSUPPORTED for float32 weights, hidden or intermediate sizes that are not
+ * multiples of 512, hidden above 2048, or a head layout other than head_dim 128 with
  * two query heads per KV head (use mk_prefill there); other errors as mk_prefill.
- * Stream-ordered on the handle's stream like mk_prefill; an id or position outside its
- * table is flagged in the device error word and read as 0, as in mk_prefill. */
+ * Stream-ordered on the handle's stream; an id or position outside its table is
+ * flagged in the device error word and read as 0, as in mk_prefill. */
 int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
                        int32_t n, int32_t* d_out_first);
 

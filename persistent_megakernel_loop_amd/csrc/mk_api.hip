@@ -61,7 +61,8 @@ struct mk_handle {
   uint32_t spin_limit = kDefaultSpinLimit;
   // batched prefill scratch, allocated by the first batched call
   uint8_t* pf_buf = nullptr;
-  float *pf_x = nullptr, *pf_part = nullptr, *pf_q = nullptr;
+  float *pf_x = nullptr, *pf_part = nullptr, *pf_q = nullptr, *pf_ss = nullptr, *pf_blk_val = nullptr;
+  int32_t* pf_blk_idx = nullptr;
   uint16_t* pf_xs = nullptr;
 };
 
@@ -221,10 +222,8 @@ int ensure_pinned(mk_handle* h, int32_t n) {
   return MK_OK;
 }
 
-// dbg_skip: positions already recorded by the caller in the debug buffers (the batched
-// prefill records its own); this launch writes after them.
 int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const int32_t* pos3, int32_t* out,
-        int logits_from, int feedback, bool prompt, int32_t dbg_skip = 0) {
+        int logits_from, int feedback, bool prompt) {
   if (n <= 0) return MK_ERR_ARG;
   if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
   if (feedback && !h->have_last) return MK_ERR_STATE;
@@ -269,10 +268,9 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   h->call_seq += 1;
   P.call_seq = h->call_seq;
   P.progress = h->progress;
-  const size_t L = (size_t)h->cfg.n_layers, skip = (size_t)dbg_skip;
-  P.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + skip * (L + 1) * h->cfg.hidden : nullptr;
-  P.dbg_trace = h->dbg_trace ? h->dbg_trace + skip * mk::kGrid * 2 : nullptr;
-  P.dbg_phase = h->dbg_phase ? h->dbg_phase + skip * (h->dbg_phase_wg < 0 ? mk::kGrid : 1) * (2 + 10 * L) * 8 : nullptr;
+  P.dbg_hidden = h->dbg_hidden;
+  P.dbg_trace = h->dbg_trace;
+  P.dbg_phase = h->dbg_phase;
   P.dbg_phase_wg = h->dbg_phase_wg;
   // tags are compared for equality: before they wrap, clear the buffers so that no old word can match
   const uint32_t need = (uint32_t)n * mk::tags_per_position(h->cfg.n_layers) + 1;
@@ -411,56 +409,80 @@ int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const in
 
 int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3, int32_t n,
                        int32_t* d_out_first) {
-  if (!h || !d_ids || n <= 0) return MK_ERR_ARG;
+  if (!h || !d_ids || n <= 0 || !d_out_first) return MK_ERR_ARG;
   const mk_cfg* c = &h->cfg;
   if ((long long)h->pos + n > c->max_seq) return MK_ERR_CAPACITY;
   const size_t part = mk::prefill_part_floats(c->hidden, c->n_q_heads, c->n_kv_heads, c->head_dim, c->intermediate);
-  if (c->weight_dtype != MK_BF16 || c->head_dim != 128 || c->n_q_heads != 2 * c->n_kv_heads || part == 0)
+  if (c->weight_dtype != MK_BF16 || c->head_dim != 128 || c->n_q_heads != 2 * c->n_kv_heads || part == 0 ||
+      c->hidden % 512 || c->hidden > 2048 || c->intermediate % 512)
     return MK_ERR_UNSUPPORTED;
-  if (n > 1) {
-    const int ch = mk::kPrefillChunk;
-    const size_t H = c->hidden, K = std::max<size_t>(std::max<size_t>(H, (size_t)c->n_q_heads * c->head_dim),
-                                                     (size_t)c->intermediate);
-    if (!h->pf_buf) {
-      const size_t bx = align_up(ch * H * 4, 256), bxs = align_up(2 * K * ch * 2, 256),
-                   bq = align_up((size_t)ch * c->n_q_heads * c->head_dim * 4, 256), bp = part * 4;
-      if (hipMalloc((void**)&h->pf_buf, bx + bxs + bq + bp) != hipSuccess) { h->pf_buf = nullptr; return MK_ERR_OOM; }
-      h->pf_x = (float*)h->pf_buf;
-      h->pf_xs = (uint16_t*)(h->pf_buf + bx);
-      h->pf_q = (float*)(h->pf_buf + bx + bxs);
-      h->pf_part = (float*)(h->pf_buf + bx + bxs + bq);
+  int e = ensure_pinned(h, 1);
+  if (e) return e;
+  const int ch = mk::kPrefillChunk;
+  const size_t H = c->hidden, K = std::max<size_t>(std::max<size_t>(H, (size_t)c->n_q_heads * c->head_dim),
+                                                   (size_t)c->intermediate);
+  const size_t n_blk = (size_t)(c->vocab + mk::kLmRowsPerBlock - 1) / mk::kLmRowsPerBlock;
+  if (!h->pf_buf) {
+    const size_t bx = align_up(ch * H * 4, 256), bxs = align_up(2 * K * ch * 2, 256),
+                 bq = align_up((size_t)ch * c->n_q_heads * c->head_dim * 4, 256),
+                 bs = align_up((size_t)ch * (H / 512) * 4, 256), bl = align_up(n_blk * 4, 256), bp = part * 4;
+    if (hipMalloc((void**)&h->pf_buf, bx + bxs + bq + bs + 2 * bl + bp) != hipSuccess) {
+      h->pf_buf = nullptr;
+      return MK_ERR_OOM;
     }
-    mk::PfArgs A{};
-    A.H = c->hidden; A.D = c->head_dim; A.NQ = c->n_q_heads; A.NKV = c->n_kv_heads; A.I = c->intermediate;
-    A.L = c->n_layers; A.vocab = c->vocab; A.max_seq = c->max_seq; A.rope_positions = c->max_seq;
-    A.n_sections = c->n_sections;
-    A.sec_end0 = c->n_sections == 1 ? c->head_dim : c->sections[0];
-    A.sec_end1 = c->n_sections > 1 ? c->sections[0] + c->sections[1] : c->head_dim;
-    A.eps = c->rms_eps;
-    A.kv_bf16 = c->kv_dtype == MK_BF16;
-    A.embed = (const uint16_t*)h->embed;
-    A.in_norm0 = h->in_norm0;
-    A.rope_cos = h->rope_cos;
-    A.rope_sin = h->rope_sin;
-    A.kcache = h->kcache;
-    A.vcache = h->vcache;
-    A.err = h->ctl;
-    A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q;
-    for (int32_t t0 = 0; t0 < n - 1; t0 += ch) {
-      A.m = std::min(ch, n - 1 - t0);
-      A.npp = (A.m + 15) / 16 * 16;
-      A.pos0 = h->pos + t0;
-      A.ids = d_ids + t0;
-      A.rows = d_rows ? d_rows + (size_t)t0 * H : nullptr;
-      A.pos3 = d_pos3 ? d_pos3 + (size_t)t0 * 3 : nullptr;
-      A.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + (size_t)t0 * (c->n_layers + 1) * H : nullptr;
-      if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) return MK_ERR_HIP;
-    }
-    h->pos += n - 1;
+    uint8_t* p = h->pf_buf;
+    h->pf_x = (float*)p;
+    h->pf_xs = (uint16_t*)(p += bx);
+    h->pf_q = (float*)(p += bxs);
+    h->pf_ss = (float*)(p += bq);
+    h->pf_blk_val = (float*)(p += bs);
+    h->pf_blk_idx = (int32_t*)(p += bl);
+    h->pf_part = (float*)(p += bl);
   }
-  const size_t last = (size_t)n - 1;
-  return run(h, 1, d_ids + last, d_rows ? d_rows + last * c->hidden : nullptr, d_pos3 ? d_pos3 + last * 3 : nullptr,
-             d_out_first, 0, 0, true, n - 1);
+  mk::PfArgs A{};
+  A.H = c->hidden; A.D = c->head_dim; A.NQ = c->n_q_heads; A.NKV = c->n_kv_heads; A.I = c->intermediate;
+  A.L = c->n_layers; A.vocab = c->vocab; A.max_seq = c->max_seq; A.rope_positions = c->max_seq;
+  A.n_sections = c->n_sections;
+  A.sec_end0 = c->n_sections == 1 ? c->head_dim : c->sections[0];
+  A.sec_end1 = c->n_sections > 1 ? c->sections[0] + c->sections[1] : c->head_dim;
+  A.eps = c->rms_eps;
+  A.kv_bf16 = c->kv_dtype == MK_BF16;
+  A.embed = (const uint16_t*)h->embed;
+  A.in_norm0 = h->in_norm0;
+  A.rope_cos = h->rope_cos;
+  A.rope_sin = h->rope_sin;
+  A.kcache = h->kcache;
+  A.vcache = h->vcache;
+  A.err = h->ctl;
+  A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q; A.ss = h->pf_ss;
+  for (int32_t t0 = 0; t0 < n; t0 += ch) {
+    A.m = std::min(ch, n - t0);
+    A.npp = (A.m + 15) / 16 * 16;
+    A.pos0 = h->pos + t0;
+    A.ids = d_ids + t0;
+    A.rows = d_rows ? d_rows + (size_t)t0 * H : nullptr;
+    A.pos3 = d_pos3 ? d_pos3 + (size_t)t0 * 3 : nullptr;
+    A.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + (size_t)t0 * (c->n_layers + 1) * H : nullptr;
+    if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) return MK_ERR_HIP;
+  }
+  // the last chunk's residual stream is still in place: its last row gives the first id
+  const uint8_t* last_layer = h->arena + (size_t)(c->n_layers - 1) * h->lay.stride;
+  mk::LmArgs M{};
+  M.lm_head = (const uint16_t*)h->lm_head;
+  M.g_final = (const float*)(last_layer + h->lay.gains) + H + 2 * c->head_dim;
+  M.n_last = A.m - 1;
+  M.blk_val = h->pf_blk_val;
+  M.blk_idx = h->pf_blk_idx;
+  M.out_first = d_out_first;
+  M.last_id = (int32_t*)(h->ctl + 2);
+  M.pinned_ids = h->pinned_ids;
+  M.progress = h->progress;
+  h->call_seq += 1;
+  M.call_seq = h->call_seq;
+  if (mk::launch_prefill_lm(A, M, h->stream)) return MK_ERR_HIP;
+  h->pos += n;
+  h->have_last = true;
+  return MK_OK;
 }
 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf, const int32_t* d_pos3,

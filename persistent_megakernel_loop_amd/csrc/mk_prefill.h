@@ -33,8 +33,25 @@ struct PfArgs {
   uint16_t* xs;              // [2][K/8][npp][8] split activations, K up to max(H, NQ*D, I)
   float* part;               // partial products, prefill_part_floats() floats
   float* q;                  // [npp][NQ][D] rotated, scaled queries
+  float* ss;                 // [npp][H/512] sums of squares of the residual row, per 512 columns
+};
+// The prompt's first id: the LM head over the last prompt position's final-norm row,
+// greedy (ties: lowest index), published like a decode step's id.
+constexpr int kLmRowsPerBlock = 64;
+struct LmArgs {
+  const uint16_t* lm_head;   // [V][H] bf16
+  const float* g_final;      // [H] final norm gains
+  int32_t n_last;            // row of the last position in the chunk's residual stream
+  float* blk_val;            // [ceil(V / kLmRowsPerBlock)] per-block maxima
+  int32_t* blk_idx;
+  int32_t* out_first;        // [1] device
+  int32_t* last_id;          // feedback id for the next decode call
+  int32_t* pinned_ids;       // host-pinned mirror, or NULL
+  unsigned long long* progress;  // host-pinned progress word
+  uint32_t call_seq;
 };
 size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I);  // 0: shape not supported
+int launch_prefill_lm(const PfArgs& a, const LmArgs& lm, void* stream);
 int launch_prefill_chunk(const PfArgs& a, const uint8_t* layers, const LayerLayout& lay, void* stream);
 int launch_gemm_selftest(const uint16_t* w, int R, int K, const float* x, int m, float* y, uint16_t* xs, float* part,
                          void* stream);

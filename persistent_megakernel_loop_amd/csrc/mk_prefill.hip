@@ -48,16 +48,6 @@ __device__ __forceinline__ float wmax(float v) {
   return v;
 }
 
-// Sum over the 256 threads of a workgroup (every thread gets the total).
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wsum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
 // Split-activation layout of a K-column input for npp positions: element k of
 // position n at [(k/8)*npp + n][k%8] (the high parts), the low parts K*npp elements
 // further.  Eight consecutive columns of one position are one 16-byte chunk, and
@@ -76,75 +66,101 @@ __device__ __forceinline__ void store_split8(uint16_t* xs, int K, int npp, int n
   *reinterpret_cast<uint4*>(xs + (size_t)K * npp + off) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
-__device__ __forceinline__ void zero_split(uint16_t* xs, int K, int npp, int n) {
-  for (int c = threadIdx.x; c < K / 8; c += blockDim.x) {
-    const size_t off = ((size_t)c * npp + n) * 8;
-    *reinterpret_cast<uint4*>(xs + off) = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(xs + (size_t)K * npp + off) = make_uint4(0, 0, 0, 0);
-  }
+__device__ __forceinline__ void zero_split8(uint16_t* xs, int K, int npp, int n, int c) {
+  const size_t off = ((size_t)c * npp + n) * 8;
+  *reinterpret_cast<uint4*>(xs + off) = make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(xs + (size_t)K * npp + off) = make_uint4(0, 0, 0, 0);
 }
 
-// RMSNorm of row x (H floats) with gains g, written split into xs for position n.
-__device__ void norm_split(const float* x, const float* g, int H, float eps, uint16_t* xs, int npp, int n, float* red) {
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// The RMSNorm feeding a product is taken apart as the decode path does: the product's
+// input is gains * x (split), and its consumer scales the result by the row's 1/rms,
+// read from per-512-column sums of squares.  A residual row is then written by H/512
+// one-wave blocks with no reduction across the row.
+__device__ __forceinline__ float row_rs(const PfArgs& A, int n) {
+  const int nb = A.H / 512;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) ss = fmaf(x[i], x[i], ss);
-  ss = block_sum(ss, red);
-  const float rs = rsqrtf(ss / (float)H + eps);
-  for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
-    float v[8];
+  for (int b = 0; b < nb; ++b) ss += A.ss[n * nb + b];
+  return rsqrtf(ss / (float)A.H + A.eps);
+}
+
+// Columns 8c .. 8c+7 of row n (values v): gains * x split for the next product, and
+// the squares summed over the block into ss[n][blockIdx.y].
+__device__ __forceinline__ void gain_split(const PfArgs& A, const float* g, int n, int c, const float v[8]) {
+  float gv[8], sq = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = g[8 * c + e] * (x[8 * c + e] * rs);
-    store_split8(xs, H, npp, n, c, v);
+  for (int e = 0; e < 8; ++e) {
+    gv[e] = g[8 * c + e] * v[e];
+    sq = fmaf(v[e], v[e], sq);
   }
+  store_split8(A.xs, A.H, A.npp, n, c, gv);
+  sq = wsum(sq);
+  if (threadIdx.x == 0) A.ss[n * (A.H / 512) + blockIdx.y] = sq;
 }
 
 // ------------------------------------------------------------------ input rows
-__global__ __launch_bounds__(256) void pf_input_kernel(PfArgs A) {
-  __shared__ float red[4];
-  const int n = blockIdx.x, H = A.H;
-  if (n >= A.m) { zero_split(A.xs, H, A.npp, n); return; }
+// grid (npp, H/512), 64 threads; thread t of block (n, b) takes columns 8(64b + t) .. +7.
+__global__ __launch_bounds__(64) void pf_input_kernel(PfArgs A) {
+  const int n = blockIdx.x, H = A.H, c = blockIdx.y * 64 + threadIdx.x;
+  if (n >= A.m) { zero_split8(A.xs, H, A.npp, n, c); return; }
   const int p = A.pos0 + n;
   int id = A.ids[n];
   if (id >= A.vocab || (id < 0 && A.rows == nullptr)) {  // flagged and read as id 0
-    if (threadIdx.x == 0) __hip_atomic_fetch_or(A.err, DEV_ERR_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0 && blockIdx.y == 0)
+      __hip_atomic_fetch_or(A.err, DEV_ERR_ID, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     id = 0;
   }
-  if ((int)threadIdx.x < A.n_sections) {
+  if (blockIdx.y == 0 && (int)threadIdx.x < A.n_sections) {
     const int v = A.pos3 ? A.pos3[n * 3 + threadIdx.x] : p;
     if (v < 0 || v >= A.rope_positions)
       __hip_atomic_fetch_or(A.err, DEV_ERR_POS, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  float* x = A.x + (size_t)n * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    const float v = id >= 0 ? from_bf16(A.embed[(size_t)id * H + i]) : A.rows[(size_t)n * H + i];
-    x[i] = v;
-    if (A.dbg_hidden) A.dbg_hidden[(size_t)n * (A.L + 1) * H + i] = v;
+  float v[8];
+  if (id >= 0) {
+    const uint4 u = *reinterpret_cast<const uint4*>(A.embed + (size_t)id * H + 8 * c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  } else {
+    load8(A.rows + (size_t)n * H + 8 * c, v);
   }
-  __syncthreads();
-  norm_split(x, A.in_norm0, H, A.eps, A.xs, A.npp, n, red);
+  store8(A.x + (size_t)n * H + 8 * c, v);
+  if (A.dbg_hidden) store8(A.dbg_hidden + (size_t)n * (A.L + 1) * H + 8 * c, v);
+  gain_split(A, A.in_norm0, n, c, v);
 }
 
 // ------------------------------------------------------------------ products
-// part[ks][n][r] = sum over the ks-th run of KC columns of W[r][k] * X[n][k].
+// part[ks][n][r] = sum over the ks-th run of WK*KC columns of W[r][k] * X[n][k].
 // Weight element (r, k) sits at w[(k/KB)*R*KB + r*KB + k%KB] (KB = K for a plain
 // row-major matrix; the O and down tiles are K-blocked per KV group and per MLP
-// slice).  One wave computes 32 rows x 16*NT positions over KC = 64*S columns: per 64
-// columns, lane group q (lanes 16q..16q+15) holds columns 16q..16q+15 of 16 rows as
-// two 8-column halves, and the activations of 16 positions over the same columns, so
-// that each 16x16x32 MFMA pairs operands over the same 32 columns whatever order the
-// hardware gives them inside the instruction.  The result tile has 4 consecutive rows
-// per lane (rows 4q..4q+3 of the tile, position lane%16).
+// slice).  A workgroup of WK waves takes 32 rows x 16*NT positions over WK*KC
+// columns, wave w the w-th run of KC = 64*S columns; the waves' results are summed
+// in LDS in wave order and written once.  Per 64 columns, lane group q (lanes
+// 16q..16q+15) holds columns 16q..16q+15 of 16 rows as two 8-column halves, and the
+// activations of 16 positions over the same columns, so that each 16x16x32 MFMA pairs
+// operands over the same 32 columns whatever order the hardware gives them inside
+// the instruction.  The result tile has 4 consecutive rows per lane (rows 4q..4q+3 of
+// the tile, position lane%16).
 template <int NT, int S>
 __global__ __launch_bounds__(256) void pf_gemm_kernel(const uint16_t* __restrict__ w, int R, int KB, int K,
-                                                      const uint16_t* __restrict__ xs, float* __restrict__ part,
-                                                      int n_waves) {
+                                                      const uint16_t* __restrict__ xs, float* __restrict__ part) {
   constexpr int NPP = 16 * NT, KC = 64 * S;
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wid >= n_waves) return;
+  __shared__ f4 red[3][2][NT][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, WK = blockDim.x >> 6;
   const int groups = R / 32;
-  const int rg = wid % groups, ks = wid / groups;
-  const int k0 = ks * KC, blk = k0 / KB, kk0 = k0 % KB;
+  const int rg = blockIdx.x % groups, ks = blockIdx.x / groups;
+  const int k0 = (ks * WK + wv) * KC, blk = k0 / KB, kk0 = k0 % KB;
   const int q = lane >> 4, i16 = lane & 15;
   const uint16_t* w0 = w + (size_t)blk * R * KB + (size_t)(rg * 32 + i16) * KB + kk0 + 16 * q;
   const uint16_t* w1 = w0 + (size_t)16 * KB;
@@ -186,6 +202,19 @@ __global__ __launch_bounds__(256) void pf_gemm_kernel(const uint16_t* __restrict
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bl[nt][hf], acc[rt][nt], 0, 0, 0);
         }
   }
+  if (wv > 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red[wv - 1][rt][nt][lane] = acc[rt][nt];
+  }
+  __syncthreads();
+  if (wv > 0) return;
+  for (int v = 1; v < WK; ++v)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[rt][nt] += red[v - 1][rt][nt][lane];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -209,6 +238,9 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
     a0 += pp[0];
     a1 += pp[64];
   }
+  const float xr = row_rs(A, n);  // the input norm's 1/rms
+  a0 *= xr;
+  a1 *= xr;
   const size_t crow = (((size_t)l * A.NKV + g) * A.max_seq + p) * D;
   if (h <= QPG) {
     const float* gn = G + A.H + (h < QPG ? 0 : D);
@@ -251,25 +283,41 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
 // QPG query heads, the block's softmax weights go through LDS, and the values are
 // read as whole rows (lane i holds dims 2i, 2i+1).  The four waves' running maxima,
 // sums and outputs merge in LDS; the result goes out split for the O product.
-__device__ __forceinline__ void load_row8(const void* cache, int bf, size_t idx, float v[8]) {
-  if (bf) {
-    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cache) + idx);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Eight cache elements as loaded (bf16: one 16-byte load, float32: two), converted later
+// so that all of a row's loads can be in flight before the first is used.
+template <bool BF> struct Row8 { uint4 u; };
+template <> struct Row8<false> { float4 a, b; };
+
+template <bool BF>
+__device__ __forceinline__ Row8<BF> ld_row8(const void* cache, size_t idx) {
+  Row8<BF> r;
+  if constexpr (BF) {
+    r.u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cache) + idx);
+  } else {
+    r.a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx);
+    r.b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx + 4);
+  }
+  return r;
+}
+
+template <bool BF>
+__device__ __forceinline__ void cvt_row8(const Row8<BF>& r, float v[8]) {
+  if constexpr (BF) {
+    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[2 * e] = __uint_as_float(w[e] << 16);
       v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
   } else {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx);
-    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
   }
 }
 
-__device__ __forceinline__ void load_pair(const void* cache, int bf, size_t idx, float& v0, float& v1) {
-  if (bf) {
+template <bool BF>
+__device__ __forceinline__ void load_pair(const void* cache, size_t idx, float& v0, float& v1) {
+  if constexpr (BF) {
     const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(cache) + idx);
     v0 = __uint_as_float(u << 16);
     v1 = __uint_as_float(u & 0xffff0000u);
@@ -280,6 +328,7 @@ __device__ __forceinline__ void load_pair(const void* cache, int bf, size_t idx,
   }
 }
 
+template <bool BF>  // cache entries in bf16, else float32
 __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
   constexpr int D = 128, QPG = 2, NW = 4;
   __shared__ float qs[QPG][D];
@@ -312,14 +361,18 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
     float s[QPG];
 #pragma unroll
     for (int h = 0; h < QPG; ++h) s[h] = 0.f;
-#pragma unroll 4
-    for (int d = 0; d < D; d += 8) {
+    Row8<BF> kr[D / 8];
+#pragma unroll
+    for (int j8 = 0; j8 < D / 8; ++j8) kr[j8] = ld_row8<BF>(A.kcache, krow + 8 * j8);
+    __builtin_amdgcn_sched_barrier(0);  // the whole key row in flight at once
+#pragma unroll
+    for (int j8 = 0; j8 < D / 8; ++j8) {
       float kv[8];
-      load_row8(A.kcache, A.kv_bf16, krow + d, kv);
+      cvt_row8<BF>(kr[j8], kv);
 #pragma unroll
       for (int h = 0; h < QPG; ++h)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[h] = fmaf(qs[h][d + e], kv[e], s[h]);
+        for (int e = 0; e < 8; ++e) s[h] = fmaf(qs[h][8 * j8 + e], kv[e], s[h]);
     }
 #pragma unroll
     for (int h = 0; h < QPG; ++h) {
@@ -337,15 +390,15 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
     // one wave complete in order)
     __builtin_amdgcn_wave_barrier();
     const int nb = min(64, nkeys - kb * 64);
-    for (int u0 = 0; u0 < nb; u0 += 8) {
-      float v0[8], v1[8];
+    for (int u0 = 0; u0 < nb; u0 += 32) {  // 32 value rows in flight at once
+      float v0[32], v1[32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 32; ++e) {
         const int u = min(u0 + e, nb - 1);  // past the block's last key: weight 0, row in range
-        load_pair(A.vcache, A.kv_bf16, cbase + (size_t)(kb * 64 + u) * D + 2 * lane, v0[e], v1[e]);
+        load_pair<BF>(A.vcache, cbase + (size_t)(kb * 64 + u) * D + 2 * lane, v0[e], v1[e]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int e = 0; e < 32; ++e)
 #pragma unroll
         for (int h = 0; h < QPG; ++h) {
           const float pu = u0 + e < nb ? pw[w][h][u0 + e] : 0.f;
@@ -392,56 +445,165 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
 }
 
 // ------------------------------------------------------------------ residual + norm
-// x[n] += sum of the ks partials (in order); the layer output is recorded when slot
-// >= 0; then RMSNorm with gains g, split for the next product.
-__global__ __launch_bounds__(256) void pf_resid_kernel(PfArgs A, const float* g, int ks, int slot) {
-  __shared__ float red[4];
-  const int n = blockIdx.x, H = A.H;
-  if (n >= A.m) { zero_split(A.xs, H, A.npp, n); return; }
-  float* x = A.x + (size_t)n * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    float y = 0.f;
-    for (int s = 0; s < ks; ++s) y += A.part[((size_t)s * A.npp + n) * H + i];
-    const float v = x[i] + y;
-    x[i] = v;
-    if (slot >= 0 && A.dbg_hidden) A.dbg_hidden[((size_t)n * (A.L + 1) + slot) * H + i] = v;
+// grid (npp, H/512), 64 threads, 8 columns per thread: x[n] += the sum of the ks
+// partials (in order); the layer output is recorded when slot >= 0; then gains * x
+// split for the next product and the block's sum of squares.
+__global__ __launch_bounds__(64) void pf_resid_kernel(PfArgs A, const float* g, int ks, int slot) {
+  const int n = blockIdx.x, H = A.H, c = blockIdx.y * 64 + threadIdx.x;
+  if (n >= A.m) { zero_split8(A.xs, H, A.npp, n, c); return; }
+  float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8];
+#pragma unroll 8
+  for (int s = 0; s < ks; ++s) {
+    float t[8];
+    load8(A.part + ((size_t)s * A.npp + n) * H + 8 * c, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] += t[e];
   }
-  __syncthreads();
-  norm_split(x, g, H, A.eps, A.xs, A.npp, n, red);
+  float* x = A.x + (size_t)n * H + 8 * c;
+  load8(x, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] += y[e];
+  store8(x, v);
+  if (slot >= 0 && A.dbg_hidden) store8(A.dbg_hidden + ((size_t)n * (A.L + 1) + slot) * H + 8 * c, v);
+  gain_split(A, g, n, c, v);
 }
 
 // ------------------------------------------------------------------ SwiGLU
-// Gate/up rows come in the arena's order: slice x of I/8 columns, 32 runs of HALF gate
-// rows then HALF up rows; column c of the intermediate is gate row x*2IX + r*2HALF + i
-// with x = c / IX, r = (c % IX) / HALF, i = c % HALF.  The output is split in natural
-// column order, which is the down tiles' column order.
-__global__ __launch_bounds__(256) void pf_swiglu_kernel(PfArgs A, int ks) {
-  const int n = blockIdx.x, I = A.I;
-  if (n >= A.m) { zero_split(A.xs, I, A.npp, n); return; }
+// grid (npp, I/512), 64 threads, 8 intermediate columns per thread.  Gate/up rows come
+// in the arena's order: slice x of I/8 columns, 32 runs of HALF gate rows then HALF up
+// rows; column c of the intermediate is gate row x*2IX + r*2HALF + i with x = c / IX,
+// r = (c % IX) / HALF, i = c % HALF.  Both sums are scaled by the row's 1/rms (the
+// post-attention norm).  The output is split in natural column order, which is the
+// down tiles' column order.
+__global__ __launch_bounds__(64) void pf_swiglu_kernel(PfArgs A, int ks) {
+  const int n = blockIdx.x, I = A.I, c = blockIdx.y * 64 + threadIdx.x;
+  if (n >= A.m) { zero_split8(A.xs, I, A.npp, n, c); return; }
   const int IX = I / kXcds, HALF = IX / kPerXcd, R = 2 * I;
-  for (int c = threadIdx.x; c < I / 8; c += blockDim.x) {
-    float v[8];
+  const float rs = row_rs(A, n);
+  int mg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int ci = 8 * c + e;
+    mg[e] = (ci / IX) * 2 * IX + ((ci % IX) / HALF) * 2 * HALF + ci % HALF;
+  }
+  float gt[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, up[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int s = 0; s < ks; ++s) {
+    const float* pp = A.part + ((size_t)s * A.npp + n) * R;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int ci = 8 * c + e;
-      const int mg = (ci / IX) * 2 * IX + ((ci % IX) / HALF) * 2 * HALF + ci % HALF;
-      float gt = 0.f, up = 0.f;
-      for (int s = 0; s < ks; ++s) {
-        const float* pp = A.part + ((size_t)s * A.npp + n) * R;
-        gt += pp[mg];
-        up += pp[mg + HALF];
-      }
-      v[e] = gt / (1.f + __expf(-gt)) * up;
+      gt[e] += pp[mg[e]];
+      up[e] += pp[mg[e] + HALF];
     }
-    store_split8(A.xs, I, A.npp, n, c, v);
+  }
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float gr = gt[e] * rs;
+    v[e] = gr / (1.f + __expf(-gr)) * (up[e] * rs);
+  }
+  store_split8(A.xs, I, A.npp, n, c, v);
+}
+
+// ------------------------------------------------------------------ first id
+// Logits of the last prompt position: the final-norm row (gains * x * 1/rms) in LDS,
+// 16 vocabulary rows per wave, 64 per workgroup, each row a 64-lane dot product over
+// 16-byte weight loads; the workgroup's largest logit (ties: lowest row) goes to
+// blk_val/blk_idx.  H is 1024 or 2048 here.
+__global__ __launch_bounds__(256) void pf_lm_kernel(PfArgs A, LmArgs M) {
+  constexpr int RPW = kLmRowsPerBlock / 4;
+  __shared__ float xn[2048];
+  __shared__ float bv[4];
+  __shared__ int bi[4];
+  const int H = A.H, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float rs = row_rs(A, M.n_last);
+  const float* x = A.x + (size_t)M.n_last * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) xn[i] = M.g_final[i] * (x[i] * rs);
+  __syncthreads();
+  const int r0 = blockIdx.x * kLmRowsPerBlock + wv * RPW;
+  float best = -INFINITY;
+  int besti = 0x7fffffff;
+  float acc[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) acc[j] = 0.f;
+  for (int t = 0; t < H / 512; ++t) {  // 512 columns per pass, 8 per lane
+    const int c = 8 * (lane + 64 * t);
+    uint4 wr[RPW];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = min(r0 + j, A.vocab - 1);  // rows past the vocabulary re-read the last one
+      wr[j] = *reinterpret_cast<const uint4*>(M.lm_head + (size_t)r * H + c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const uint32_t w[4] = {wr[j].x, wr[j].y, wr[j].z, wr[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[j] = fmaf(__uint_as_float(w[e] << 16), xn[c + 2 * e], acc[j]);
+        acc[j] = fmaf(__uint_as_float(w[e] & 0xffff0000u), xn[c + 2 * e + 1], acc[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const float v = wsum(acc[j]);
+    const int r = r0 + j;
+    if (r < A.vocab && (v > best || (v == best && r < besti))) { best = v; besti = r; }
+  }
+  if (lane == 0) { bv[wv] = best; bi[wv] = besti; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int v = 1; v < 4; ++v)
+      if (bv[v] > best || (bv[v] == best && bi[v] < besti)) { best = bv[v]; besti = bi[v]; }
+    M.blk_val[blockIdx.x] = best;
+    M.blk_idx[blockIdx.x] = besti;
+  }
+}
+
+// The largest of the workgroup maxima (ties: lowest row), published: the device
+// output, the feedback id, the pinned mirror, then the progress word.
+__global__ __launch_bounds__(256) void pf_argmax_kernel(LmArgs M, int n_blk) {
+  __shared__ float bv[256];
+  __shared__ int bi[256];
+  float best = -INFINITY;
+  int besti = 0x7fffffff;
+  for (int k = threadIdx.x; k < n_blk; k += blockDim.x) {
+    const float v = M.blk_val[k];
+    const int i = M.blk_idx[k];
+    if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+  }
+  bv[threadIdx.x] = best;
+  bi[threadIdx.x] = besti;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      const float v = bv[threadIdx.x + s];
+      const int i = bi[threadIdx.x + s];
+      if (v > bv[threadIdx.x] || (v == bv[threadIdx.x] && i < bi[threadIdx.x])) {
+        bv[threadIdx.x] = v;
+        bi[threadIdx.x] = i;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int id = bi[0];
+    if (id == 0x7fffffff) id = 0;  // every logit NaN: row 0
+    M.out_first[0] = id;
+    *M.last_id = id;
+    if (M.pinned_ids) __hip_atomic_store(M.pinned_ids, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __threadfence_system();
+    __hip_atomic_store(M.progress, ((unsigned long long)M.call_seq << 32) | 1ull, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
 // ------------------------------------------------------------------ self-test helpers
-__global__ __launch_bounds__(256) void pf_split_kernel(const float* x, int K, int m, int npp, uint16_t* xs) {
+__global__ __launch_bounds__(64) void pf_split_kernel(const float* x, int K, int m, int npp, uint16_t* xs) {
   const int n = blockIdx.x;
-  if (n >= m) { zero_split(xs, K, npp, n); return; }
   for (int c = threadIdx.x; c < K / 8; c += blockDim.x) {
+    if (n >= m) { zero_split8(xs, K, npp, n, c); continue; }
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = x[(size_t)n * K + 8 * c + e];
@@ -459,40 +621,48 @@ __global__ __launch_bounds__(256) void pf_reduce_kernel(const float* part, int k
 }
 
 // ------------------------------------------------------------------ host side
+// How a product is cut: KC columns per wave (the widest of 256/128/64 dividing the K
+// block that still gives 1024 waves or more: a wave streams 32 rows x KC columns, so
+// narrower runs put more weight bytes in flight at once), and WK waves per workgroup
+// over adjacent runs (the most, up to 4, whose WK*KC columns stay inside one K block),
+// which leaves K / (WK*KC) partial sums per output.
+struct Cut { int kc, wk, ks; };
+Cut pick_cut(int R, int KB, int K) {
+  Cut c{-1, 0, 0};
+  if (R % 32 || KB % 64 || K % KB) return c;
+  int kc = 256;
+  while (kc > 64 && KB % kc) kc /= 2;
+  while (kc > 64 && (R / 32) * (K / kc) < 1024) kc /= 2;
+  int wk = 4;
+  while (wk > 1 && KB % (wk * kc)) --wk;
+  c.kc = kc;
+  c.wk = wk;
+  c.ks = K / (wk * kc);
+  return c;
+}
+
 template <int NT>
-int launch_gemm_nt(const uint16_t* w, int R, int KB, int K, int kc, const uint16_t* xs, float* part, hipStream_t st) {
-  const int waves = (R / 32) * (K / kc);
-  const dim3 grid((waves + 3) / 4), block(256);
-  switch (kc) {
-    case 64: hipLaunchKernelGGL((pf_gemm_kernel<NT, 1>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
-    case 128: hipLaunchKernelGGL((pf_gemm_kernel<NT, 2>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
-    case 256: hipLaunchKernelGGL((pf_gemm_kernel<NT, 4>), grid, block, 0, st, w, R, KB, K, xs, part, waves); break;
+int launch_gemm_nt(const uint16_t* w, int R, int KB, int K, Cut c, const uint16_t* xs, float* part, hipStream_t st) {
+  const dim3 grid((R / 32) * c.ks), block(64 * c.wk);
+  switch (c.kc) {
+    case 64: hipLaunchKernelGGL((pf_gemm_kernel<NT, 1>), grid, block, 0, st, w, R, KB, K, xs, part); break;
+    case 128: hipLaunchKernelGGL((pf_gemm_kernel<NT, 2>), grid, block, 0, st, w, R, KB, K, xs, part); break;
+    case 256: hipLaunchKernelGGL((pf_gemm_kernel<NT, 4>), grid, block, 0, st, w, R, KB, K, xs, part); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// Columns per wave of a product: the widest of 256/128/64 that divides the K block,
-// narrowed while the product has fewer than 1024 waves (a wave streams 32 rows x KC
-// columns, so narrower runs put more weight bytes in flight at once).
-int pick_kc(int R, int KB, int K) {
-  int kc = 256;
-  while (kc > 64 && KB % kc) kc /= 2;
-  if (KB % kc || K % kc || R % 32) return -1;
-  while (kc > 64 && (R / 32) * (K / kc) < 1024) kc /= 2;
-  return kc;
-}
-
 int launch_gemm(const uint16_t* w, int R, int KB, int K, int npp, const uint16_t* xs, float* part, hipStream_t st,
                 int* ks) {
-  const int kc = pick_kc(R, KB, K);
-  if (kc < 0) return -1;
-  *ks = K / kc;
+  const Cut c = pick_cut(R, KB, K);
+  if (c.kc < 0) return -1;
+  *ks = c.ks;
   switch (npp) {
-    case 16: return launch_gemm_nt<1>(w, R, KB, K, kc, xs, part, st);
-    case 32: return launch_gemm_nt<2>(w, R, KB, K, kc, xs, part, st);
-    case 48: return launch_gemm_nt<3>(w, R, KB, K, kc, xs, part, st);
-    case 64: return launch_gemm_nt<4>(w, R, KB, K, kc, xs, part, st);
+    case 16: return launch_gemm_nt<1>(w, R, KB, K, c, xs, part, st);
+    case 32: return launch_gemm_nt<2>(w, R, KB, K, c, xs, part, st);
+    case 48: return launch_gemm_nt<3>(w, R, KB, K, c, xs, part, st);
+    case 64: return launch_gemm_nt<4>(w, R, KB, K, c, xs, part, st);
   }
   return -1;
 }
@@ -504,9 +674,9 @@ size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I) {
   const int dims[4][3] = {{NKV * (QPG + 2) * D, H, H}, {H, QPG * D, NQ * D}, {2 * I, H, H}, {H, I / kXcds, I}};
   size_t best = 0;
   for (const auto& d : dims) {
-    const int kc = pick_kc(d[0], d[1], d[2]);
-    if (kc < 0) return 0;
-    const size_t need = (size_t)(d[2] / kc) * kPrefillChunk * d[0];
+    const Cut c = pick_cut(d[0], d[1], d[2]);
+    if (c.kc < 0) return 0;
+    const size_t need = (size_t)c.ks * kPrefillChunk * d[0];
     if (need > best) best = need;
   }
   return best;
@@ -515,9 +685,11 @@ size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I) {
 int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayout& lay, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int H = A.H, D = A.D, NQ = A.NQ, NKV = A.NKV, I = A.I, QPG = NQ / NKV;
-  if (D != 128 || QPG != 2 || A.npp % 16 || A.npp > kPrefillChunk || A.m <= 0 || A.m > A.npp) return -1;
+  if (D != 128 || QPG != 2 || H % 512 || I % 512 || A.npp % 16 || A.npp > kPrefillChunk || A.m <= 0 || A.m > A.npp)
+    return -1;
   const dim3 b256(256);
-  hipLaunchKernelGGL(pf_input_kernel, dim3(A.npp), b256, 0, st, A);
+  const dim3 b64(64), rows_h(A.npp, H / 512), rows_i(A.npp, I / 512);
+  hipLaunchKernelGGL(pf_input_kernel, rows_h, b64, 0, st, A);
   for (int l = 0; l < A.L; ++l) {
     const uint8_t* base = layers + (size_t)l * lay.stride;
     const float* G = reinterpret_cast<const float*>(base + lay.gains);
@@ -526,17 +698,27 @@ int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayo
                     st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_qkv_kernel, dim3(NKV, A.m), b256, 0, st, A, l, G, ks);
-    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), b256, 0, st, A, l);
+    if (A.kv_bf16) hipLaunchKernelGGL(pf_attn_kernel<true>, dim3(NKV, A.npp), b256, 0, st, A, l);
+    else hipLaunchKernelGGL(pf_attn_kernel<false>, dim3(NKV, A.npp), b256, 0, st, A, l);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
       return -1;
-    hipLaunchKernelGGL(pf_resid_kernel, dim3(A.npp), b256, 0, st, A, G, ks, -1);
+    hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G, ks, -1);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.gu), 2 * I, H, H, A.npp, A.xs, A.part, st, &ks))
       return -1;
-    hipLaunchKernelGGL(pf_swiglu_kernel, dim3(A.npp), b256, 0, st, A, ks);
+    hipLaunchKernelGGL(pf_swiglu_kernel, rows_i, b64, 0, st, A, ks);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.down), H, I / kXcds, I, A.npp, A.xs, A.part, st, &ks))
       return -1;
-    hipLaunchKernelGGL(pf_resid_kernel, dim3(A.npp), b256, 0, st, A, G + H + 2 * D, ks, l + 1);
+    hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G + H + 2 * D, ks, l + 1);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_prefill_lm(const PfArgs& A, const LmArgs& M, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (A.H % 512 || A.H > 2048 || M.n_last < 0 || M.n_last >= A.m) return -1;
+  const int n_blk = (A.vocab + kLmRowsPerBlock - 1) / kLmRowsPerBlock;
+  hipLaunchKernelGGL(pf_lm_kernel, dim3(n_blk), dim3(256), 0, st, A, M);
+  hipLaunchKernelGGL(pf_argmax_kernel, dim3(1), dim3(256), 0, st, M, n_blk);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -544,7 +726,7 @@ int launch_gemm_selftest(const uint16_t* w, int R, int K, const float* x, int m,
                          void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int npp = (m + 15) / 16 * 16;
-  hipLaunchKernelGGL(pf_split_kernel, dim3(npp), dim3(256), 0, st, x, K, m, npp, xs);
+  hipLaunchKernelGGL(pf_split_kernel, dim3(npp), dim3(64), 0, st, x, K, m, npp, xs);
   int ks = 0;
   if (launch_gemm(w, R, K, K, npp, xs, part, st, &ks)) return -1;
   hipLaunchKernelGGL(pf_reduce_kernel, dim3(m), dim3(256), 0, st, part, ks, npp, R, m, y);

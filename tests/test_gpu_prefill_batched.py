@@ -8,8 +8,9 @@
 * against the position-by-position prefill on the same handle: same first id (unless
   the oracle's top two logits are within rounding of each other), hidden states and
   the following decode steps within the parity tolerance;
-* a one-position prompt equals mk_prefill bit for bit (it is the same launch), and a
-  float32-weight handle is refused with MK_ERR_UNSUPPORTED.
+* the smallest prompt (one position), the full text vocabulary in the first id's LM
+  head, the progress word and greedy feedback after the call, and a float32-weight
+  handle refused with MK_ERR_UNSUPPORTED.
 """
 import numpy as np
 import pytest
@@ -91,23 +92,44 @@ def test_full_talker_0p6b_prompt():
     _case(shape)
 
 
-def test_one_position_prompt_is_the_persistent_launch():
+def test_one_position_prompt():
+    """The smallest prompt: one position, a single 16-column tile with one live column."""
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-pb1", n_layers=2, prompt_len=1, steps=4)
+    _case(shape)
+
+
+def test_text_vocab_lm_head_two_layers():
+    """The full 151936-row text vocabulary in the first id's LM head."""
+    shape = wl.TEXT_0P6B.replace(name="q06-2l-pbV", n_layers=2, prompt_len=12, steps=2)
+    _case(shape)
+
+
+def test_progress_and_feedback_after_batched_prefill():
+    """The first id is published like a decode step's: the progress word reads 1 and a
+    feedback decode continues from it exactly as after mk_prefill with the same id."""
     import torch
     from persistent_megakernel_loop_amd.binding import Decoder, weights_to_device
 
-    shape = wl.TALKER_0P6B.replace(name="talker-2l-pb1", n_layers=2, prompt_len=1, steps=4)
-    print(f"[case] {shape.name}: one position, batched vs mk_prefill", flush=True)
-    inp = make_inputs(shape)
+    shape = wl.TEXT_0P6B.replace(name="q06-2l-v1000-fb", n_layers=2, vocab=1000, prompt_len=10, steps=6)
+    print(f"[case] {shape.name}: progress word and greedy feedback after the batched prefill", flush=True)
     dec = Decoder(shape, weights_to_device(wl.make_weights(shape)))
-    outs = []
-    for batched in (False, True):
-        dec.reset()
-        outs.append(run_gpu(shape, None, inp, dec=dec, batched=batched))
-    dec.close()
+    ids = torch.from_numpy(wl.make_prompt_ids(shape)).cuda()
+    first = dec.prefill(ids, batched=True)
     torch.cuda.synchronize()
-    a, b = outs
-    assert a.first_id == b.first_id and np.array_equal(a.ids, b.ids)
-    assert np.array_equal(a.hidden.view(np.uint32), b.hidden.view(np.uint32))
+    assert dec.progress() == 1
+    out = dec.decode(shape.steps)
+    torch.cuda.synchronize()
+    dec.check()
+    # the same prompt position by position, decoded teacher-forced from the batched first id
+    dec.reset()
+    dec.prefill(ids)
+    steps = torch.cat([first, out[:-1]]).to(torch.int32)
+    ref = dec.decode(shape.steps, steps)
+    torch.cuda.synchronize()
+    dec.check()
+    dec.close()
+    # the cache entries differ by rounding order only: the greedy ids agree on this case
+    assert np.array_equal(out.cpu().numpy(), ref.cpu().numpy())
 
 
 def test_float32_weights_refused():
