@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--workload", default="talker-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ttfc-trials", type=int, default=10)
+    ap.add_argument("--ablation-steps", type=int, default=32,
+                    help="decode steps of the launch-per-phase ablation (0 turns it off)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (known bytes for scaling HBM counters) and exit")
     ap.add_argument("--hbm-summary", metavar="DIR", help="only print the HBM counter summary of the passes under DIR")
@@ -356,6 +358,31 @@ def main():
         ttfc_pp = ttfc_run(False)
         pf_ms = {"batched": prefill_ms(True), "per_position": prefill_ms(False)}
 
+    # launch-per-phase ablation: the same decode steps, each as one launch per phase (the
+    # batched prefill's kernels at one position: input, 9 per layer, LM head, argmax),
+    # after the same prompt; greedy workloads feed each call's id to the next call
+    ablation = {}
+    n_abl = min(args.ablation_steps, K)
+    if P and n_abl > 0:
+        prepare()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for st in range(n_abl):
+            ids = inp["step_ids"][st:st + 1] if inp["step_ids"] is not None else first
+            rows = inp["step_rows"][st:st + 1] if inp["step_rows"] is not None else None
+            pos3 = inp["step_pos3"][st:st + 1] if inp["step_pos3"] is not None else None
+            dec.prefill(ids, rows, pos3, out=first, batched=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        host = (time.perf_counter() - t0) * 1e3 / n_abl
+        dec.check()
+        per = a.elapsed_time(b) / n_abl
+        ablation = {"ms_per_step": round(per, 4), "host_ms_per_step": round(host, 4),
+                    "over_persistent": round(per / ms_step, 2), "steps": n_abl,
+                    "launches_per_step": 9 * shape.n_layers + 3}
+
     # barrier share: in-kernel wait ticks over position ticks, one separate traced run
     prepare()
     trace = torch.zeros((K, dec.grid_size(), 2), dtype=torch.int64, device="cuda")
@@ -388,6 +415,7 @@ def main():
         "ttfc_ms": ttfc,
         "ttfc_ms_per_position_prefill": ttfc_pp,
         "prefill_ms": pf_ms,
+        "launch_per_phase": ablation,
         "rtf_talker_only": round(ms_step / FRAME_MS, 5),
         "barrier_share": round(share, 4),
         "wall_ms_timed_launch": round(wall_ms, 3),

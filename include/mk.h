@@ -185,6 +185,20 @@ int mk_set_spin_limit(mk_handle* h, uint32_t polls);
  * time-to-first-chunk.  A prefill publishes one id. */
 int mk_progress(mk_handle* h, int64_t* steps_done);
 
+/* Host-side streaming of the ids as they are published (the dev.to article "Porting a
+ * 1200-line persistent CUDA megakernel to Qwen3-TTS", "Making it talk end-to-end":
+ * audio tokens leave chunk by chunk, and the first chunk cannot wait for the rest).
+ * Copies ids [first, first + count) of the most recently enqueued
+ * prefill/decode call from the pinned mirror into host_out, without synchronizing.
+ * MK_ERR_ARG if fewer than first + count ids are published yet (see mk_progress) or
+ * an argument is out of range. */
+int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out);
+
+/* *idle = 1 if the handle's stream has finished everything enqueued on it, else 0;
+ * no synchronization (a poll loop over mk_progress uses it to notice a call that
+ * ended early, e.g. on a wait timeout).  MK_ERR_HIP if the stream reports an error. */
+int mk_query(mk_handle* h, int32_t* idle);
+
 /* Synchronize the stream and report the device error word (MK_OK when clean).
  * The word is cleared by the read. */
 int mk_status(mk_handle* h);

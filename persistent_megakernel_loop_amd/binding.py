@@ -18,7 +18,7 @@ _LIB_NAME = "libmk.so"
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_grid_size",
+           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
@@ -74,6 +74,8 @@ def lib():
     L.mk_set_phase_trace.argtypes = [vp, vp, i32]
     L.mk_set_spin_limit.argtypes = [vp, ctypes.c_uint32]
     L.mk_progress.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
+    L.mk_read_ids.argtypes = [vp, i32, i32, pi32]
+    L.mk_query.argtypes = [vp, pi32]
     L.mk_status.argtypes = [vp]
     L.mk_error_info.argtypes = [vp, pi32]
     L.mk_selftest_lds_dma.argtypes = [vp, vp, i32, i32, vp]
@@ -215,6 +217,39 @@ class Decoder:
         v = ctypes.c_int64()
         _check(lib().mk_progress(self.handle, ctypes.byref(v)), "mk_progress")
         return v.value
+
+    def read_ids(self, first: int, count: int) -> np.ndarray:
+        """Ids [first, first + count) of the last call, from the pinned mirror (no sync)."""
+        buf = (ctypes.c_int32 * max(count, 1))()
+        _check(lib().mk_read_ids(self.handle, first, count, buf), "mk_read_ids")
+        return np.frombuffer(buf, dtype=np.int32, count=count).copy()
+
+    def idle(self) -> bool:
+        v = ctypes.c_int32()
+        _check(lib().mk_query(self.handle, ctypes.byref(v)), "mk_query")
+        return bool(v.value)
+
+    def stream(self, n_steps: int, ids=None, rows=None, pos3=None, chunk: int = 4, out=None):
+        """Enqueue one decode launch of n_steps steps and yield its ids as numpy chunks of
+        `chunk` (the last may be shorter) while the kernel runs, read from the pinned
+        mirror as the progress word advances.  Raises MkError if the launch ends early
+        with a device error."""
+        self.decode(n_steps, ids, rows, pos3, out=out)
+        done = 0
+        while done < n_steps:
+            p = self.progress()
+            if p - done >= chunk or p == n_steps:
+                yield self.read_ids(done, p - done)
+                done = p
+            elif self.idle():
+                p = self.progress()
+                if p > done:
+                    yield self.read_ids(done, p - done)
+                    done = p
+                if done < n_steps:
+                    self.check()
+                    raise RuntimeError(f"decode ended after {done} of {n_steps} ids")
+        self.check()
 
     def status(self) -> int:
         return lib().mk_status(self.handle)

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -548,6 +549,25 @@ int mk_progress(mk_handle* h, int64_t* steps_done) {
   const unsigned long long v = *(volatile unsigned long long*)h->progress;
   *steps_done = (uint32_t)(v >> 32) == h->call_seq ? (int64_t)(v & 0xffffffffu) : 0;
   return MK_OK;
+}
+
+int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out) {
+  if (!h || !host_out || first < 0 || count < 0) return MK_ERR_ARG;
+  int64_t done = 0;
+  mk_progress(h, &done);
+  if ((int64_t)first + count > done || first + count > h->pinned_cap) return MK_ERR_ARG;
+  // the progress word is stored after the ids it counts (device side, system scope)
+  std::atomic_thread_fence(std::memory_order_acquire);
+  for (int32_t i = 0; i < count; ++i) host_out[i] = ((volatile int32_t*)h->pinned_ids)[first + i];
+  return MK_OK;
+}
+
+int mk_query(mk_handle* h, int32_t* idle) {
+  if (!h || !idle) return MK_ERR_ARG;
+  const hipError_t e = hipStreamQuery(h->stream);
+  if (e == hipSuccess) { *idle = 1; return MK_OK; }
+  if (e == hipErrorNotReady) { *idle = 0; return MK_OK; }
+  return MK_ERR_HIP;
 }
 
 int mk_status(mk_handle* h) {

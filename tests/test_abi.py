@@ -161,6 +161,8 @@ def test_null_handle_calls(lib):
     info = (ctypes.c_int32 * 5)()
     assert lib.mk_prefill(None, 0x10, None, None, 4, 0x20) == -1
     assert lib.mk_prefill_batched(None, 0x10, None, None, 4, 0x20) == -1
+    assert lib.mk_read_ids(None, 0, 1, (ctypes.c_int32 * 1)()) == -1
+    assert lib.mk_query(None, ctypes.byref(ctypes.c_int32())) == -1
     assert lib.mk_decode(None, 4, None, None, None, 0x20) == -1
     assert lib.mk_load_kv(None, 0x10, 4) == -1
     assert lib.mk_reset(None) == -1
