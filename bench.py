@@ -73,6 +73,30 @@ def gpu_inputs(shape, n_prompt, n_steps, torch):
                 step_rows=rows[n_prompt:].contiguous(), step_pos3=pos3[n_prompt:].contiguous())
 
 
+def stream_ceiling(torch, gib: int = 2, runs: int = 5) -> dict:
+    """GB/s of the library's streaming-read kernel over a gib-GiB buffer (best of runs,
+    HIP events on the launch stream), with plain and with non-temporal loads."""
+    from persistent_megakernel_loop_amd.binding import bench_stream_read
+
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {}
+    for nt in (False, True):
+        best = float("inf")
+        for _ in range(runs + 1):  # the first run warms up
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            bench_stream_read(buf, nontemporal=nt, sink=sink, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        out["nontemporal_gbps" if nt else "plain_gbps"] = round(buf.numel() / (best * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(shape, n_prompt, n_steps, budget_s=12.0):
     """The oracle (float64 numpy) timed on this host on a bounded sample of the same workload.
 
@@ -221,7 +245,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="talker-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--ttfc-trials", type=int, default=10)
+    ap.add_argument("--ttfc-trials", type=int, default=20)
     ap.add_argument("--ablation-steps", type=int, default=32,
                     help="decode steps of the launch-per-phase ablation (0 turns it off)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -392,7 +416,12 @@ def main():
     dec.set_debug(None, None)
     tr = trace.cpu().numpy().astype(np.float64)
     share = float(tr[:, :, 0].sum() / max(tr[:, :, 1].sum(), 1.0))
+    per_step = tr[:, :, 0].sum(axis=1) / np.maximum(tr[:, :, 1].sum(axis=1), 1.0)
+    share_p99 = float(np.percentile(per_step, 99))
     dec.check()
+
+    # read-stream ceiling: the bandwidth a plain streaming read reaches on this device
+    ceiling = stream_ceiling(torch)
 
     res = {
         "metric": METRIC,
@@ -418,6 +447,8 @@ def main():
         "launch_per_phase": ablation,
         "rtf_talker_only": round(ms_step / FRAME_MS, 5),
         "barrier_share": round(share, 4),
+        "barrier_share_p99": round(share_p99, 4),
+        "stream_ceiling": dict(ceiling, decode_frac_of_ceiling=round(gbps / max(ceiling.values()), 4)),
         "wall_ms_timed_launch": round(wall_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(shape.name, K),

@@ -222,6 +222,16 @@ int mk_selftest_lds_dma(const void* d_src, void* d_dst, int32_t n_chunks, int32_
 int mk_selftest_gemm(const void* d_w, int32_t rows, int32_t k, const float* d_x, int32_t n, float* d_y,
                      void* stream);
 
+/* Measurement kernel: one streaming read of `bytes` from d_src (16-byte loads, 256
+ * threads per workgroup, `blocks` workgroups in a grid-stride loop; non-temporal
+ * loads when nontemporal != 0).  Its time gives the read bandwidth the device
+ * reaches, the ceiling the decode kernel's achieved bytes per second compare with.
+ * d_sink [blocks] uint64 is written only in a case that does not occur for real
+ * data patterns, so the loads stay.  Asynchronous on `stream`.  MK_ERR_ARG for NULL
+ * pointers, bytes not a positive multiple of 16, or blocks outside 1..65536. */
+int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal, uint64_t* d_sink, int32_t blocks,
+                         void* stream);
+
 /* Number of workgroups of the persistent grid (one per CU). */
 int mk_grid_size(mk_handle* h, int32_t* n);
 

@@ -608,6 +608,14 @@ int mk_selftest_gemm(const void* d_w, int32_t rows, int32_t k, const float* d_x,
   return e;
 }
 
+int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal, uint64_t* d_sink, int32_t blocks,
+                         void* stream) {
+  if (!d_src || !d_sink || bytes < 16 || bytes % 16 || blocks <= 0 || blocks > 65536) return MK_ERR_ARG;
+  return mk::launch_stream_read(d_src, (size_t)bytes, nontemporal, (unsigned long long*)d_sink, blocks, stream)
+             ? MK_ERR_HIP
+             : MK_OK;
+}
+
 int mk_grid_size(mk_handle* h, int32_t* n) {
   if (!h || !n) return MK_ERR_ARG;
   *n = mk::kGrid;

@@ -53,6 +53,9 @@ struct LmArgs {
 size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I);  // 0: shape not supported
 int launch_prefill_lm(const PfArgs& a, const LmArgs& lm, void* stream);
 int launch_prefill_chunk(const PfArgs& a, const uint8_t* layers, const LayerLayout& lay, void* stream);
+// Read-stream ceiling (a measurement kernel, not part of the decode path).
+int launch_stream_read(const void* src, size_t bytes, int nontemporal, unsigned long long* sink, int blocks,
+                       void* stream);
 int launch_gemm_selftest(const uint16_t* w, int R, int K, const float* x, int m, float* y, uint16_t* xs, float* part,
                          void* stream);
 

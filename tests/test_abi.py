@@ -184,6 +184,11 @@ def test_selftest_and_embed_sum_argument_checks(lib):
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 4, 8, None) == -1
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 9217, 0, None) == -1
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 1, 144 * 1024 - 8, None) == -1
+    # read-stream measurement kernel: non-null buffers, bytes a positive multiple of 16, 1..65536 blocks
+    assert lib.mk_bench_stream_read(None, 1024, 0, 0x10, 64, None) == -1
+    assert lib.mk_bench_stream_read(0x10, 1000, 0, 0x20, 64, None) == -1
+    assert lib.mk_bench_stream_read(0x10, 1024, 0, 0x20, 0, None) == -1
+    assert lib.mk_bench_stream_read(0x10, 1024, 0, None, 64, None) == -1
     # product self-test: rows % 32, k % 64, 1 <= n <= 64, non-null buffers
     assert lib.mk_selftest_gemm(None, 32, 64, 0x10, 1, 0x20, None) == -1
     assert lib.mk_selftest_gemm(0x10, 33, 64, 0x20, 1, 0x30, None) == -1
