@@ -131,7 +131,12 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
 /* The hot path: n_steps decode steps in ONE launch.  Step s runs at position
  * position+s and reads
  *   d_ids == NULL : the id picked by the previous step (step 0: by the last prefill
- *                   or decode call; MK_ERR_STATE if there is none);
+ *                   or decode call; MK_ERR_STATE if there is none): embed[id], and
+ *                   when d_embed_buf is given, embed[id] + row s of d_embed_buf: the
+ *                   talker's fed-back codebook-0 embedding plus the rest of the frame's
+ *                   17 embeddings, summed by the caller (the theaicatchup article, "Why
+ *                   Does a Single Kernel Even Matter for TTS?": the input is a sum of
+ *                   16 codebook embeddings and a text embedding);
  *   d_ids[s] >= 0 : embed[d_ids[s]];
  *   d_ids[s] <  0 : row s of d_embed_buf ([n_steps][hidden] float32).
  * d_pos3 as in mk_prefill.  d_out_ids [n_steps] int32 receives the greedy ids

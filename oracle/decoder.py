@@ -235,6 +235,13 @@ class Decoder:
             raise ValueError("a negative id needs a precomputed row")
         return np.asarray(row, dtype=np.float32).astype(self.dtype)
 
+    def feedback_row(self, token_id: int, rest: np.ndarray) -> np.ndarray:
+        """Greedy feedback with a precomputed row: the fed-back id's embedding plus the
+        rest of the frame's embeddings ([P3] "Why Does a Single Kernel Even Matter for
+        TTS?": the input is the sum of 16 codebook rows and a text row; the talker's own
+        table gives the fed-back codebook-0 row, the caller sums the other 16)."""
+        return self.embed[token_id] + np.asarray(rest, dtype=np.float32).astype(self.dtype)
+
     def step(self, x0: np.ndarray, pos3: Optional[Sequence[int]] = None,
              want_logits: bool = True):
         """Run position ``self.pos`` on input row x0.

@@ -1857,11 +1857,15 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
         }
         if (id >= 0) {
           const uint8_t* row = reinterpret_cast<const uint8_t*>(P.embed) + (size_t)id * B::H * B::WB;
+          // greedy feedback with rows: the fed-back id's embedding plus row t (the rest of
+          // the frame's embeddings, summed by the caller)
+          const float* rest = (P.feedback && P.rows) ? P.rows + (size_t)t * B::H : nullptr;
 #pragma unroll
           for (int k = 0; k < B::HPL; ++k) {
             const int i = lane + 64 * k;
-            S.xs[i] = B::BF16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(row)[i])
-                              : reinterpret_cast<const float*>(row)[i];
+            const float e = B::BF16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(row)[i])
+                                    : reinterpret_cast<const float*>(row)[i];
+            S.xs[i] = rest ? e + rest[i] : e;
           }
         } else {
           const float* row = P.rows + (size_t)t * B::H;

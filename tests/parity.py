@@ -125,7 +125,10 @@ def run_oracle(shape, weights, inp: Inputs, gpu: GpuRun, dtype=np.float64, steps
         ids = inp.step_ids[:n]
     logits = np.full((n, shape.vocab), np.nan)
     for s in range(n):
-        x0 = dec.input_row(int(ids[s]), None if inp.step_rows is None else inp.step_rows[s])
+        if inp.step_ids is None and inp.step_rows is not None:  # feedback id + the frame's other rows
+            x0 = dec.feedback_row(int(ids[s]), inp.step_rows[s])
+        else:
+            x0 = dec.input_row(int(ids[s]), None if inp.step_rows is None else inp.step_rows[s])
         want = s % logits_every == 0 or s == n - 1
         lg, h = dec.step(x0, None if inp.step_pos3 is None else inp.step_pos3[s], want_logits=want)
         if want:

@@ -63,6 +63,24 @@ def test_q17_talker_two_layers():
     _case(shape)
 
 
+@pytest.mark.parametrize("shape", [
+    wl.TALKER_0P6B.replace(name="talker-2l-fbrows", n_layers=2, prompt_len=8, steps=24),
+    wl.TALKER_1P7B.replace(name="talker-1.7b-2l-fbrows", n_layers=2, kv_prefill=0, prompt_len=8, steps=12),
+], ids=lambda s: s.name)
+def test_greedy_feedback_plus_frame_rows(shape):
+    """Greedy feedback with rows: each step's input is the fed-back id's embedding plus
+    the step's row (the frame's other embeddings); the oracle replays the GPU's ids."""
+    import dataclasses
+
+    from persistent_megakernel_loop_amd.binding import weights_to_device
+
+    print(f"[case] {shape.name}: greedy feedback + rows, {shape.steps} steps", flush=True)
+    weights = wl.make_weights(shape)
+    inp = dataclasses.replace(make_inputs(shape), step_ids=None)
+    gpu = run_gpu(shape, weights_to_device(weights), inp)
+    print(f"[case] {shape.name}: {compare(gpu, run_oracle(shape, weights, inp, gpu))}", flush=True)
+
+
 def test_determinism_bitwise():
     from persistent_megakernel_loop_amd.binding import weights_to_device
 

@@ -230,3 +230,26 @@ def test_prefilled_cache_is_read_as_is():
     row = np.random.default_rng(14).standard_normal(64).astype(np.float32)
     _, h = dec.step(dec.input_row(-1, row), (5, 2, 1), want_logits=False)
     assert np.all(np.isfinite(h)) and dec.pos == 6
+
+
+def test_feedback_row_is_the_17_row_sum_with_the_fed_back_codebook0_row():
+    """Greedy feedback with rows: when the talker's embedding table holds codebook 0,
+    feedback_row(id, rest) is the 17-row input sum with codebook 0 at the fed-back id,
+    rest being the other 16 rows (codebooks 1..15 and text), up to the order of the
+    float32 additions."""
+    shape = _talker_small()
+    weights = wl.make_weights(shape)
+    tables = wl.make_talker_tables(shape.hidden, text_vocab=500, codebook_size=64)
+    cb0 = tables["codebooks"][0]
+    dec = Decoder.from_shape(shape, weights)
+    dec.embed = np.stack([wl_bf16(cb0[i]) for i in range(cb0.shape[0])]).astype(np.float64)
+    zero0 = tables["codebooks"].copy()
+    zero0[0] = 0  # bf16 bits of +0.0: the sum without codebook 0
+    for t in wl.make_talker_ids(6, text_vocab=500, codebook_size=64):
+        full = embed_sum17(tables["codebooks"], tables["text"], t)
+        rest = embed_sum17(zero0, tables["text"], t)
+        got = dec.feedback_row(int(t[0]), rest)
+        np.testing.assert_allclose(got, full, rtol=1e-6, atol=1e-7)
+        # a plausible slip (the row of another id, or no row at all) is caught
+        assert not np.allclose(dec.feedback_row(int(t[0]) ^ 1, rest), full, rtol=1e-6, atol=1e-7)
+        assert not np.allclose(rest, full, rtol=1e-6, atol=1e-7)
