@@ -145,3 +145,44 @@ def test_float32_weights_refused():
     assert e.value.code == MK_ERR_UNSUPPORTED
     assert dec.position == 0
     dec.close()
+
+
+def _batched_prefill_hidden(dec, shape, ids, rows=None, pos3=None):
+    import torch
+
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    L, H = shape.n_layers, shape.hidden
+    dec.reset()
+    hid = torch.zeros((len(ids), L + 1, H), dtype=torch.float32, device="cuda")
+    dec.set_debug(hid, None)
+    first = dec.prefill(t(ids), t(rows), t(pos3), batched=True)
+    torch.cuda.synchronize()
+    code = dec.status()
+    dec.set_debug(None, None)
+    return code, int(first.cpu()[0]), hid.cpu().numpy()
+
+
+def test_bad_id_and_position_flagged_and_read_as_zero():
+    """As on the persistent path: an id past the vocabulary and a rotary stream past the
+    table are flagged in the device error word (MK_ERR_DEVICE) and read as 0; the prompt
+    then equals, bit for bit, the prompt with 0 in their place."""
+    from persistent_megakernel_loop_amd.binding import Decoder, weights_to_device
+
+    MK_ERR_DEVICE = -7
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-pbbad", n_layers=2, prompt_len=20, steps=1)
+    print(f"[case] {shape.name}: batched prompt with a bad id, then a bad position stream", flush=True)
+    inp = make_inputs(shape)
+    dec = Decoder(shape, weights_to_device(wl.make_weights(shape)))
+    ids, fixed = inp.prompt_ids.copy(), inp.prompt_ids.copy()
+    ids[5], fixed[5] = shape.vocab + 7, 0
+    a = _batched_prefill_hidden(dec, shape, ids, inp.prompt_rows, inp.prompt_pos3)
+    b = _batched_prefill_hidden(dec, shape, fixed, inp.prompt_rows, inp.prompt_pos3)
+    assert a[0] == MK_ERR_DEVICE and b[0] == 0
+    assert a[1] == b[1] and np.array_equal(a[2].view(np.uint32), b[2].view(np.uint32))
+    pos, pfixed = inp.prompt_pos3.copy(), inp.prompt_pos3.copy()
+    pos[7, 1], pfixed[7, 1] = 1 << 24, 0
+    c = _batched_prefill_hidden(dec, shape, inp.prompt_ids, inp.prompt_rows, pos)
+    d = _batched_prefill_hidden(dec, shape, inp.prompt_ids, inp.prompt_rows, pfixed)
+    dec.close()
+    assert c[0] == MK_ERR_DEVICE and d[0] == 0
+    assert c[1] == d[1] and np.array_equal(c[2].view(np.uint32), d[2].view(np.uint32))
