@@ -447,13 +447,12 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   A.sec_end0 = c->n_sections == 1 ? c->head_dim : c->sections[0];
   A.sec_end1 = c->n_sections > 1 ? c->sections[0] + c->sections[1] : c->head_dim;
   A.eps = c->rms_eps;
-  A.kv_bf16 = c->kv_dtype == MK_BF16;
   A.embed = (const uint16_t*)h->embed;
   A.in_norm0 = h->in_norm0;
   A.rope_cos = h->rope_cos;
   A.rope_sin = h->rope_sin;
-  A.kcache = h->kcache;
-  A.vcache = h->vcache;
+  A.kcache = (uint16_t*)h->kcache;  // bf16: mk_create ties the cache dtype to the weight dtype
+  A.vcache = (uint16_t*)h->vcache;
   A.err = h->ctl;
   A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q; A.ss = h->pf_ss;
   for (int32_t t0 = 0; t0 < n; t0 += ch) {

@@ -14,13 +14,12 @@ struct PfArgs {
   int32_t H, D, NQ, NKV, I, L, vocab, max_seq, rope_positions;
   int32_t n_sections, sec_end0, sec_end1;
   float eps;
-  int32_t kv_bf16;
   const uint16_t* embed;     // [V][H] bf16
   const float* in_norm0;     // [H]
   const float* rope_cos;     // [rope_positions][D/2]
   const float* rope_sin;
-  void* kcache;              // [L][NKV][max_seq][D]
-  void* vcache;
+  uint16_t* kcache;          // [L][NKV][max_seq][D] bf16 (the batched path serves bf16 bodies, whose cache is bf16)
+  uint16_t* vcache;
   uint32_t* err;             // device error word
   int32_t m;                 // positions in the chunk
   int32_t npp;               // columns of the products: m rounded up to a multiple of 16

@@ -257,23 +257,13 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
       float* qo = A.q + ((size_t)n * A.NQ + g * QPG + h) * D;
       qo[lane] = o0 * qscale;
       qo[lane + 64] = o1 * qscale;
-    } else if (A.kv_bf16) {
-      uint16_t* kc = reinterpret_cast<uint16_t*>(A.kcache) + crow;
-      kc[lane] = to_bf16(o0);
-      kc[lane + 64] = to_bf16(o1);
     } else {
-      float* kc = reinterpret_cast<float*>(A.kcache) + crow;
-      kc[lane] = o0;
-      kc[lane + 64] = o1;
+      A.kcache[crow + lane] = to_bf16(o0);
+      A.kcache[crow + lane + 64] = to_bf16(o1);
     }
-  } else if (A.kv_bf16) {
-    uint16_t* vc = reinterpret_cast<uint16_t*>(A.vcache) + crow;
-    vc[lane] = to_bf16(a0);
-    vc[lane + 64] = to_bf16(a1);
   } else {
-    float* vc = reinterpret_cast<float*>(A.vcache) + crow;
-    vc[lane] = a0;
-    vc[lane + 64] = a1;
+    A.vcache[crow + lane] = to_bf16(a0);
+    A.vcache[crow + lane + 64] = to_bf16(a1);
   }
 }
 
@@ -283,52 +273,16 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
 // QPG query heads, the block's softmax weights go through LDS, and the values are
 // read as whole rows (lane i holds dims 2i, 2i+1).  The four waves' running maxima,
 // sums and outputs merge in LDS; the result goes out split for the O product.
-// Eight cache elements as loaded (bf16: one 16-byte load, float32: two), converted later
-// so that all of a row's loads can be in flight before the first is used.
-template <bool BF> struct Row8 { uint4 u; };
-template <> struct Row8<false> { float4 a, b; };
-
-template <bool BF>
-__device__ __forceinline__ Row8<BF> ld_row8(const void* cache, size_t idx) {
-  Row8<BF> r;
-  if constexpr (BF) {
-    r.u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(cache) + idx);
-  } else {
-    r.a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx);
-    r.b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(cache) + idx + 4);
-  }
-  return r;
-}
-
-template <bool BF>
-__device__ __forceinline__ void cvt_row8(const Row8<BF>& r, float v[8]) {
-  if constexpr (BF) {
-    const uint32_t w[4] = {r.u.x, r.u.y, r.u.z, r.u.w};
+// Eight bf16 cache elements widened to float32.
+__device__ __forceinline__ void cvt_row8(const uint4 r, float v[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __uint_as_float(w[e] << 16);
-      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-    }
-  } else {
-    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
-    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = __uint_as_float(w[e] << 16);
+    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
   }
 }
 
-template <bool BF>
-__device__ __forceinline__ void load_pair(const void* cache, size_t idx, float& v0, float& v1) {
-  if constexpr (BF) {
-    const uint32_t u = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(cache) + idx);
-    v0 = __uint_as_float(u << 16);
-    v1 = __uint_as_float(u & 0xffff0000u);
-  } else {
-    const float2 a = *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(cache) + idx);
-    v0 = a.x;
-    v1 = a.y;
-  }
-}
-
-template <bool BF>  // cache entries in bf16, else float32
 __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
   constexpr int D = 128, QPG = 2, NW = 4;
   __shared__ float qs[QPG][D];
@@ -361,14 +315,14 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
     float s[QPG];
 #pragma unroll
     for (int h = 0; h < QPG; ++h) s[h] = 0.f;
-    Row8<BF> kr[D / 8];
+    uint4 kr[D / 8];  // the whole key row in flight at once, converted after
 #pragma unroll
-    for (int j8 = 0; j8 < D / 8; ++j8) kr[j8] = ld_row8<BF>(A.kcache, krow + 8 * j8);
-    __builtin_amdgcn_sched_barrier(0);  // the whole key row in flight at once
+    for (int j8 = 0; j8 < D / 8; ++j8) kr[j8] = *reinterpret_cast<const uint4*>(A.kcache + krow + 8 * j8);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j8 = 0; j8 < D / 8; ++j8) {
       float kv[8];
-      cvt_row8<BF>(kr[j8], kv);
+      cvt_row8(kr[j8], kv);
 #pragma unroll
       for (int h = 0; h < QPG; ++h)
 #pragma unroll
@@ -395,7 +349,9 @@ __global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const int u = min(u0 + e, nb - 1);  // past the block's last key: weight 0, row in range
-        load_pair<BF>(A.vcache, cbase + (size_t)(kb * 64 + u) * D + 2 * lane, v0[e], v1[e]);
+        const uint32_t vv = *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)(kb * 64 + u) * D + 2 * lane);
+        v0[e] = __uint_as_float(vv << 16);
+        v1[e] = __uint_as_float(vv & 0xffff0000u);
       }
 #pragma unroll
       for (int e = 0; e < 32; ++e)
@@ -698,8 +654,7 @@ int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayo
                     st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_qkv_kernel, dim3(NKV, A.m), b256, 0, st, A, l, G, ks);
-    if (A.kv_bf16) hipLaunchKernelGGL(pf_attn_kernel<true>, dim3(NKV, A.npp), b256, 0, st, A, l);
-    else hipLaunchKernelGGL(pf_attn_kernel<false>, dim3(NKV, A.npp), b256, 0, st, A, l);
+    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), b256, 0, st, A, l);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G, ks, -1);
