@@ -211,7 +211,8 @@ def hbm_summary(outdir: str, workload: str, steps: int, copy_mib: int) -> str:
     fetch_b, write_b = f_dec * fs * 1024, w_dec * ws * 1024
     shape = wl.BY_NAME[workload]
     algo = step_bytes(shape, shape.kv_prefill + shape.prompt_len, steps)
-    base = "--ttfc-trials 0 --no-cpu-baseline" + ("" if workload == "talker-0.6b" else f" --workload {workload}")
+    base = "--ttfc-trials 0 --ablation-steps 0 --no-ceiling --no-cpu-baseline" + (
+        "" if workload == "talker-0.6b" else f" --workload {workload}")
     if steps != 256:
         base += f" --steps {steps}"
     lines = [
@@ -245,6 +246,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="talker-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="leave out the read-stream ceiling measurement")
     ap.add_argument("--ttfc-trials", type=int, default=20)
     ap.add_argument("--ablation-steps", type=int, default=32,
                     help="decode steps of the launch-per-phase ablation (0 turns it off)")
@@ -421,7 +423,7 @@ def main():
     dec.check()
 
     # read-stream ceiling: the bandwidth a plain streaming read reaches on this device
-    ceiling = stream_ceiling(torch)
+    ceiling = {} if args.no_ceiling else stream_ceiling(torch)
 
     res = {
         "metric": METRIC,
@@ -448,7 +450,7 @@ def main():
         "rtf_talker_only": round(ms_step / FRAME_MS, 5),
         "barrier_share": round(share, 4),
         "barrier_share_p99": round(share_p99, 4),
-        "stream_ceiling": dict(ceiling, decode_frac_of_ceiling=round(gbps / max(ceiling.values()), 4)),
+        "stream_ceiling": dict(ceiling, decode_frac_of_ceiling=round(gbps / max(ceiling.values()), 4)) if ceiling else {},
         "wall_ms_timed_launch": round(wall_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(shape.name, K),

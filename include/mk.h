@@ -237,6 +237,17 @@ int mk_selftest_gemm(const void* d_w, int32_t rows, int32_t k, const float* d_x,
 int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal, uint64_t* d_sink, int32_t blocks,
                          void* stream);
 
+/* Stress test of the tagged-word exchange every hop of the decode kernel uses (its own
+ * publish and gather code): one cooperative launch of the persistent grid runs `iters`
+ * rounds; in each, every workgroup publishes 64 words and gathers all 256 x 64 words of
+ * the round, checking every value against what its writer stored.  result (host,
+ * [3]): [0] words read with the right tag but a wrong value (stale or torn: must be 0),
+ * [1] workgroups whose wait gave up, [2] the device error word.  spin_limit as in
+ * mk_set_spin_limit (0: the default); a small limit forces the give-up path.
+ * Allocates and frees its buffers; synchronizes `stream`.  MK_ERR_ARG for iters <= 0 or
+ * a NULL result; MK_ERR_COOP if the grid cannot be launched co-resident. */
+int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, uint32_t* result, void* stream);
+
 /* Number of workgroups of the persistent grid (one per CU). */
 int mk_grid_size(mk_handle* h, int32_t* n);
 

@@ -18,7 +18,7 @@ _LIB_NAME = "libmk.so"
 MK_F32, MK_BF16 = 0, 1
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_bench_stream_read", "mk_grid_size",
+           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
@@ -80,6 +80,7 @@ def lib():
     L.mk_error_info.argtypes = [vp, pi32]
     L.mk_selftest_lds_dma.argtypes = [vp, vp, i32, i32, vp]
     L.mk_selftest_gemm.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    L.mk_selftest_exchange.argtypes = [i32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32), vp]
     L.mk_bench_stream_read.argtypes = [vp, ctypes.c_uint64, i32, vp, i32, vp]
     L.mk_grid_size.argtypes = [vp, pi32]
     L.mk_embed_sum.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp]
@@ -296,6 +297,13 @@ def selftest_gemm(w, x, y=None, stream=None):
         y = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     _check(lib().mk_selftest_gemm(_ptr(w), rows, k, _ptr(x), n, _ptr(y), _stream_handle(stream)), "mk_selftest_gemm")
     return y
+
+
+def selftest_exchange(iters: int, spin_limit: int = 0, stream=None):
+    """Stress test of the exchange protocol: (mismatched words, workgroups that gave up, device error word)."""
+    res = (ctypes.c_uint32 * 3)()
+    _check(lib().mk_selftest_exchange(iters, spin_limit, res, _stream_handle(stream)), "mk_selftest_exchange")
+    return tuple(int(v) for v in res)
 
 
 def bench_stream_read(src, nontemporal: bool = False, sink=None, blocks: int = 2048, stream=None):

@@ -615,6 +615,39 @@ int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal,
              : MK_OK;
 }
 
+int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, uint32_t* result, void* stream) {
+  if (iters <= 0 || !result) return MK_ERR_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t n_words = 2 * (size_t)mk::kGrid * 64;
+  unsigned long long* words = nullptr;
+  uint32_t* ctl = nullptr;
+  if (hipMalloc((void**)&words, n_words * 8) != hipSuccess) return MK_ERR_OOM;
+  if (hipMalloc((void**)&ctl, 256) != hipSuccess) {
+    hipFree(words);
+    return MK_ERR_OOM;
+  }
+  int e = MK_OK;
+  if (hipMemsetAsync(words, 0, n_words * 8, st) != hipSuccess || hipMemsetAsync(ctl, 0, 256, st) != hipSuccess)
+    e = MK_ERR_HIP;
+  Params P{};
+  P.tag0 = 1;
+  P.spin_limit = spin_limit ? spin_limit : kDefaultSpinLimit;
+  P.err = ctl;
+  P.abort_flag = ctl + 1;
+  P.xq = words;
+  uint32_t* bad = ctl + 16;  // [0] mismatched words, [1] workgroups whose wait gave up
+  if (e == MK_OK && mk::launch_exchange_stress(P, words, iters, bad, st)) e = MK_ERR_COOP;
+  uint32_t host[18] = {0};
+  if (hipStreamSynchronize(st) != hipSuccess || hipMemcpy(host, ctl, sizeof host, hipMemcpyDeviceToHost) != hipSuccess)
+    e = MK_ERR_HIP;
+  result[0] = host[16];
+  result[1] = host[17];
+  result[2] = host[0];
+  hipFree(words);
+  hipFree(ctl);
+  return e;
+}
+
 int mk_grid_size(mk_handle* h, int32_t* n) {
   if (!h || !n) return MK_ERR_ARG;
   *n = mk::kGrid;

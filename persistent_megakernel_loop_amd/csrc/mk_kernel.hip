@@ -2232,6 +2232,55 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_kernel(Params P) { persis
 // ------------------------------------------------------------------ small kernels
 // Self-test of the LDS DMA primitive: the seven worker waves copy n chunks of src into LDS
 // at byte offset off, wait for their copies, and every thread copies LDS back to dst.
+// Exchange stress test of the tagged-word protocol every hop uses: `iters` rounds in
+// which each workgroup publishes 64 words (tag tag0 + k, value a function of the
+// workgroup, the round and the word) into its slot of buffer k & 1, then gathers all
+// grid x 64 words of the round with `exchange`, the control wave and the seven worker
+// waves taking blocks in turn as in the decode gathers.  Every gathered word is
+// compared with the value its writer stored; bad[0] counts mismatches (a stale or torn
+// word whose tag matched), bad[1] the workgroups whose wait gave up.  Two buffers
+// suffice: a workgroup publishes round k + 1 only after it has read all of round k.
+__device__ __forceinline__ float stress_value(int b, int k, int i) {
+  return (float)((b * 977 + k * 131 + i * 7) & 0xffffff);  // exact in float32
+}
+
+__global__ void __launch_bounds__(kThreads) xchg_stress_kernel(Params P, u64* words, int iters, uint32_t* bad) {
+  constexpr int W = 64, N = kGrid * W;
+  __shared__ float got[N];
+  __shared__ int stop;
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) stop = 0;
+  __syncthreads();
+  uint32_t rounds = 0;
+  unsigned long long first_round = 0;
+  for (int k = 0; k < iters; ++k) {
+    u64* buf = words + (size_t)(k & 1) * N;
+    const uint32_t tag = P.tag0 + (uint32_t)k;
+    bool ok;
+    if (wave == 0) {
+      ok = exchange<Kp<N, kWorkerWaves + 1>::value, kWorkerWaves + 1>(
+          buf, N, tag, got, b * W, (b + 1) * W,
+          [&]() {
+            const float v = stress_value(b, k, lane);
+            st_tag(buf + b * W + lane, v, tag);
+            got[b * W + lane] = v;
+          },
+          lane, P, rounds, first_round, 0);
+    } else {
+      ok = exchange<Kp<N, kWorkerWaves + 1>::value, kWorkerWaves + 1>(buf, N, tag, got, b * W, (b + 1) * W, []() {},
+                                                                       lane, P, rounds, first_round, wave);
+    }
+    if (!ok) stop = 1;
+    __syncthreads();
+    if (stop) break;
+    uint32_t miss = 0;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) miss += got[i] != stress_value(i / W, k, i % W);
+    if (miss) atomicAdd(bad, miss);
+    __syncthreads();
+  }
+  if (stop && threadIdx.x == 0) atomicAdd(bad + 1, 1u);
+}
+
 __global__ void __launch_bounds__(kThreads) lds_dma_selftest_kernel(const u4* src, u4* dst, int n, int off) {
   __shared__ __align__(16) u4 buf[144 * 1024 / 16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -2329,6 +2378,15 @@ int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* t
   hipLaunchKernelGGL(embed_sum_kernel, dim3(n), dim3(256), 0, (hipStream_t)stream, codebooks, n_cb, cb_size, text,
                      text_vocab, hidden, bf16, ids, rows, bad);
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_exchange_stress(const Params& p, unsigned long long* words, int iters, uint32_t* bad, void* stream) {
+  Params pp = p;
+  u64* w = words;
+  void* args[] = {&pp, &w, &iters, &bad};
+  hipError_t e = hipLaunchCooperativeKernel((const void*)xchg_stress_kernel, dim3(kGrid), dim3(kThreads), args, 0,
+                                            (hipStream_t)stream);
+  return e == hipSuccess ? 0 : -1;
 }
 
 int launch_lds_dma_selftest(const void* src, void* dst, int n_chunks, int offset_bytes, void* stream) {
