@@ -155,3 +155,27 @@ def test_forced_timeout_reported_and_recovered(shape):
     dec.check()
     dec.close()
     assert np.array_equal(again.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("batched", [False, True], ids=["per-position", "batched"])
+def test_fill_to_capacity_then_refuse(batched):
+    """The cache filled to its last slot (capacity = prompt + steps exactly), against the
+    oracle up to that slot; one more step is refused on the host (MK_ERR_CAPACITY) and
+    the position stays at the capacity."""
+    from persistent_megakernel_loop_amd.binding import Decoder, MkError, weights_to_device
+
+    MK_ERR_CAPACITY = -4
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-full", n_layers=2, prompt_len=20, steps=12)
+    assert shape.capacity == 32
+    print(f"[case] {shape.name}: cache filled to capacity {shape.capacity} ({'batched' if batched else 'per-position'} "
+          "prefill), then one step more", flush=True)
+    weights = wl.make_weights(shape)
+    inp = make_inputs(shape)
+    dec = Decoder(shape, weights_to_device(weights))
+    gpu = run_gpu(shape, None, inp, dec=dec, batched=batched)
+    print(f"[case] {shape.name}: {compare(gpu, run_oracle(shape, weights, inp, gpu))}", flush=True)
+    assert dec.position == shape.capacity
+    with pytest.raises(MkError) as e:
+        dec.decode(1)
+    assert e.value.code == MK_ERR_CAPACITY and dec.position == shape.capacity
+    dec.close()
