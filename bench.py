@@ -378,18 +378,20 @@ def main():
         dec.check()
         return round(float(np.median(trials)), 3)
 
+    # the batched prefill serves the bf16 bodies; a float32 body's prompt runs position by position
+    batched_ok = shape.weight_dtype == "bf16"
     ttfc, ttfc_pp, pf_ms = {}, {}, {}
     if P and args.ttfc_trials > 0:
-        ttfc = ttfc_run(True)
+        ttfc = ttfc_run(batched_ok)
         ttfc_pp = ttfc_run(False)
-        pf_ms = {"batched": prefill_ms(True), "per_position": prefill_ms(False)}
+        pf_ms = {"batched": prefill_ms(True) if batched_ok else None, "per_position": prefill_ms(False)}
 
     # launch-per-phase ablation: the same decode steps, each as one launch per phase (the
     # batched prefill's kernels at one position: input, 9 per layer, LM head, argmax),
     # after the same prompt; greedy workloads feed each call's id to the next call
     ablation = {}
     n_abl = min(args.ablation_steps, K)
-    if P and n_abl > 0:
+    if P and n_abl > 0 and batched_ok:
         prepare()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
