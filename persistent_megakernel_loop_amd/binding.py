@@ -236,6 +236,8 @@ class Decoder:
         `chunk` (the last may be shorter) while the kernel runs, read from the pinned
         mirror as the progress word advances.  Raises MkError if the launch ends early
         with a device error."""
+        if chunk < 1:
+            raise ValueError("chunk must be at least 1")
         self.decode(n_steps, ids, rows, pos3, out=out)
         done = 0
         while done < n_steps:

@@ -210,3 +210,10 @@ def test_selftest_and_embed_sum_argument_checks(lib):
         assert call(**kw) == -1, kw
     assert call(n=0) == 0  # nothing to do, nothing launched
     assert call(n=0, cb=None, tx=None, ids=None, rows=None) == 0
+
+
+def test_stream_rejects_empty_chunks():
+    """Decoder.stream checks its chunk size before it enqueues anything."""
+    dec = object.__new__(B.Decoder)
+    with pytest.raises(ValueError):
+        next(dec.stream(4, chunk=0))
