@@ -115,3 +115,29 @@ def test_full_talker_long_context():
 def test_full_talker_1p7b():
     """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions: one launch of 12 steps."""
     _case(wl.TALKER_1P7B, n_steps=12)
+
+
+def _sweep_cases():
+    rng = np.random.default_rng(20261202)
+    cases = []
+    for i in range(6):
+        p = int(rng.integers(1, 101))
+        kv = int(rng.choice([0, int(rng.integers(1, 401))]))
+        n = int(rng.integers(1, 17))
+        cases.append((f"sweep{i}-p{p}-kv{kv}-n{n}", p, kv, n, bool(i % 2)))
+    return cases
+
+
+@pytest.mark.parametrize("name,prompt_len,kv_prefill,n_steps,batched", _sweep_cases(), ids=lambda c: str(c))
+def test_seeded_shape_sweep(name, prompt_len, kv_prefill, n_steps, batched):
+    """Seeded prompt lengths (ragged position tiles, several prefill chunks), pre-filled
+    caches and step counts on the 2-layer talker, both prefill paths, against the oracle."""
+    from persistent_megakernel_loop_amd.binding import weights_to_device
+
+    shape = wl.TALKER_0P6B.replace(name=name, n_layers=2, prompt_len=prompt_len, kv_prefill=kv_prefill,
+                                   steps=n_steps)
+    print(f"[case] {name} ({'batched' if batched else 'per-position'} prefill)", flush=True)
+    weights = wl.make_weights(shape)
+    inp = make_inputs(shape)
+    gpu = run_gpu(shape, weights_to_device(weights), inp, batched=batched)
+    print(f"[case] {name}: {compare(gpu, run_oracle(shape, weights, inp, gpu))}", flush=True)
