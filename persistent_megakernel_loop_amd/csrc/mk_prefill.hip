@@ -268,11 +268,14 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
 }
 
 // ------------------------------------------------------------------ attention
-// One workgroup per (KV group g, position n) over cache positions 0..p: wave w takes
-// the 64-key blocks w, w+4, ...; lane j of a block scores key j against the group's
-// QPG query heads, the block's softmax weights go through LDS, and the values are
-// read as whole rows (lane i holds dims 2i, 2i+1).  The four waves' running maxima,
-// sums and outputs merge in LDS; the result goes out split for the O product.
+// One workgroup of kPfAttnWaves waves per (KV group g, position n) over cache positions
+// 0..p: wave w takes the 64-key blocks w, w + kPfAttnWaves, ...; lane j of a block
+// scores key j against the group's QPG query heads, the block's softmax weights go
+// through LDS, and the values are read as whole rows (lane i holds dims 2i, 2i+1).
+// The waves' running maxima, sums and outputs merge in LDS; the result goes out split
+// for the O product.  Behind a long cache each wave's blocks form a chain of dependent
+// loads, so more waves per workgroup shorten it.
+
 // Eight bf16 cache elements widened to float32.
 __device__ __forceinline__ void cvt_row8(const uint4 r, float v[8]) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -283,8 +286,10 @@ __device__ __forceinline__ void cvt_row8(const uint4 r, float v[8]) {
   }
 }
 
-__global__ __launch_bounds__(256) void pf_attn_kernel(PfArgs A, int l) {
-  constexpr int D = 128, QPG = 2, NW = 4;
+constexpr int kPfAttnWaves = 8;  // two per SIMD: each wave may use 256 VGPRs
+
+__global__ __launch_bounds__(64 * kPfAttnWaves) void pf_attn_kernel(PfArgs A, int l) {
+  constexpr int D = 128, QPG = 2, NW = kPfAttnWaves;
   __shared__ float qs[QPG][D];
   __shared__ float pw[NW][QPG][64];
   __shared__ float mw[NW][QPG], lw[NW][QPG];
@@ -654,7 +659,7 @@ int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayo
                     st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_qkv_kernel, dim3(NKV, A.m), b256, 0, st, A, l, G, ks);
-    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), b256, 0, st, A, l);
+    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), dim3(64 * kPfAttnWaves), 0, st, A, l);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G, ks, -1);
