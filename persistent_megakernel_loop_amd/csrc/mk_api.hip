@@ -64,6 +64,7 @@ struct mk_handle {
   uint8_t* pf_buf = nullptr;
   float *pf_x = nullptr, *pf_part = nullptr, *pf_q = nullptr, *pf_ss = nullptr, *pf_blk_val = nullptr;
   int32_t* pf_blk_idx = nullptr;
+  float* pf_att = nullptr;
   uint16_t* pf_xs = nullptr;
 };
 
@@ -426,8 +427,9 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   if (!h->pf_buf) {
     const size_t bx = align_up(ch * H * 4, 256), bxs = align_up(2 * K * ch * 2, 256),
                  bq = align_up((size_t)ch * c->n_q_heads * c->head_dim * 4, 256),
-                 bs = align_up((size_t)ch * (H / 512) * 4, 256), bl = align_up(n_blk * 4, 256), bp = part * 4;
-    if (hipMalloc((void**)&h->pf_buf, bx + bxs + bq + bs + 2 * bl + bp) != hipSuccess) {
+                 bs = align_up((size_t)ch * (H / 512) * 4, 256), bl = align_up(n_blk * 4, 256),
+                 ba = align_up((size_t)c->n_kv_heads * mk::kFlashRanges * 2 * ch * (c->head_dim + 2) * 4, 256), bp = part * 4;
+    if (hipMalloc((void**)&h->pf_buf, bx + bxs + bq + bs + 2 * bl + ba + bp) != hipSuccess) {
       h->pf_buf = nullptr;
       return MK_ERR_OOM;
     }
@@ -438,7 +440,8 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
     h->pf_ss = (float*)(p += bq);
     h->pf_blk_val = (float*)(p += bs);
     h->pf_blk_idx = (int32_t*)(p += bl);
-    h->pf_part = (float*)(p += bl);
+    h->pf_att = (float*)(p += bl);
+    h->pf_part = (float*)(p += ba);
   }
   mk::PfArgs A{};
   A.H = c->hidden; A.D = c->head_dim; A.NQ = c->n_q_heads; A.NKV = c->n_kv_heads; A.I = c->intermediate;
@@ -454,7 +457,7 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   A.kcache = (uint16_t*)h->kcache;  // bf16: mk_create ties the cache dtype to the weight dtype
   A.vcache = (uint16_t*)h->vcache;
   A.err = h->ctl;
-  A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q; A.ss = h->pf_ss;
+  A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q; A.ss = h->pf_ss; A.att = h->pf_att;
   for (int32_t t0 = 0; t0 < n; t0 += ch) {
     A.m = std::min(ch, n - t0);
     A.npp = (A.m + 15) / 16 * 16;

@@ -10,6 +10,7 @@ namespace mk {
 // Batched prompt prefill (all prompt positions but the last, in chunks of up to
 // kPrefillChunk positions): arguments of one chunk.
 constexpr int kPrefillChunk = 64;
+constexpr int kFlashRanges = 64;  // key ranges of the prefill attention, at most
 struct PfArgs {
   int32_t H, D, NQ, NKV, I, L, vocab, max_seq, rope_positions;
   int32_t n_sections, sec_end0, sec_end1;
@@ -32,6 +33,7 @@ struct PfArgs {
   uint16_t* xs;              // [2][K/8][npp][8] split activations, K up to max(H, NQ*D, I)
   float* part;               // partial products, prefill_part_floats() floats
   float* q;                  // [npp][NQ][D] rotated, scaled queries
+  float* att;                // [NKV][kFlashRanges][2 npp rows][D + 2] attention partials (max, sum, output)
   float* ss;                 // [npp][H/512] sums of squares of the residual row, per 512 columns
 };
 // The prompt's first id: the LM head over the last prompt position's final-norm row,

@@ -405,6 +405,210 @@ __global__ __launch_bounds__(64 * kPfAttnWaves) void pf_attn_kernel(PfArgs A, in
   }
 }
 
+// ------------------------------------------------------------------ attention (flash)
+// One workgroup of 4 waves per (KV group g, key range s) takes every query row of the
+// chunk (row 2n + h: position n, head h of the group) against keys [s*SK, s*SK + SK)
+// clipped to the chunk's last position, 32 keys at a time:
+//   S = Q K^T on the matrix cores (16 rows x 16 keys per MFMA tile, the queries split
+//   into bf16 high and low parts, the keys exact in bf16); causal mask (row n sees keys
+//   up to pos0 + n); a running maximum and sum per row across the range (a row's 16
+//   keys of a tile sit in 16 lanes, reduced with xor shuffles);
+//   P = exp(S - max) through LDS as bf16 high/low parts, and the value tile transposed
+//   into LDS, so that O += P V is on the matrix cores too.
+// Wave w takes row tiles w, w + 4, ... (16 rows each).  Each range leaves, per row, its
+// maximum, sum and unnormalised output; pf_attn_combine_kernel merges the ranges in
+// order.  Rows with no visible key in a range leave maximum -inf and sum 0.
+constexpr int kFlashKeys = 128;  // keys per range, widened so that there are at most kFlashRanges
+// Contexts up to this many keys take pf_attn_kernel instead (256 workgroups and no merge
+// launch; measured faster up to about 1000-2000 keys, the key ranges faster beyond).
+constexpr int kFlashMinKeys = 2048;
+
+__device__ __forceinline__ bf16x8 bf16x8_of(const uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+template <int NT>
+__global__ __launch_bounds__(256) void pf_flash_kernel(PfArgs A, int l, int sk) {
+  constexpr int D = 128, QPG = 2, NPP = 16 * NT, ROWS = QPG * NPP, RT = ROWS / 16;
+  __shared__ __align__(16) uint16_t vt[D][32 + 8];  // value tile transposed: [dim][key] (+8: bank spread)
+  __shared__ __align__(16) uint16_t ph[4][16][32 + 8], pl[4][16][32 + 8];  // per wave: P high/low parts
+  const int g = blockIdx.x, s = blockIdx.y, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, i16 = lane & 15;
+  const int kend = A.pos0 + A.m;                 // keys [0, kend) exist
+  const int k0 = s * sk, k1 = min(kend, k0 + sk);
+  const size_t cbase = ((size_t)l * A.NKV + g) * A.max_seq * D;
+  float* out = A.att + ((size_t)(g * kFlashRanges + s) * ROWS) * (D + 2);
+  // this wave's row tiles (at most 2 for 64 positions)
+  constexpr int MT = (RT + 3) / 4;
+  bf16x8 qh[MT][4], ql[MT][4];
+  f4 o[MT][8];
+  float m[MT][4], ls[MT][4];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int rt = wv + 4 * t;
+    const int row = rt * 16 + i16, n = row >> 1, h = row & 1;
+    const bool live = rt < RT && n < A.m;
+    const float* qrow = A.q + ((size_t)n * A.NQ + g * QPG + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      float v[8];
+      if (live) load8(qrow + kk * 32 + 8 * q4, v);
+      else for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = to_bf16(v[2 * e]), h1 = to_bf16(v[2 * e + 1]);
+        hi[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[e] = (uint32_t)to_bf16(v[2 * e] - from_bf16(h0)) | ((uint32_t)to_bf16(v[2 * e + 1] - from_bf16(h1)) << 16);
+      }
+      qh[t][kk] = bf16x8_of(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      ql[t][kk] = bf16x8_of(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[t][d] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { m[t][e] = -INFINITY; ls[t][e] = 0.f; }
+  }
+  for (int kt = k0; kt < k1; kt += 32) {
+    // the value tile, transposed into LDS by the whole workgroup (rows past the range
+    // re-read its last key: their weights are 0)
+    __syncthreads();
+    {
+      const int key = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kk = key + 16 * half;
+        const uint4 u = *reinterpret_cast<const uint4*>(A.vcache + cbase + (size_t)min(kt + kk, k1 - 1) * D + d0);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vt[d0 + 2 * e][kk] = (uint16_t)(w[e] & 0xffffu);
+          vt[d0 + 2 * e + 1][kk] = (uint16_t)(w[e] >> 16);
+        }
+      }
+    }
+    __syncthreads();
+    // key fragments: lane (i16, q4) holds key kt + 16c + i16, dims 32kk + 8q4 .. + 7
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int key = min(kt + 16 * c + i16, k1 - 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[c][kk] = bf16x8_of(*reinterpret_cast<const uint4*>(A.kcache + cbase + (size_t)key * D + kk * 32 + 8 * q4));
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int rt = wv + 4 * t;
+      if (rt >= RT) break;
+      f4 sc[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        sc[c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          sc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[t][kk], kf[c][kk], sc[c], 0, 0, 0);
+          sc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[t][kk], kf[c][kk], sc[c], 0, 0, 0);
+        }
+      }
+      // lane holds rows 4q4 + e of the tile, keys kt + 16c + i16
+      float p[2][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = (rt * 16 + 4 * q4 + e) >> 1;
+        const int kmax = A.pos0 + n;  // causal: keys up to the row's own position
+        float sv[2], mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int key = kt + 16 * c + i16;
+          sv[c] = (key < k1 && key <= kmax) ? sc[c][e] : -INFINITY;
+          mx = fmaxf(mx, sv[c]);
+        }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) mx = fmaxf(mx, __shfl_xor(mx, x, 64));
+        const float mn = fmaxf(m[t][e], mx);
+        const bool none = mn == -INFINITY;  // no visible key yet: nothing to add
+        const float corr = none ? 1.f : __expf(m[t][e] - mn);
+        float sum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          p[c][e] = (none || sv[c] == -INFINITY) ? 0.f : __expf(sv[c] - mn);
+          sum += p[c][e];
+        }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) sum += __shfl_xor(sum, x, 64);
+        ls[t][e] = ls[t][e] * corr + sum;
+        m[t][e] = mn;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[t][d][e] *= corr;
+      }
+      // P into LDS (this wave's area), high and low parts, [row][key]
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t hb = to_bf16(p[c][e]);
+          ph[wv][4 * q4 + e][16 * c + i16] = hb;
+          pl[wv][4 * q4 + e][16 * c + i16] = to_bf16(p[c][e] - from_bf16(hb));
+        }
+      __builtin_amdgcn_wave_barrier();
+      // A fragments of P: lane (i16, q4) holds row i16, keys 8q4 .. 8q4 + 7
+      const bf16x8 pa = bf16x8_of(*reinterpret_cast<const uint4*>(&ph[wv][i16][8 * q4]));
+      const bf16x8 pb = bf16x8_of(*reinterpret_cast<const uint4*>(&pl[wv][i16][8 * q4]));
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        // B fragment of V: lane (i16, q4) holds dim 16d + i16, keys 8q4 .. 8q4 + 7
+        const bf16x8 vb = bf16x8_of(*reinterpret_cast<const uint4*>(&vt[16 * d + i16][8 * q4]));
+        o[t][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t][d], 0, 0, 0);
+        o[t][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pb, vb, o[t][d], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // this range's partials: per row its maximum, sum and unnormalised output
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int rt = wv + 4 * t;
+    if (rt >= RT) break;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float* r = out + (size_t)(rt * 16 + 4 * q4 + e) * (D + 2);
+      if (i16 == 0) { r[0] = m[t][e]; r[1] = ls[t][e]; }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) r[2 + 16 * d + i16] = o[t][d][e];
+    }
+  }
+}
+
+// Merge of the key ranges for (KV group g, position n): per head, the ranges' outputs
+// weighted by exp(max_s - max) over the total sum, in range order; split for the O
+// product (padding positions: zeros).
+__global__ __launch_bounds__(256) void pf_attn_combine_kernel(PfArgs A, int n_ranges) {
+  constexpr int D = 128, QPG = 2;
+  const int g = blockIdx.x, n = blockIdx.y, h = threadIdx.x >> 7, d = threadIdx.x & 127;
+  const int K = A.NQ * D, ROWS = QPG * A.npp;
+  const int e = (g * QPG + h) * D + d;
+  const size_t off = ((size_t)(e / 8) * A.npp + n) * 8 + e % 8;
+  if (n >= A.m) {
+    A.xs[off] = 0;
+    A.xs[(size_t)K * A.npp + off] = 0;
+    return;
+  }
+  const int row = 2 * n + h;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_ranges; ++s)
+    mx = fmaxf(mx, A.att[((size_t)(g * kFlashRanges + s) * ROWS + row) * (D + 2)]);
+  float sum = 0.f, acc = 0.f;
+  for (int s = 0; s < n_ranges; ++s) {
+    const float* r = A.att + ((size_t)(g * kFlashRanges + s) * ROWS + row) * (D + 2);
+    const float f = r[0] == -INFINITY ? 0.f : __expf(r[0] - mx);
+    sum = fmaf(f, r[1], sum);
+    acc = fmaf(f, r[2 + d], acc);
+  }
+  const float v = acc / sum;
+  const uint16_t hb = to_bf16(v);
+  A.xs[off] = hb;
+  A.xs[(size_t)K * A.npp + off] = to_bf16(v - from_bf16(hb));
+}
+
 // ------------------------------------------------------------------ residual + norm
 // grid (npp, H/512), 64 threads, 8 columns per thread: x[n] += the sum of the ks
 // partials (in order); the layer output is recorded when slot >= 0; then gains * x
@@ -659,7 +863,22 @@ int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayo
                     st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_qkv_kernel, dim3(NKV, A.m), b256, 0, st, A, l, G, ks);
-    hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), dim3(64 * kPfAttnWaves), 0, st, A, l);
+    if (A.pos0 + A.m <= kFlashMinKeys) {  // a short context: one workgroup per (group, position)
+      hipLaunchKernelGGL(pf_attn_kernel, dim3(NKV, A.npp), dim3(64 * kPfAttnWaves), 0, st, A, l);
+    } else {  // causal attention: key ranges on the matrix cores, then their merge
+      const int kend = A.pos0 + A.m;
+      int sk = kFlashKeys;
+      while ((kend + sk - 1) / sk > kFlashRanges) sk += 32;
+      const int nr = (kend + sk - 1) / sk;
+      const dim3 fg(NKV, nr);
+      switch (A.npp / 16) {
+        case 1: hipLaunchKernelGGL(pf_flash_kernel<1>, fg, b256, 0, st, A, l, sk); break;
+        case 2: hipLaunchKernelGGL(pf_flash_kernel<2>, fg, b256, 0, st, A, l, sk); break;
+        case 3: hipLaunchKernelGGL(pf_flash_kernel<3>, fg, b256, 0, st, A, l, sk); break;
+        default: hipLaunchKernelGGL(pf_flash_kernel<4>, fg, b256, 0, st, A, l, sk); break;
+      }
+      hipLaunchKernelGGL(pf_attn_combine_kernel, dim3(NKV, A.npp), b256, 0, st, A, nr);
+    }
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G, ks, -1);

@@ -81,6 +81,13 @@ def test_talker_two_layers_several_chunks_behind_cache():
     _case(shape)
 
 
+def test_talker_two_layers_behind_long_cache():
+    """A prompt behind 2100 cached positions: the attention takes the key-range path
+    (MFMA tiles per range of keys, then the ranges' merge), chunks of 64 and 1."""
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-pb-kv2100", n_layers=2, kv_prefill=2100, prompt_len=65, steps=3)
+    _case(shape)
+
+
 def test_q17_talker_two_layers():
     shape = wl.TALKER_1P7B.replace(name="talker-1.7b-2l-pb", n_layers=2, kv_prefill=40, prompt_len=24, steps=6)
     _case(shape)
