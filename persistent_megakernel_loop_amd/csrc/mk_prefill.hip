@@ -12,7 +12,8 @@
 // stream:
 //   input rows and RMSNorm (layer 0) or residual + RMSNorm (later layers)
 //   QKV product -> per-head q/k RMSNorm, rotary embedding, cache write
-//   causal attention, one workgroup per (position, KV group)
+//   causal attention: one workgroup per (position, KV group) for short contexts, key
+//   ranges on the matrix cores and their merge behind a long cache
 //   O product -> residual + post-attention RMSNorm
 //   gate/up product -> SwiGLU
 //   down product -> residual + next input RMSNorm
