@@ -1,8 +1,8 @@
 // Batched prompt prefill.
 //
 // The persistent decode kernel runs one position per pass over the weights, so a
-// prompt of P positions costs P passes.  Every prompt position but the last is
-// known up front, which makes the prompt a batch: each layer's projections become
+// prompt of P positions costs P passes.  Every prompt position is known up front,
+// which makes the prompt a batch: each layer's projections become
 // matrix products with P columns, and the weights stream once per chunk of up to 64
 // positions instead of once per position.  The causal mask keeps the result the same
 // as the position-by-position run (up to rounding order): position p attends to
@@ -21,8 +21,9 @@
 // (no second copy of the weights) and run on the matrix cores: 16x16x32 bf16 MFMA
 // with the activations split into a bf16 high and low part (two products per tile),
 // so the activations keep about 16 significant bits, as the fp32 dot products of the
-// decode path do up to rounding.  The last prompt position still runs through the
-// persistent kernel, which reads the filled cache and produces the first id.
+// decode path do up to rounding.  After the last chunk, the LM head over the last
+// position and a greedy argmax produce the first id and publish it as the persistent
+// kernel would (device output, feedback id, pinned mirror, progress word).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
