@@ -7,8 +7,8 @@
 
 namespace mk {
 
-// Batched prompt prefill (all prompt positions but the last, in chunks of up to
-// kPrefillChunk positions): arguments of one chunk.
+// Batched prompt prefill (every prompt position, in chunks of up to kPrefillChunk
+// positions): arguments of one chunk.
 constexpr int kPrefillChunk = 64;
 constexpr int kFlashRanges = 64;  // key ranges of the prefill attention, at most
 struct PfArgs {
