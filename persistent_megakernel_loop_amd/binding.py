@@ -177,8 +177,9 @@ class Decoder:
         return self._h
 
     def prefill(self, ids, rows=None, pos3=None, out=None, batched: bool = False):
-        """Run the prompt; batched=True takes mk_prefill_batched (all positions but the
-        last as a batch, the last through the persistent kernel)."""
+        """Run the prompt; batched=True takes mk_prefill_batched (the whole prompt as a
+        batch through per-layer kernels, then the first id's LM head) instead of the
+        persistent kernel position by position."""
         import torch
         n = ids.numel()
         if out is None:

@@ -75,8 +75,8 @@ def test_text_two_layers_ids_ragged_vocab():
 
 
 def test_talker_two_layers_several_chunks_behind_cache():
-    """150 prompt positions behind 70 cached ones: chunks of 64, 64 and 21 (ragged last
-    tile), then the last position through the persistent kernel."""
+    """150 prompt positions behind 70 cached ones: chunks of 64, 64 and 22 (ragged last
+    tile), then the first id's LM head over the last position."""
     shape = wl.TALKER_0P6B.replace(name="talker-2l-pb150", n_layers=2, kv_prefill=70, prompt_len=150, steps=6)
     _case(shape)
 
