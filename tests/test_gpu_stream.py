@@ -40,6 +40,12 @@ def test_stream_chunks_arrive_while_running():
     assert all(len(c) >= 8 for c in chunks[:-1])
     # 64 steps take about 29 ms; the first 8 ids are out after about an eighth of that
     assert arrive[0] < 0.5 * arrive[-1]
+    # the pinned mirror holds exactly the published ids: the whole launch reads back,
+    # one more is refused
+    from persistent_megakernel_loop_amd.binding import MkError
+    assert np.array_equal(dec.read_ids(0, inp.n_steps), got)
+    with pytest.raises(MkError):
+        dec.read_ids(0, inp.n_steps + 1)
     # the same inputs again through a plain decode give the same ids
     dec.reset()
     dec.prefill(*prompt, batched=True)
