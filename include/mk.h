@@ -89,8 +89,9 @@ typedef struct mk_weights {
 
 typedef struct mk_handle mk_handle;
 
-/* Validate cfg, allocate the arena, KV cache, exchange buffers and the pinned
- * progress word, pack the weights, build the rotary cos/sin table (computed in
+/* Validate cfg, allocate the arena, KV cache, exchange buffers, the pinned
+ * progress word and the pinned id mirror (for calls of up to 4096 ids; a larger call
+ * grows it, with a stream synchronization), pack the weights, build the rotary cos/sin table (computed in
  * double, stored as float) and check that one workgroup per CU fits co-resident.
  * stream: a hipStream_t (NULL = the null stream).  Synchronous.
  * Returns MK_OK and *out, or a negative code with *out = NULL. */

@@ -370,6 +370,9 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   if ((size_t)(p - h->xbuf) > h->xbuf_words) { free_handle(h); return MK_ERR_ARG; }
   if (hipHostMalloc((void**)&h->progress, 64, hipHostMallocCoherent) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
   *(volatile unsigned long long*)h->progress = 0;
+  // the pinned id mirror for calls of up to 4096 ids, so that a first call does not pay
+  // for the allocation (larger calls grow it)
+  if (ensure_pinned(h, std::min(cfg->max_seq, 4096))) { free_handle(h); return MK_ERR_OOM; }
 
   hipStream_t s = h->stream;
   if (hipMemsetAsync(h->xbuf, 0, h->xbuf_words * 8, s) != hipSuccess || hipMemsetAsync(h->ctl, 0, 256, s) != hipSuccess) {
