@@ -756,9 +756,16 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
 }
 
 // Attention at position p covers positions 0..p, cut into n_chunks contiguous chunks
-// of chunk_len positions; chunk r goes to rank r of the group's XCD.
+// of chunk_len positions; chunk r goes to rank r of the group's XCD.  At most 28 chunks
+// in the LDS-tile bodies and 24 in the H = 2048 body (measured: fewer, longer chunks
+// shorten the combine's gather more than they lengthen the attention at long contexts).
 constexpr int kMinChunk = 56;  // one batch of 8 positions per worker wave
-__device__ __forceinline__ int n_chunks(int p) { return min(kPerXcd, max(1, (p + 1 + kMinChunk - 1) / kMinChunk)); }
+template <class B>
+constexpr int kMaxChunks = B::H <= 1024 ? 28 : 24;
+template <class B>
+__device__ __forceinline__ int n_chunks(int p) {
+  return min(kMaxChunks<B>, max(1, (p + 1 + kMinChunk - 1) / kMinChunk));
+}
 
 // RMSNorm of x with gains g into out (fp32), lane L working on 8-element chunks L,
 // L + 64, ... (16-byte LDS accesses; the order of the sum of squares is the one the bf16
@@ -895,13 +902,35 @@ __device__ __forceinline__ void combine_part(Lds<B>& S, int nc, int pw, int lane
   const float Ls = wave_sum(S.part[cl][h][1] * f);
   S.chw[pw][lane] = f;  // this wave's own LDS writes are seen by its later reads
   if (lane < CW) {
+    // the weights past nc are zero and the chunk index is clamped, so the loop may run
+    // past nc: in the LDS-tile bodies it is unrolled to the next of 8, 16 or 32 chunks
+    // (all LDS reads independent); the H = 2048 body keeps a loop (its registers are full)
+    auto sum_chunks = [&](auto n_max) {
+      constexpr int NM = decltype(n_max)::value;
+      float a = 0.f;
+#pragma unroll
+      for (int c0 = 0; c0 < NM; c0 += 4) {
+        const f4 w = *reinterpret_cast<const f4*>(&S.chw[pw][c0]);  // zero past nc
+        a = fmaf(S.part[min(c0 + 0, nc - 1)][h][2 + d], w.x, a);
+        a = fmaf(S.part[min(c0 + 1, nc - 1)][h][2 + d], w.y, a);
+        a = fmaf(S.part[min(c0 + 2, nc - 1)][h][2 + d], w.z, a);
+        a = fmaf(S.part[min(c0 + 3, nc - 1)][h][2 + d], w.w, a);
+      }
+      return a;
+    };
     float a = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += 4) {
-      const f4 w = *reinterpret_cast<const f4*>(&S.chw[pw][c0]);  // zero past nc
-      a = fmaf(S.part[min(c0 + 0, nc - 1)][h][2 + d], w.x, a);
-      a = fmaf(S.part[min(c0 + 1, nc - 1)][h][2 + d], w.y, a);
-      a = fmaf(S.part[min(c0 + 2, nc - 1)][h][2 + d], w.z, a);
-      a = fmaf(S.part[min(c0 + 3, nc - 1)][h][2 + d], w.w, a);
+    if constexpr (B::H <= 1024) {
+      a = nc <= 8    ? sum_chunks(std::integral_constant<int, 8>{})
+          : nc <= 16 ? sum_chunks(std::integral_constant<int, 16>{})
+                     : sum_chunks(std::integral_constant<int, kPerXcd>{});
+    } else {
+      for (int c0 = 0; c0 < nc; c0 += 4) {
+        const f4 w = *reinterpret_cast<const f4*>(&S.chw[pw][c0]);  // zero past nc
+        a = fmaf(S.part[min(c0 + 0, nc - 1)][h][2 + d], w.x, a);
+        a = fmaf(S.part[min(c0 + 1, nc - 1)][h][2 + d], w.y, a);
+        a = fmaf(S.part[min(c0 + 2, nc - 1)][h][2 + d], w.z, a);
+        a = fmaf(S.part[min(c0 + 3, nc - 1)][h][2 + d], w.w, a);
+      }
     }
     S.ov[col] = a * __builtin_amdgcn_rcpf(Ls);
   }
@@ -1332,7 +1361,7 @@ __device__ __forceinline__ void worker_loop_regs(const Params& P, Lds<B>& S, int
     auto layer = [&](int l, auto last) -> bool {
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
-      const int nc = n_chunks(p);
+      const int nc = n_chunks<B>(p);
       const int csz = (p + 1 + nc - 1) / nc;
       const bool attn = grp && r < nc;
       const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
@@ -1552,7 +1581,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const bool lm_now = lm && l + 1 == L;
       // this rank's chunk of cache positions: its first batch is loaded now
-      const int nc = n_chunks(p);
+      const int nc = n_chunks<B>(p);
       const int csz = (p + 1 + nc - 1) / nc;
       const bool attn = grp && r < nc;
       const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
@@ -1989,7 +2018,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       // ------------------------------------------------------------ attention combine
       if (!sync()) return;
       {
-        const int nc = n_chunks(p);
+        const int nc = n_chunks<B>(p);
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
         // this rank's chunk partial: the worker waves' partials merged in a fixed order
         float cM[B::QPG], cL[B::QPG], ca[B::QPG][B::DPL];
