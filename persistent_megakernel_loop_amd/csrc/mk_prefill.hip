@@ -636,40 +636,52 @@ __global__ __launch_bounds__(64) void pf_resid_kernel(PfArgs A, const float* g, 
 }
 
 // ------------------------------------------------------------------ SwiGLU
-// grid (npp, I/512), 64 threads, 8 intermediate columns per thread.  Gate/up rows come
-// in the arena's order: slice x of I/8 columns, 32 runs of HALF gate rows then HALF up
-// rows; column c of the intermediate is gate row x*2IX + r*2HALF + i with x = c / IX,
-// r = (c % IX) / HALF, i = c % HALF.  Both sums are scaled by the row's 1/rms (the
-// post-attention norm).  The output is split in natural column order, which is the
-// down tiles' column order.
+// grid (npp, I/256), 64 threads; thread t of block (n, b) takes the four intermediate
+// columns 4(64b + t) .. +3.  Gate/up rows come in the arena's order: slice x of I/8
+// columns, 32 runs of HALF = I/256 gate rows then HALF up rows; column c of the
+// intermediate is gate row x*2IX + r*2HALF + i with x = c / IX, r = (c % IX) / HALF,
+// i = c % HALF, and its up row HALF further.  HALF is a multiple of 4 (the host checks
+// I % 1024), so a thread's four columns lie in one run and each partial is read as one
+// float4 per half.  Both sums are scaled by the row's 1/rms (the post-attention norm).
+// The output is split in natural column order, which is the down tiles' column order.
 __global__ __launch_bounds__(64) void pf_swiglu_kernel(PfArgs A, int ks) {
-  const int n = blockIdx.x, I = A.I, c = blockIdx.y * 64 + threadIdx.x;
-  if (n >= A.m) { zero_split8(A.xs, I, A.npp, n, c); return; }
+  const int n = blockIdx.x, I = A.I, k0 = 4 * (blockIdx.y * 64 + threadIdx.x);
+  // columns k0 .. k0+3 in the split layout: chunk k0/8, its half (k0 % 8) / 4
+  const size_t off = ((size_t)(k0 / 8) * A.npp + n) * 8 + k0 % 8;
+  uint2* hi = reinterpret_cast<uint2*>(A.xs + off);
+  uint2* lo = reinterpret_cast<uint2*>(A.xs + (size_t)I * A.npp + off);
+  if (n >= A.m) {
+    *hi = make_uint2(0, 0);
+    *lo = make_uint2(0, 0);
+    return;
+  }
   const int IX = I / kXcds, HALF = IX / kPerXcd, R = 2 * I;
   const float rs = row_rs(A, n);
-  int mg[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int ci = 8 * c + e;
-    mg[e] = (ci / IX) * 2 * IX + ((ci % IX) / HALF) * 2 * HALF + ci % HALF;
-  }
-  float gt[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, up[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+  const int mg = (k0 / IX) * 2 * IX + ((k0 % IX) / HALF) * 2 * HALF + k0 % HALF;
+  float gt[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < ks; ++s) {
-    const float* pp = A.part + ((size_t)s * A.npp + n) * R;
+    const float* pp = A.part + ((size_t)s * A.npp + n) * R + mg;
+    const float4 g4 = *reinterpret_cast<const float4*>(pp), u4 = *reinterpret_cast<const float4*>(pp + HALF);
+    gt[0] += g4.x; gt[1] += g4.y; gt[2] += g4.z; gt[3] += g4.w;
+    up[0] += u4.x; up[1] += u4.y; up[2] += u4.z; up[3] += u4.w;
+  }
+  uint32_t h[2], l[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gt[e] += pp[mg[e]];
-      up[e] += pp[mg[e] + HALF];
+  for (int e = 0; e < 2; ++e) {
+    float v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float gr = gt[2 * e + j] * rs;
+      v[j] = gr / (1.f + __expf(-gr)) * (up[2 * e + j] * rs);
     }
+    const uint16_t h0 = to_bf16(v[0]), h1 = to_bf16(v[1]);
+    const uint16_t l0 = to_bf16(v[0] - from_bf16(h0)), l1 = to_bf16(v[1] - from_bf16(h1));
+    h[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
   }
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float gr = gt[e] * rs;
-    v[e] = gr / (1.f + __expf(-gr)) * (up[e] * rs);
-  }
-  store_split8(A.xs, I, A.npp, n, c, v);
+  *hi = make_uint2(h[0], h[1]);
+  *lo = make_uint2(l[0], l[1]);
 }
 
 // ------------------------------------------------------------------ first id
@@ -852,10 +864,10 @@ size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I) {
 int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayout& lay, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int H = A.H, D = A.D, NQ = A.NQ, NKV = A.NKV, I = A.I, QPG = NQ / NKV;
-  if (D != 128 || QPG != 2 || H % 512 || I % 512 || A.npp % 16 || A.npp > kPrefillChunk || A.m <= 0 || A.m > A.npp)
+  if (D != 128 || QPG != 2 || H % 512 || I % 1024 || A.npp % 16 || A.npp > kPrefillChunk || A.m <= 0 || A.m > A.npp)
     return -1;
   const dim3 b256(256);
-  const dim3 b64(64), rows_h(A.npp, H / 512), rows_i(A.npp, I / 512);
+  const dim3 b64(64), rows_h(A.npp, H / 512), rows_i(A.npp, I / 256);
   hipLaunchKernelGGL(pf_input_kernel, rows_h, b64, 0, st, A);
   for (int l = 0; l < A.L; ++l) {
     const uint8_t* base = layers + (size_t)l * lay.stride;
