@@ -308,23 +308,37 @@ __global__ __launch_bounds__(64 * kPfAttnWaves) void pf_attn_kernel(PfArgs A, in
     return;
   }
   const int p = A.pos0 + n, nkeys = p + 1;
+  const size_t cbase = ((size_t)l * A.NKV + g) * A.max_seq * D;
+  // A block's key row (the whole row in flight at once, converted after) and its first 32
+  // value rows (2 dims per lane; rows past the block's last key read that key's row, with
+  // weight 0) are issued together; for the wave's first block, before q is read, so the
+  // three loads overlap.
+  uint4 kr[D / 8];
+  uint32_t vr[32];
+  auto load_block = [&](int kb) {
+    const int j = kb * 64 + lane;
+    const size_t krow = cbase + (size_t)(j < nkeys ? j : p) * D;
+#pragma unroll
+    for (int j8 = 0; j8 < D / 8; ++j8) kr[j8] = *reinterpret_cast<const uint4*>(A.kcache + krow + 8 * j8);
+    const int nb = min(64, nkeys - kb * 64);
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      vr[e] = *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)(kb * 64 + min(e, nb - 1)) * D + 2 * lane);
+  };
+  if (w * 64 < nkeys) load_block(w);
   for (int i = threadIdx.x; i < QPG * D; i += blockDim.x)
     qs[i / D][i % D] = A.q[((size_t)n * A.NQ + g * QPG) * D + i];
   __syncthreads();
-  const size_t cbase = ((size_t)l * A.NKV + g) * A.max_seq * D;
   float M[QPG], Ls[QPG], acc[QPG][2];
 #pragma unroll
   for (int h = 0; h < QPG; ++h) { M[h] = -INFINITY; Ls[h] = 0.f; acc[h][0] = acc[h][1] = 0.f; }
   for (int kb = w; kb * 64 < nkeys; kb += NW) {
+    if (kb != w) load_block(kb);
     const int j = kb * 64 + lane;
     const bool valid = j < nkeys;
-    const size_t krow = cbase + (size_t)(valid ? j : p) * D;
     float s[QPG];
 #pragma unroll
     for (int h = 0; h < QPG; ++h) s[h] = 0.f;
-    uint4 kr[D / 8];  // the whole key row in flight at once, converted after
-#pragma unroll
-    for (int j8 = 0; j8 < D / 8; ++j8) kr[j8] = *reinterpret_cast<const uint4*>(A.kcache + krow + 8 * j8);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j8 = 0; j8 < D / 8; ++j8) {
@@ -351,11 +365,20 @@ __global__ __launch_bounds__(64 * kPfAttnWaves) void pf_attn_kernel(PfArgs A, in
     // one wave complete in order)
     __builtin_amdgcn_wave_barrier();
     const int nb = min(64, nkeys - kb * 64);
-    for (int u0 = 0; u0 < nb; u0 += 32) {  // 32 value rows in flight at once
+    // value rows 0..31 of the block (loaded with its key row), then 32..63 if it has them
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+#pragma unroll
+      for (int h = 0; h < QPG; ++h) {
+        const float pu = e < nb ? pw[w][h][e] : 0.f;
+        acc[h][0] = fmaf(pu, __uint_as_float(vr[e] << 16), acc[h][0]);
+        acc[h][1] = fmaf(pu, __uint_as_float(vr[e] & 0xffff0000u), acc[h][1]);
+      }
+    if (nb > 32) {  // 32 value rows in flight at once
       float v0[32], v1[32];
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        const int u = min(u0 + e, nb - 1);  // past the block's last key: weight 0, row in range
+        const int u = min(32 + e, nb - 1);  // past the block's last key: weight 0, row in range
         const uint32_t vv = *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)(kb * 64 + u) * D + 2 * lane);
         v0[e] = __uint_as_float(vv << 16);
         v1[e] = __uint_as_float(vv & 0xffff0000u);
@@ -364,7 +387,7 @@ __global__ __launch_bounds__(64 * kPfAttnWaves) void pf_attn_kernel(PfArgs A, in
       for (int e = 0; e < 32; ++e)
 #pragma unroll
         for (int h = 0; h < QPG; ++h) {
-          const float pu = u0 + e < nb ? pw[w][h][u0 + e] : 0.f;
+          const float pu = 32 + e < nb ? pw[w][h][32 + e] : 0.f;
           acc[h][0] = fmaf(pu, v0[e], acc[h][0]);
           acc[h][1] = fmaf(pu, v1[e], acc[h][1]);
         }
