@@ -637,17 +637,32 @@ __global__ __launch_bounds__(256) void pf_attn_combine_kernel(PfArgs A, int n_ra
 // ------------------------------------------------------------------ residual + norm
 // grid (npp, H/512), 64 threads, 8 columns per thread: x[n] += the sum of the ks
 // partials (in order); the layer output is recorded when slot >= 0; then gains * x
-// split for the next product and the block's sum of squares.
-__global__ __launch_bounds__(64) void pf_resid_kernel(PfArgs A, const float* g, int ks, int slot) {
+// split for the next product and the block's sum of squares.  KS > 0 is the partial count
+// known at compile time: every partial's load is issued before the first add, so the
+// thread waits for one memory round trip instead of one per few partials; KS = 0 reads
+// the count from ks.
+template <int KS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 4))) void pf_resid_kernel(PfArgs A, const float* g,
+                                                                                                int ks, int slot) {
   const int n = blockIdx.x, H = A.H, c = blockIdx.y * 64 + threadIdx.x;
   if (n >= A.m) { zero_split8(A.xs, H, A.npp, n, c); return; }
   float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8];
-#pragma unroll 8
-  for (int s = 0; s < ks; ++s) {
-    float t[8];
-    load8(A.part + ((size_t)s * A.npp + n) * H + 8 * c, t);
+  if constexpr (KS > 0) {
+    float t[KS][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] += t[e];
+    for (int s = 0; s < KS; ++s) load8(A.part + ((size_t)s * A.npp + n) * H + 8 * c, t[s]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] += t[s][e];
+  } else {
+#pragma unroll 8
+    for (int s = 0; s < ks; ++s) {
+      float t[8];
+      load8(A.part + ((size_t)s * A.npp + n) * H + 8 * c, t);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] += t[e];
+    }
   }
   float* x = A.x + (size_t)n * H + 8 * c;
   load8(x, v);
@@ -884,6 +899,14 @@ size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I) {
   return best;
 }
 
+static void launch_resid(dim3 grid, hipStream_t st, const PfArgs& A, const float* g, int ks, int slot) {
+  switch (ks) {
+    case 8: hipLaunchKernelGGL(pf_resid_kernel<8>, grid, dim3(64), 0, st, A, g, ks, slot); break;
+    case 16: hipLaunchKernelGGL(pf_resid_kernel<16>, grid, dim3(64), 0, st, A, g, ks, slot); break;
+    default: hipLaunchKernelGGL(pf_resid_kernel<0>, grid, dim3(64), 0, st, A, g, ks, slot); break;
+  }
+}
+
 int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayout& lay, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   const int H = A.H, D = A.D, NQ = A.NQ, NKV = A.NKV, I = A.I, QPG = NQ / NKV;
@@ -918,13 +941,13 @@ int launch_prefill_chunk(const PfArgs& A, const uint8_t* layers, const LayerLayo
     }
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.o), H, QPG * D, NQ * D, A.npp, A.xs, A.part, st, &ks))
       return -1;
-    hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G, ks, -1);
+    launch_resid(rows_h, st, A, G, ks, -1);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.gu), 2 * I, H, H, A.npp, A.xs, A.part, st, &ks))
       return -1;
     hipLaunchKernelGGL(pf_swiglu_kernel, rows_i, b64, 0, st, A, ks);
     if (launch_gemm(reinterpret_cast<const uint16_t*>(base + lay.down), H, I / kXcds, I, A.npp, A.xs, A.part, st, &ks))
       return -1;
-    hipLaunchKernelGGL(pf_resid_kernel, rows_h, b64, 0, st, A, G + H + 2 * D, ks, l + 1);
+    launch_resid(rows_h, st, A, G + H + 2 * D, ks, l + 1);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
