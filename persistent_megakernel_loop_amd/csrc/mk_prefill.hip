@@ -155,8 +155,8 @@ __global__ __launch_bounds__(64) void pf_input_kernel(PfArgs A) {
 // the instruction.  The result tile has 4 consecutive rows per lane (rows 4q..4q+3 of
 // the tile, position lane%16).
 template <int NT, int S>
-__global__ __launch_bounds__(256) void pf_gemm_kernel(const uint16_t* __restrict__ w, int R, int KB, int K,
-                                                      const uint16_t* __restrict__ xs, float* __restrict__ part) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void pf_gemm_kernel(
+    const uint16_t* __restrict__ w, int R, int KB, int K, const uint16_t* __restrict__ xs, float* __restrict__ part) {
   constexpr int NPP = 16 * NT, KC = 64 * S;
   __shared__ f4 red[3][2][NT][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, WK = blockDim.x >> 6;
@@ -176,33 +176,42 @@ __global__ __launch_bounds__(256) void pf_gemm_kernel(const uint16_t* __restrict
       a[s][0][hf] = *reinterpret_cast<const bf16x8*>(w0 + s * 64 + hf * 8);
       a[s][1][hf] = *reinterpret_cast<const bf16x8*>(w1 + s * 64 + hf * 8);
     }
-  // every weight load of the wave is in flight before the first product waits on one
-  __builtin_amdgcn_sched_barrier(0);
   f4 acc[2][NT];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+  // The activations of SG column steps are loaded together (16 NT SG VGPRs, at most 128),
+  // the first group's behind the weights: every load of a group is in flight before the
+  // first product waits on one.
+  constexpr int SG = NT * S <= 8 ? S : (8 / NT > 0 ? 8 / NT : 1);
+  static_assert(S % SG == 0, "whole groups of column steps");
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    bf16x8 bh[NT][2], bl[NT][2];
+  for (int s0 = 0; s0 < S; s0 += SG) {
+    bf16x8 bh[SG][NT][2], bl[SG][NT][2];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int sg = 0; sg < SG; ++sg)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const size_t off = ((size_t)(s * 8 + hf) * NPP + nt * 16) * 8;
-        bh[nt][hf] = *reinterpret_cast<const bf16x8*>(xh + off);
-        bl[nt][hf] = *reinterpret_cast<const bf16x8*>(xl + off);
-      }
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bh[nt][hf], acc[rt][nt], 0, 0, 0);
-          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bl[nt][hf], acc[rt][nt], 0, 0, 0);
+        for (int hf = 0; hf < 2; ++hf) {
+          const size_t off = ((size_t)((s0 + sg) * 8 + hf) * NPP + nt * 16) * 8;
+          bh[sg][nt][hf] = *reinterpret_cast<const bf16x8*>(xh + off);
+          bl[sg][nt][hf] = *reinterpret_cast<const bf16x8*>(xl + off);
         }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int sg = 0; sg < SG; ++sg)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const int s = s0 + sg;
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bh[sg][nt][hf], acc[rt][nt], 0, 0, 0);
+            acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s][rt][hf], bl[sg][nt][hf], acc[rt][nt], 0, 0, 0);
+          }
   }
   if (wv > 0) {
 #pragma unroll
