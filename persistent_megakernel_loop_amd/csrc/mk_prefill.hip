@@ -243,6 +243,12 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
   const int p = A.pos0 + n;
   const int R = A.NKV * (QPG + 2) * D;
   const int row = g * (QPG + 2) * D + h * D + lane;
+  // the rotary pair's cos/sin first: their loads depend on the position stream's, and
+  // this way both are in flight with the partials'
+  const int sct = lane < A.sec_end0 ? 0 : (lane < A.sec_end1 ? 1 : 2);
+  int ps = A.pos3 ? A.pos3[n * 3 + sct] : p;
+  ps = (ps < 0 || ps >= A.rope_positions) ? 0 : ps;
+  const float c = A.rope_cos[(size_t)ps * (D / 2) + lane], sn = A.rope_sin[(size_t)ps * (D / 2) + lane];
   float a0 = 0.f, a1 = 0.f;
   for (int s = 0; s < ks; ++s) {
     const float* pp = A.part + ((size_t)s * A.npp + n) * R + row;
@@ -258,10 +264,6 @@ __global__ __launch_bounds__(256) void pf_qkv_kernel(PfArgs A, int l, const floa
     const float ss = wsum(fmaf(a1, a1, a0 * a0));
     const float rs = rsqrtf(ss / (float)D + A.eps);
     const float n0 = gn[lane] * (a0 * rs), n1 = gn[lane + 64] * (a1 * rs);
-    const int sct = lane < A.sec_end0 ? 0 : (lane < A.sec_end1 ? 1 : 2);
-    int ps = A.pos3 ? A.pos3[n * 3 + sct] : p;
-    ps = (ps < 0 || ps >= A.rope_positions) ? 0 : ps;
-    const float c = A.rope_cos[(size_t)ps * (D / 2) + lane], sn = A.rope_sin[(size_t)ps * (D / 2) + lane];
     const float o0 = n0 * c - n1 * sn, o1 = n1 * c + n0 * sn;
     if (h < QPG) {
       const float qscale = rsqrtf((float)D);
