@@ -89,7 +89,12 @@ typedef struct mk_weights {
 
 typedef struct mk_handle mk_handle;
 
-/* Validate cfg, allocate the arena, KV cache, exchange buffers, the pinned
+/* Build a decoder: the dev.to article "Porting a 1,200-line persistent CUDA megakernel to
+ * Qwen3-TTS", "Porting it to Qwen3-TTS-1.7B", fixes the model constants when the decoder is
+ * built (vocabulary, untied head, rotary sections), and the theaicatchup article, "So,
+ * What's the Catch with These Megakernels?", has the rotary frequency tables computed on
+ * the host; both are what this call does before any decode.
+ * Validate cfg, allocate the arena, KV cache, exchange buffers, the pinned
  * progress word and the pinned id mirror (for calls of up to 4096 ids; a larger call
  * grows it, with a stream synchronization), pack the weights, build the rotary cos/sin table (computed in
  * double, stored as float) and check that one workgroup per CU fits co-resident.
@@ -97,7 +102,9 @@ typedef struct mk_handle mk_handle;
  * Returns MK_OK and *out, or a negative code with *out = NULL. */
 int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** out);
 
-/* Run n prompt positions starting at the current position (0 after create/reset,
+/* The prompt before the first decode step (dev.to article, "Making it talk end-to-end":
+ * the first audio chunk waits for the prompt, so it is part of the time to first chunk).
+ * Run n prompt positions starting at the current position (0 after create/reset,
  * n_pos after mk_load_kv) position by position through the same persistent kernel;
  * the LM head runs only at the last one and its greedy id (ties: lowest index) is
  * written to d_out_first[0] (device int32) and kept as the feedback id.
@@ -121,8 +128,8 @@ int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const in
  * equal mk_prefill's up to rounding order, the debug hidden states too; the barrier
  * trace and phase timeline are not written for these positions.
  * Allocates its scratch (about 40 MB at hidden 2048) on the first call.
- * MK_ERR_UNSUPPORTED for float32 weights, hidden or intermediate sizes that are not
- * multiples of 512, hidden above 2048, or a head layout other than head_dim 128 with
+ * MK_ERR_UNSUPPORTED for float32 weights, a hidden size that is not a multiple of 512,
+ * an intermediate size that is not a multiple of 1024, hidden above 2048, or a head layout other than head_dim 128 with
  * two query heads per KV head (use mk_prefill there); other errors as mk_prefill.
  * Stream-ordered on the handle's stream; an id or position outside its table is
  * flagged in the device error word and read as 0, as in mk_prefill. */
@@ -145,12 +152,22 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
               const int32_t* d_pos3, int32_t* d_out_ids);
 
-/* Install n_pos already-rotated cache positions and set the position to n_pos.
- * d_kv: device [n_layers][2][n_kv][n_pos][head_dim] in cfg.kv_dtype (K then V). */
+/* A cache that already holds n_pos positions: the conversation history a later decode
+ * attends over (the dev.to article, "The idea: one kernel that never exits": attention at
+ * each step reads every cached position; the long-context workloads start from such a
+ * cache).  Install n_pos already-rotated cache positions and set the position to n_pos.
+ * d_kv: device [n_layers][2][n_kv][n_pos][head_dim] in cfg.kv_dtype (K then V), copied
+ * stream-ordered (the caller may free it after the stream reaches this point).
+ * MK_ERR_ARG for a NULL handle or pointer or n_pos < 0; MK_ERR_CAPACITY if n_pos > max_seq. */
 int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos);
 
-/* Rewind to position 0 and forget the feedback id (the cache is not cleared: it is
- * only read at positions that have been written since). */
+/* Start a new utterance on the same decoder (the dev.to article, "Making it talk
+ * end-to-end": each utterance is its own prompt and decode).  Rewind to position 0 and
+ * forget the feedback id (the cache is not cleared: it is only read at positions that
+ * have been written since), and re-arm the device side, stream-ordered: the device error
+ * word, the abort flag a timed-out wait raised and the timeout record are cleared.  Read
+ * them first with mk_status / mk_error_info if they matter.  MK_ERR_ARG for a NULL handle,
+ * MK_ERR_HIP if the clearing cannot be enqueued. */
 int mk_reset(mk_handle* h);
 
 /* Current position (positions written so far).  Host only, no sync. */
@@ -182,7 +199,7 @@ int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
  * that gives up latches MK_ERR_TIMEOUT in the device error word and raises the abort
  * flag; every other wait sees the flag within 128 rounds, so every wave of the launch
  * leaves and the call completes; mk_status then returns MK_ERR_TIMEOUT, mk_error_info
- * says where, and the handle needs mk_reset before it decodes again.  A small limit is
+ * says where, and mk_reset (which clears the flag and the error word) re-arms the handle.  A small limit is
  * how a host forces that path.  MK_ERR_ARG for a NULL handle. */
 int mk_set_spin_limit(mk_handle* h, uint32_t polls);
 
@@ -205,8 +222,14 @@ int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out);
  * ended early, e.g. on a wait timeout).  MK_ERR_HIP if the stream reports an error. */
 int mk_query(mk_handle* h, int32_t* idle);
 
-/* Synchronize the stream and report the device error word (MK_OK when clean).
- * The word is cleared by the read. */
+/* Faults found inside the running kernel (an id outside the vocabulary, a position
+ * outside the rotary table, a wait for another workgroup that gave up) cannot return
+ * from a launch that loops over many steps (the dev.to article, "The idea: one kernel
+ * that never exits"): they are latched on the device and read here.
+ * Synchronize the stream and report the device error word: MK_OK when clean,
+ * MK_ERR_TIMEOUT after a wait gave up, MK_ERR_DEVICE for a bad id or position,
+ * MK_ERR_HIP if the stream reports an error.  The word and the abort flag are cleared
+ * by the read. */
 int mk_status(mk_handle* h);
 
 /* Where the first wait that timed out was (after mk_status returned MK_ERR_TIMEOUT):

@@ -180,18 +180,28 @@ class Decoder:
         """Run the prompt; batched=True takes mk_prefill_batched (the whole prompt as a
         batch through per-layer kernels, then the first id's LM head) instead of the
         persistent kernel position by position."""
-        import torch
         n = ids.numel()
         if out is None:
-            out = torch.empty(1, dtype=torch.int32, device=ids.device)
+            out = self._empty(1, ids.device)
         fn, name = (lib().mk_prefill_batched, "mk_prefill_batched") if batched else (lib().mk_prefill, "mk_prefill")
         _check(fn(self.handle, _ptr(ids), _ptr(rows), _ptr(pos3), n, _ptr(out)), name)
         return out
 
-    def decode(self, n_steps: int, ids=None, rows=None, pos3=None, out=None, device="cuda"):
+    def _empty(self, n: int, device):
+        """An int32 device tensor the kernel writes on the handle's stream: allocated from
+        torch's cache on that stream, so its block is not handed out again before the
+        stream has passed the launch that writes it."""
         import torch
+        dev = torch.device(device)
+        cur = torch.cuda.current_stream(dev)
+        if self._stream in (None, 0, cur.cuda_stream):
+            return torch.empty(n, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(torch.cuda.ExternalStream(self._stream, device=dev)):
+            return torch.empty(n, dtype=torch.int32, device=dev)
+
+    def decode(self, n_steps: int, ids=None, rows=None, pos3=None, out=None, device="cuda"):
         if out is None:
-            out = torch.empty(n_steps, dtype=torch.int32, device=device if ids is None else ids.device)
+            out = self._empty(n_steps, device if ids is None else ids.device)
         _check(lib().mk_decode(self.handle, n_steps, _ptr(ids), _ptr(rows), _ptr(pos3), _ptr(out)), "mk_decode")
         return out
 
@@ -239,7 +249,9 @@ class Decoder:
         with a device error."""
         if chunk < 1:
             raise ValueError("chunk must be at least 1")
-        self.decode(n_steps, ids, rows, pos3, out=out)
+        # the launch writes its ids into `out` until it ends: the tensor stays referenced
+        # here for the generator's whole life
+        out = self.decode(n_steps, ids, rows, pos3, out=out)
         done = 0
         while done < n_steps:
             p = self.progress()

@@ -419,7 +419,7 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   if ((long long)h->pos + n > c->max_seq) return MK_ERR_CAPACITY;
   const size_t part = mk::prefill_part_floats(c->hidden, c->n_q_heads, c->n_kv_heads, c->head_dim, c->intermediate);
   if (c->weight_dtype != MK_BF16 || c->head_dim != 128 || c->n_q_heads != 2 * c->n_kv_heads || part == 0 ||
-      c->hidden % 512 || c->hidden > 2048 || c->intermediate % 512)
+      c->hidden % 512 || c->hidden > 2048 || c->intermediate % 1024)
     return MK_ERR_UNSUPPORTED;
   int e = ensure_pinned(h, 1);
   if (e) return e;
@@ -518,6 +518,11 @@ int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos) {
 
 int mk_reset(mk_handle* h) {
   if (!h) return MK_ERR_ARG;
+  // re-arm the device side too (stream-ordered): the error word, the abort flag a timed-out
+  // wait raised (every later wait would give up early otherwise) and the timeout record
+  if (hipMemsetAsync(h->ctl, 0, 2 * sizeof(uint32_t), h->stream) != hipSuccess ||
+      hipMemsetAsync(h->ctl + 3, 0, 5 * sizeof(uint32_t), h->stream) != hipSuccess)
+    return MK_ERR_HIP;
   h->pos = 0;
   h->have_last = false;
   return MK_OK;

@@ -167,3 +167,29 @@ def compare(gpu: GpuRun, orc: OracleRun, n_steps: Optional[int] = None):
     worst = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= HIDDEN_RTOL, f"hidden rel-L2 {err.max():.3e} at position {worst[0]} layer {worst[1]}"
     return {"ids_checked": checked, "strict_ids": strict, "max_hidden_rel_l2": float(err.max()), "median_hidden_rel_l2": float(np.median(err))}
+
+
+def check_free_run(shape, weights, inp: Inputs, gpu: GpuRun, orc: OracleRun, dtype=np.float64):
+    """The oracle's own free-running greedy decode (``Decoder.generate``) from its own
+    prefill gives the GPU's ids up to the first position whose oracle top-1/top-2 margin
+    is at most MARGIN (there the two may legitimately part).  Greedy-feedback workloads
+    (ids inputs) only.  Returns the number of ids compared."""
+    assert inp.step_ids is None and inp.step_rows is None and inp.prompt_ids is not None
+    dec = OracleDecoder.from_shape(shape, weights, dtype=dtype)
+    if inp.kv is not None:
+        dec.load_kv(inp.kv)
+    first, first_logits, _ = dec.prefill(inp.prompt_ids)
+    if top2_margin(first_logits) <= MARGIN:
+        return 0
+    assert first == gpu.first_id, f"prefill: oracle {first} != gpu {gpu.first_id}"
+    # the teacher-forced replay read the GPU's ids, so its margins are the free run's up to
+    # the first difference: ids before the first low-margin step are strict
+    n = orc.logits.shape[0]
+    m = n
+    for s in range(n):
+        if np.isnan(orc.logits[s, 0]) or top2_margin(orc.logits[s]) <= MARGIN:
+            m = s
+            break
+    free = dec.generate(first, m)
+    assert np.array_equal(free, gpu.ids[:m]), f"the oracle's free run parts from the GPU's ids before step {m}"
+    return m

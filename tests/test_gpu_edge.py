@@ -120,7 +120,8 @@ def test_forced_timeout_reported_and_recovered(shape):
     """A spin limit of one poll round makes the first wait for another workgroup give up:
     the launch still completes (every wave leaves at the same barrier), mk_status reports
     MK_ERR_TIMEOUT with the place recorded, and after mk_reset with the default limit the
-    handle decodes exactly as before (each body: fp32 LDS tiles, bf16 LDS tiles, register
+    handle decodes exactly as before, also when mk_reset is called without reading the
+    status first (each body: fp32 LDS tiles, bf16 LDS tiles, register
     rings)."""
     import torch
     from persistent_megakernel_loop_amd.binding import lib
@@ -153,8 +154,21 @@ def test_forced_timeout_reported_and_recovered(shape):
     again = dec.decode(inp.n_steps, *steps)
     torch.cuda.synchronize()
     dec.check()
-    dec.close()
     assert np.array_equal(again.cpu().numpy(), ref)
+
+    # mk_reset alone re-arms the handle: a timed-out launch, no mk_status, then reset
+    dec.reset()
+    dec.set_spin_limit(1)
+    dec.prefill(*prompt)
+    dec.decode(inp.n_steps, *steps)
+    dec.set_spin_limit(0)
+    dec.reset()
+    dec.prefill(*prompt)
+    third = dec.decode(inp.n_steps, *steps)
+    torch.cuda.synchronize()
+    assert dec.status() == 0
+    dec.close()
+    assert np.array_equal(third.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("batched", [False, True], ids=["per-position", "batched"])

@@ -9,13 +9,13 @@ import numpy as np
 import pytest
 
 from persistent_megakernel_loop_amd import workload as wl
-from tests.parity import compare, make_inputs, run_gpu, run_oracle
+from tests.parity import check_free_run, compare, make_inputs, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
 
 def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=None, random_gains=False,
-          logits_every=1):
+          logits_every=1, free_run=False):
     from persistent_megakernel_loop_amd.binding import weights_to_device
 
     print(f"[case] {shape.name} L={shape.n_layers} V={shape.vocab} steps={n_steps} prompt={prompt_len} "
@@ -27,13 +27,16 @@ def _case(shape, n_steps=None, prompt_len=None, kv_prefill=None, steps_checked=N
     del dw
     orc = run_oracle(shape, weights, inp, gpu, steps=steps_checked, logits_every=logits_every)
     summary = compare(gpu, orc)
+    if free_run:
+        summary["free_run_ids_equal"] = check_free_run(shape, weights, inp, gpu, orc)
     print(f"[case] {shape.name}: {summary}", flush=True)
     return gpu, summary
 
 
 def test_tiny_fp32_full_run():
-    """The tiny fp32 decoder: 8 prompt ids, 32 greedy steps."""
-    _case(wl.TINY)
+    """The tiny fp32 decoder: 8 prompt ids, 32 greedy steps; the oracle's own free run
+    gives the GPU's ids up to its first low-margin step."""
+    _case(wl.TINY, free_run=True)
 
 
 def test_tiny_random_gains_ragged_vocab():
@@ -103,8 +106,10 @@ def test_full_talker_0p6b():
 
 def test_full_text_0p6b():
     """The Qwen3-0.6B-shaped text decoder (151936-row tied head): 16 prompt ids, one launch of
-    64 greedy steps; every layer at every position, ids at every 4th step and the last."""
-    _case(wl.TEXT_0P6B, n_steps=64, logits_every=4)
+    64 greedy steps; every layer at every position and every id (the full head each step),
+    and the oracle's own free run against the GPU's ids up to the first low-margin step."""
+    _, summary = _case(wl.TEXT_0P6B, n_steps=64, free_run=True)
+    assert summary["ids_checked"] == 64
 
 
 def test_full_talker_long_context():

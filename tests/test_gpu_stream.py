@@ -1,13 +1,15 @@
 """Host-side streaming of the decode ids (mk_progress / mk_read_ids / mk_query) on the
-full 28-layer talker: the chunks arrive while the launch is still running, and
-together they are exactly the launch's device output."""
+full 28-layer talker: the chunks arrive while the launch is still running, together
+they are exactly the launch's device output, and every streamed id passes the parity
+rule against the oracle run on the same inputs."""
 import time
 
 import numpy as np
 import pytest
 
 from persistent_megakernel_loop_amd import workload as wl
-from tests.parity import make_inputs
+from oracle import Decoder as OracleDecoder
+from tests.parity import check_id, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +21,8 @@ def test_stream_chunks_arrive_while_running():
     shape = wl.TALKER_0P6B.replace(name="talker-0.6b-stream", steps=64)
     print(f"[case] {shape.name}: 64 steps streamed in chunks of 8", flush=True)
     inp = make_inputs(shape)
-    dec = Decoder(shape, weights_to_device(wl.make_weights(shape)))
+    weights = wl.make_weights(shape)
+    dec = Decoder(shape, weights_to_device(weights))
     t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     prompt = (t(inp.prompt_ids), t(inp.prompt_rows), t(inp.prompt_pos3))
     steps = (t(inp.step_ids), t(inp.step_rows), t(inp.step_pos3))
@@ -54,3 +57,12 @@ def test_stream_chunks_arrive_while_running():
     dec.check()
     dec.close()
     assert np.array_equal(again.cpu().numpy(), got)
+    # the streamed ids against the oracle: the talker's inputs are sentinel rows, so the
+    # oracle runs the same positions on its own (no feedback to replay)
+    orc = OracleDecoder.from_shape(shape, weights)
+    orc.prefill(inp.prompt_ids, inp.prompt_rows, inp.prompt_pos3)
+    strict = 0
+    for s in range(inp.n_steps):
+        logits, _ = orc.step(orc.input_row(int(inp.step_ids[s]), inp.step_rows[s]), inp.step_pos3[s])
+        strict += check_id(int(got[s]), logits, f"streamed step {s}")
+    print(f"[case] streamed ids against the oracle: {inp.n_steps} checked, {strict} strict", flush=True)

@@ -253,3 +253,27 @@ def test_feedback_row_is_the_17_row_sum_with_the_fed_back_codebook0_row():
         # a plausible slip (the row of another id, or no row at all) is caught
         assert not np.allclose(dec.feedback_row(int(t[0]) ^ 1, rest), full, rtol=1e-6, atol=1e-7)
         assert not np.allclose(rest, full, rtol=1e-6, atol=1e-7)
+
+
+def test_generate_matches_transformers_greedy_generate():
+    """Decoder.generate (the free-running greedy loop) against transformers' own greedy
+    generate on the same weights: an untied tiny decoder whose head is scaled so every
+    step's top-1/top-2 margin is decisive, and whose ids vary (a loop that fed back the
+    wrong id, or the same id, would diverge)."""
+    shape = wl.TINY.replace(name="tiny-untied-gen", tied=False, vocab=300)
+    weights = wl.make_weights(shape)
+    weights["lm_head"] = (np.asarray(weights["lm_head"], np.float32) * 40.0).astype(np.float32)
+    prompt = wl.make_prompt_ids(shape)
+    n = 24
+    dec = Decoder.from_shape(shape, weights)
+    first, logits, _ = dec.prefill(prompt)
+    ours = [first] + list(dec.generate(first, n - 1))
+    m = qwen3_from_weights(shape, weights)
+    with torch.no_grad():
+        g = m.generate(torch.from_numpy(prompt.astype(np.int64))[None], max_new_tokens=n, do_sample=False,
+                       output_scores=True, return_dict_in_generate=True, pad_token_id=0)
+    ref = g.sequences[0, len(prompt):].tolist()
+    margins = [float(np.diff(np.sort(s[0].numpy())[-2:])[0]) for s in g.scores]
+    assert min(margins) > 1e-3, margins
+    assert len(set(ref)) >= 6 and sum(a != b for a, b in zip(ref, ref[1:])) >= n // 2, ref
+    assert ours == ref
