@@ -213,8 +213,11 @@ int mk_progress(mk_handle* h, int64_t* steps_done);
  * audio tokens leave chunk by chunk, and the first chunk cannot wait for the rest).
  * Copies ids [first, first + count) of the most recently enqueued
  * prefill/decode call from the pinned mirror into host_out, without synchronizing.
+ * Each mirror entry carries the call that wrote it; an entry the progress word already
+ * counts but that has not arrived yet (the device does not order the two stores) is read
+ * again until it does.
  * MK_ERR_ARG if fewer than first + count ids are published yet (see mk_progress) or
- * an argument is out of range. */
+ * an argument is out of range; MK_ERR_TIMEOUT if a counted entry never arrives. */
 int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out);
 
 /* *idle = 1 if the handle's stream has finished everything enqueued on it, else 0;

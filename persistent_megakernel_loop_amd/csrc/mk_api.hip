@@ -47,7 +47,7 @@ struct mk_handle {
   uint32_t* ctl = nullptr;  // [0] err, [1] abort, [2] last id
   // pinned
   unsigned long long* progress = nullptr;
-  int32_t* pinned_ids = nullptr;
+  unsigned long long* pinned_ids = nullptr;  // entries (call_seq << 32) | id
   int32_t pinned_cap = 0;
   // state
   int32_t pos = 0;
@@ -218,7 +218,7 @@ int ensure_pinned(mk_handle* h, int32_t n) {
   if (h->pinned_ids) hipHostFree(h->pinned_ids);
   h->pinned_ids = nullptr;
   h->pinned_cap = 0;
-  if (hipHostMalloc((void**)&h->pinned_ids, sizeof(int32_t) * (size_t)n, hipHostMallocCoherent) != hipSuccess)
+  if (hipHostMalloc((void**)&h->pinned_ids, sizeof(unsigned long long) * (size_t)n, hipHostMallocCoherent) != hipSuccess)
     return MK_ERR_OOM;
   h->pinned_cap = n;
   return MK_OK;
@@ -566,9 +566,18 @@ int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out) {
   int64_t done = 0;
   mk_progress(h, &done);
   if ((int64_t)first + count > done || first + count > h->pinned_cap) return MK_ERR_ARG;
-  // the progress word is stored after the ids it counts (device side, system scope)
+  // every entry carries the call that wrote it: an entry still behind the progress word
+  // (the two stores are not ordered on the device) is read again until it arrives
   std::atomic_thread_fence(std::memory_order_acquire);
-  for (int32_t i = 0; i < count; ++i) host_out[i] = ((volatile int32_t*)h->pinned_ids)[first + i];
+  const volatile unsigned long long* m = h->pinned_ids;
+  for (int32_t i = 0; i < count; ++i) {
+    unsigned long long v = m[first + i];
+    for (int spin = 0; (uint32_t)(v >> 32) != h->call_seq; ++spin) {
+      if (spin == 10000000) return MK_ERR_TIMEOUT;
+      v = m[first + i];
+    }
+    host_out[i] = (int32_t)(uint32_t)v;
+  }
   return MK_OK;
 }
 

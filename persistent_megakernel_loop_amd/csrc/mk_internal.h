@@ -70,7 +70,7 @@ struct Params {
   const float* rows;         // [n_pos][H] or NULL
   const int32_t* pos3;       // [n_pos][3] or NULL
   int32_t* out_ids;          // [n_pos - logits_from] or NULL
-  int32_t* pinned_ids;       // host-pinned mirror of out_ids, or NULL
+  unsigned long long* pinned_ids;  // host-pinned mirror of out_ids, entries (call_seq << 32) | id, or NULL
   unsigned long long* progress;  // host-pinned step counter
   float* dbg_hidden;         // [n_pos][L+1][H] or NULL
   unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL

@@ -820,7 +820,9 @@ __global__ __launch_bounds__(256) void pf_argmax_kernel(LmArgs M, int n_blk) {
     if (id == 0x7fffffff) id = 0;  // every logit NaN: row 0
     M.out_first[0] = id;
     *M.last_id = id;
-    if (M.pinned_ids) __hip_atomic_store(M.pinned_ids, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (M.pinned_ids)
+      __hip_atomic_store(M.pinned_ids, ((unsigned long long)M.call_seq << 32) | (uint32_t)id, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
     __threadfence_system();
     __hip_atomic_store(M.progress, ((unsigned long long)M.call_seq << 32) | 1ull, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_SYSTEM);
