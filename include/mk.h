@@ -50,6 +50,11 @@ extern "C" {
 #define MK_ERR_DEVICE      -7   /* device error word: bad id or bad position        */
 #define MK_ERR_TIMEOUT     -8   /* device error word: a cross-workgroup wait timed out */
 #define MK_ERR_STATE       -9   /* call order: e.g. feedback decode with no previous id */
+#define MK_ERR_SCRATCH    -10   /* the shape needs more than MK_STATIC_SCRATCH_BYTES of scratch */
+
+/* Size of the fixed device array mk_prefill_batched_noalloc works in (48 MiB); every
+ * device the library runs on holds one from its first handle until the process ends. */
+#define MK_STATIC_SCRATCH_BYTES (48u << 20)
 
 /* ---- dtypes ----------------------------------------------------------------- */
 #define MK_F32  0
@@ -98,6 +103,8 @@ typedef struct mk_handle mk_handle;
  * progress word and the pinned id mirror (for calls of up to 4096 ids; a larger call
  * grows it, with a stream synchronization), pack the weights, build the rotary cos/sin table (computed in
  * double, stored as float) and check that one workgroup per CU fits co-resident.
+ * The first handle on a device also looks up that device's address of the fixed
+ * scratch array of mk_prefill_batched_noalloc (MK_ERR_HIP if that fails).
  * stream: a hipStream_t (NULL = the null stream).  Synchronous.
  * Returns MK_OK and *out, or a negative code with *out = NULL. */
 int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** out);
@@ -135,6 +142,22 @@ int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const in
  * flagged in the device error word and read as 0, as in mk_prefill. */
 int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
                        int32_t n, int32_t* d_out_first);
+
+/* mk_prefill_batched for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * kernels and results (bit for bit) as mk_prefill_batched; its scratch is a fixed
+ * array of MK_STATIC_SCRATCH_BYTES per device instead of a buffer the handle allocates,
+ * and it calls no allocating routine (the pinned mirror entry it publishes into was
+ * allocated by mk_create).  Every call on a device shares that device's array and
+ * leaves its contents behind; each word a call reads it has written first, so nothing
+ * needs clearing.  Calls that overlap on one device, from any handle or stream, race
+ * on the array: the caller orders them.  MK_ERR_SCRATCH if the handle's shape needs
+ * more than the array holds (no shape with a built body does: the hidden-2048 body
+ * needs about 41 MiB, whatever n is, as the prompt runs in chunks of 64); MK_ERR_STATE
+ * if the array's device address is not known (mk_create looks it up on the handle's
+ * device); other errors as mk_prefill_batched. */
+int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
+                               int32_t n, int32_t* d_out_first);
 
 /* The hot path: n_steps decode steps in ONE launch.  Step s runs at position
  * position+s and reads

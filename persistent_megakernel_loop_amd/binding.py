@@ -17,7 +17,7 @@ _LIB_NAME = "libmk.so"
 
 MK_F32, MK_BF16 = 0, 1
 
-EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
+EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_prefill_batched_noalloc", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
            "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
@@ -66,6 +66,7 @@ def lib():
     L.mk_create.argtypes = [ctypes.POINTER(MkWeights), ctypes.POINTER(MkCfg), vp, ctypes.POINTER(vp)]
     L.mk_prefill.argtypes = [vp, vp, vp, vp, i32, vp]
     L.mk_prefill_batched.argtypes = [vp, vp, vp, vp, i32, vp]
+    L.mk_prefill_batched_noalloc.argtypes = [vp, vp, vp, vp, i32, vp]
     L.mk_decode.argtypes = [vp, i32, vp, vp, vp, vp]
     L.mk_load_kv.argtypes = [vp, vp, i32]
     L.mk_reset.argtypes = [vp]
@@ -185,6 +186,14 @@ class Decoder:
             out = self._empty(1, ids.device)
         fn, name = (lib().mk_prefill_batched, "mk_prefill_batched") if batched else (lib().mk_prefill, "mk_prefill")
         _check(fn(self.handle, _ptr(ids), _ptr(rows), _ptr(pos3), n, _ptr(out)), name)
+        return out
+
+    def prefill_batched_noalloc(self, ids, out, rows=None, pos3=None):
+        """mk_prefill_batched_noalloc: the batched prefill in the library's fixed scratch
+        array; the caller passes the output (a device int32 tensor of at least one
+        element), so the call allocates nothing."""
+        _check(lib().mk_prefill_batched_noalloc(self.handle, _ptr(ids), _ptr(rows), _ptr(pos3), ids.numel(),
+                                                _ptr(out)), "mk_prefill_batched_noalloc")
         return out
 
     def _empty(self, n: int, device):

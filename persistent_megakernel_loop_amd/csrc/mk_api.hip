@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -60,12 +61,8 @@ struct mk_handle {
   unsigned long long* dbg_phase = nullptr;
   int32_t dbg_phase_wg = 0;
   uint32_t spin_limit = kDefaultSpinLimit;
-  // batched prefill scratch, allocated by the first batched call
+  // batched prefill scratch, allocated by the first mk_prefill_batched call
   uint8_t* pf_buf = nullptr;
-  float *pf_x = nullptr, *pf_part = nullptr, *pf_q = nullptr, *pf_ss = nullptr, *pf_blk_val = nullptr;
-  int32_t* pf_blk_idx = nullptr;
-  float* pf_att = nullptr;
-  uint16_t* pf_xs = nullptr;
 };
 
 namespace {
@@ -291,6 +288,133 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   return MK_OK;
 }
 
+
+// Byte offsets of the batched prefill's scratch regions (activations, their bf16 split,
+// queries, sums of squares, LM-head block maxima, attention and product partials) for a
+// handle's shape; `bytes` is the whole.  0 bytes: the shape is not supported.
+struct PfScratch { size_t x, xs, q, ss, blk_val, blk_idx, att, part, bytes; };
+
+PfScratch pf_scratch(const mk_cfg* c) {
+  PfScratch r{};
+  const size_t part = mk::prefill_part_floats(c->hidden, c->n_q_heads, c->n_kv_heads, c->head_dim, c->intermediate);
+  if (c->weight_dtype != MK_BF16 || c->head_dim != 128 || c->n_q_heads != 2 * c->n_kv_heads || part == 0 ||
+      c->hidden % 512 || c->hidden > 2048 || c->intermediate % 1024)
+    return r;
+  const size_t ch = mk::kPrefillChunk, H = c->hidden;
+  const size_t K = std::max<size_t>(std::max<size_t>(H, (size_t)c->n_q_heads * c->head_dim), (size_t)c->intermediate);
+  const size_t n_blk = (size_t)(c->vocab + mk::kLmRowsPerBlock - 1) / mk::kLmRowsPerBlock;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes, 256); return at; };
+  r.x = take(ch * H * 4);
+  r.xs = take(2 * K * ch * 2);
+  r.q = take(ch * c->n_q_heads * c->head_dim * 4);
+  r.ss = take(ch * (H / 512) * 4);
+  r.blk_val = take(n_blk * 4);
+  r.blk_idx = take(n_blk * 4);
+  r.att = take((size_t)c->n_kv_heads * mk::kFlashRanges * 2 * ch * (c->head_dim + 2) * 4);
+  r.part = take(part * 4);
+  r.bytes = off;
+  return r;
+}
+
+// Every batched prefill step on scratch `buf` (pf_scratch(&h->cfg).bytes bytes of device
+// memory).  Each scratch word the launches read was written earlier in the same call, so
+// the buffer needs no clearing.  Allocates nothing.
+int prefill_batched(mk_handle* h, uint8_t* buf, const PfScratch& S, const int32_t* d_ids, const float* d_rows,
+                    const int32_t* d_pos3, int32_t n, int32_t* d_out_first) {
+  const mk_cfg* c = &h->cfg;
+  const int ch = mk::kPrefillChunk;
+  const size_t H = c->hidden;
+  mk::PfArgs A{};
+  A.H = c->hidden; A.D = c->head_dim; A.NQ = c->n_q_heads; A.NKV = c->n_kv_heads; A.I = c->intermediate;
+  A.L = c->n_layers; A.vocab = c->vocab; A.max_seq = c->max_seq; A.rope_positions = c->max_seq;
+  A.n_sections = c->n_sections;
+  A.sec_end0 = c->n_sections == 1 ? c->head_dim : c->sections[0];
+  A.sec_end1 = c->n_sections > 1 ? c->sections[0] + c->sections[1] : c->head_dim;
+  A.eps = c->rms_eps;
+  A.embed = (const uint16_t*)h->embed;
+  A.in_norm0 = h->in_norm0;
+  A.rope_cos = h->rope_cos;
+  A.rope_sin = h->rope_sin;
+  A.kcache = (uint16_t*)h->kcache;  // bf16: mk_create ties the cache dtype to the weight dtype
+  A.vcache = (uint16_t*)h->vcache;
+  A.err = h->ctl;
+  A.x = (float*)(buf + S.x);
+  A.xs = (uint16_t*)(buf + S.xs);
+  A.part = (float*)(buf + S.part);
+  A.q = (float*)(buf + S.q);
+  A.ss = (float*)(buf + S.ss);
+  A.att = (float*)(buf + S.att);
+  for (int32_t t0 = 0; t0 < n; t0 += ch) {
+    A.m = std::min(ch, n - t0);
+    A.npp = (A.m + 15) / 16 * 16;
+    A.pos0 = h->pos + t0;
+    A.ids = d_ids + t0;
+    A.rows = d_rows ? d_rows + (size_t)t0 * H : nullptr;
+    A.pos3 = d_pos3 ? d_pos3 + (size_t)t0 * 3 : nullptr;
+    A.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + (size_t)t0 * (c->n_layers + 1) * H : nullptr;
+    if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) return MK_ERR_HIP;
+  }
+  // the last chunk's residual stream is still in place: its last row gives the first id
+  const uint8_t* last_layer = h->arena + (size_t)(c->n_layers - 1) * h->lay.stride;
+  mk::LmArgs M{};
+  M.lm_head = (const uint16_t*)h->lm_head;
+  M.g_final = (const float*)(last_layer + h->lay.gains) + H + 2 * c->head_dim;
+  M.n_last = A.m - 1;
+  M.blk_val = (float*)(buf + S.blk_val);
+  M.blk_idx = (int32_t*)(buf + S.blk_idx);
+  M.out_first = d_out_first;
+  M.last_id = (int32_t*)(h->ctl + 2);
+  M.pinned_ids = h->pinned_ids;
+  M.progress = h->progress;
+  h->call_seq += 1;
+  M.call_seq = h->call_seq;
+  if (mk::launch_prefill_lm(A, M, h->stream)) return MK_ERR_HIP;
+  h->pos += n;
+  h->have_last = true;
+  return MK_OK;
+}
+
+// Scratch of mk_prefill_batched_noalloc: a fixed array that every device the library
+// runs on holds from the code object's load until the process ends.  Host code never
+// passes its name to a kernel: the name is a host-side stand-in, and the device address
+// comes from scratch_setup.
+constexpr size_t kStaticScratchBytes = (size_t)MK_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device; NULL before set-up
+
+// Looks up the address of `scratch` on `dev`, which must be the current device; once
+// per device.
+int scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return MK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return MK_OK;
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+    (void)hipGetLastError();
+    return MK_ERR_HIP;
+  }
+  g_scratch_ptr[dev] = (uint8_t*)ptr;
+  return MK_OK;
+}
+
+uint8_t* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
+int prefill_batched_args(mk_handle* h, const int32_t* d_ids, int32_t n, int32_t* d_out_first, PfScratch* S) {
+  if (!h || !d_ids || n <= 0 || !d_out_first) return MK_ERR_ARG;
+  if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
+  *S = pf_scratch(&h->cfg);
+  if (S->bytes == 0) return MK_ERR_UNSUPPORTED;
+  return MK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,6 +447,7 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   h->wb = cfg->weight_dtype == MK_BF16 ? 2 : 4;
   h->kvb = cfg->kv_dtype == MK_BF16 ? 2 : 4;
   hipGetDevice(&h->device);
+  if (scratch_setup(h->device)) { free_handle(h); return MK_ERR_HIP; }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) { free_handle(h); return MK_ERR_HIP; }
   if (prop.multiProcessorCount != mk::kGrid || blocks < 1 || !prop.cooperativeLaunch) { free_handle(h); return MK_ERR_COOP; }
@@ -414,81 +539,28 @@ int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const in
 
 int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3, int32_t n,
                        int32_t* d_out_first) {
-  if (!h || !d_ids || n <= 0 || !d_out_first) return MK_ERR_ARG;
-  const mk_cfg* c = &h->cfg;
-  if ((long long)h->pos + n > c->max_seq) return MK_ERR_CAPACITY;
-  const size_t part = mk::prefill_part_floats(c->hidden, c->n_q_heads, c->n_kv_heads, c->head_dim, c->intermediate);
-  if (c->weight_dtype != MK_BF16 || c->head_dim != 128 || c->n_q_heads != 2 * c->n_kv_heads || part == 0 ||
-      c->hidden % 512 || c->hidden > 2048 || c->intermediate % 1024)
-    return MK_ERR_UNSUPPORTED;
-  int e = ensure_pinned(h, 1);
+  PfScratch S;
+  int e = prefill_batched_args(h, d_ids, n, d_out_first, &S);
   if (e) return e;
-  const int ch = mk::kPrefillChunk;
-  const size_t H = c->hidden, K = std::max<size_t>(std::max<size_t>(H, (size_t)c->n_q_heads * c->head_dim),
-                                                   (size_t)c->intermediate);
-  const size_t n_blk = (size_t)(c->vocab + mk::kLmRowsPerBlock - 1) / mk::kLmRowsPerBlock;
-  if (!h->pf_buf) {
-    const size_t bx = align_up(ch * H * 4, 256), bxs = align_up(2 * K * ch * 2, 256),
-                 bq = align_up((size_t)ch * c->n_q_heads * c->head_dim * 4, 256),
-                 bs = align_up((size_t)ch * (H / 512) * 4, 256), bl = align_up(n_blk * 4, 256),
-                 ba = align_up((size_t)c->n_kv_heads * mk::kFlashRanges * 2 * ch * (c->head_dim + 2) * 4, 256), bp = part * 4;
-    if (hipMalloc((void**)&h->pf_buf, bx + bxs + bq + bs + 2 * bl + ba + bp) != hipSuccess) {
-      h->pf_buf = nullptr;
-      return MK_ERR_OOM;
-    }
-    uint8_t* p = h->pf_buf;
-    h->pf_x = (float*)p;
-    h->pf_xs = (uint16_t*)(p += bx);
-    h->pf_q = (float*)(p += bxs);
-    h->pf_ss = (float*)(p += bq);
-    h->pf_blk_val = (float*)(p += bs);
-    h->pf_blk_idx = (int32_t*)(p += bl);
-    h->pf_att = (float*)(p += bl);
-    h->pf_part = (float*)(p += ba);
+  e = ensure_pinned(h, 1);
+  if (e) return e;
+  if (!h->pf_buf && hipMalloc((void**)&h->pf_buf, S.bytes) != hipSuccess) {
+    h->pf_buf = nullptr;
+    return MK_ERR_OOM;
   }
-  mk::PfArgs A{};
-  A.H = c->hidden; A.D = c->head_dim; A.NQ = c->n_q_heads; A.NKV = c->n_kv_heads; A.I = c->intermediate;
-  A.L = c->n_layers; A.vocab = c->vocab; A.max_seq = c->max_seq; A.rope_positions = c->max_seq;
-  A.n_sections = c->n_sections;
-  A.sec_end0 = c->n_sections == 1 ? c->head_dim : c->sections[0];
-  A.sec_end1 = c->n_sections > 1 ? c->sections[0] + c->sections[1] : c->head_dim;
-  A.eps = c->rms_eps;
-  A.embed = (const uint16_t*)h->embed;
-  A.in_norm0 = h->in_norm0;
-  A.rope_cos = h->rope_cos;
-  A.rope_sin = h->rope_sin;
-  A.kcache = (uint16_t*)h->kcache;  // bf16: mk_create ties the cache dtype to the weight dtype
-  A.vcache = (uint16_t*)h->vcache;
-  A.err = h->ctl;
-  A.x = h->pf_x; A.xs = h->pf_xs; A.part = h->pf_part; A.q = h->pf_q; A.ss = h->pf_ss; A.att = h->pf_att;
-  for (int32_t t0 = 0; t0 < n; t0 += ch) {
-    A.m = std::min(ch, n - t0);
-    A.npp = (A.m + 15) / 16 * 16;
-    A.pos0 = h->pos + t0;
-    A.ids = d_ids + t0;
-    A.rows = d_rows ? d_rows + (size_t)t0 * H : nullptr;
-    A.pos3 = d_pos3 ? d_pos3 + (size_t)t0 * 3 : nullptr;
-    A.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + (size_t)t0 * (c->n_layers + 1) * H : nullptr;
-    if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) return MK_ERR_HIP;
-  }
-  // the last chunk's residual stream is still in place: its last row gives the first id
-  const uint8_t* last_layer = h->arena + (size_t)(c->n_layers - 1) * h->lay.stride;
-  mk::LmArgs M{};
-  M.lm_head = (const uint16_t*)h->lm_head;
-  M.g_final = (const float*)(last_layer + h->lay.gains) + H + 2 * c->head_dim;
-  M.n_last = A.m - 1;
-  M.blk_val = h->pf_blk_val;
-  M.blk_idx = h->pf_blk_idx;
-  M.out_first = d_out_first;
-  M.last_id = (int32_t*)(h->ctl + 2);
-  M.pinned_ids = h->pinned_ids;
-  M.progress = h->progress;
-  h->call_seq += 1;
-  M.call_seq = h->call_seq;
-  if (mk::launch_prefill_lm(A, M, h->stream)) return MK_ERR_HIP;
-  h->pos += n;
-  h->have_last = true;
-  return MK_OK;
+  return prefill_batched(h, h->pf_buf, S, d_ids, d_rows, d_pos3, n, d_out_first);
+}
+
+int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
+                               int32_t n, int32_t* d_out_first) {
+  PfScratch S;
+  int e = prefill_batched_args(h, d_ids, n, d_out_first, &S);
+  if (e) return e;
+  if (S.bytes > kStaticScratchBytes) return MK_ERR_SCRATCH;
+  if (h->pinned_cap < 1) return MK_ERR_STATE;  // mk_create sizes the mirror for at least one id
+  uint8_t* buf = scratch_ptr(h->device);
+  if (!buf) return MK_ERR_STATE;  // mk_create looks the address up on the handle's device
+  return prefill_batched(h, buf, S, d_ids, d_rows, d_pos3, n, d_out_first);
 }
 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf, const int32_t* d_pos3,
@@ -700,6 +772,7 @@ const char* mk_strerror(int code) {
     case MK_ERR_DEVICE: return "device reported a bad id or position";
     case MK_ERR_TIMEOUT: return "device wait timed out";
     case MK_ERR_STATE: return "no previous id for feedback decode";
+    case MK_ERR_SCRATCH: return "shape needs more scratch than the fixed array holds";
   }
   return "unknown error";
 }

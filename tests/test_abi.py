@@ -77,7 +77,7 @@ def test_struct_layout_matches_header(tmp_path):
 def test_error_strings(lib):
     codes = header_codes()
     errs = {k: v for k, v in codes.items() if k.startswith("MK_ERR") or k == "MK_OK"}
-    assert errs["MK_OK"] == 0 and len(errs) == 10
+    assert errs["MK_OK"] == 0 and len(errs) == 11
     seen = set()
     for name, code in errs.items():
         s = lib.mk_strerror(code).decode()
@@ -161,6 +161,7 @@ def test_null_handle_calls(lib):
     info = (ctypes.c_int32 * 5)()
     assert lib.mk_prefill(None, 0x10, None, None, 4, 0x20) == -1
     assert lib.mk_prefill_batched(None, 0x10, None, None, 4, 0x20) == -1
+    assert lib.mk_prefill_batched_noalloc(None, 0x10, None, None, 4, 0x20) == -1
     assert lib.mk_read_ids(None, 0, 1, (ctypes.c_int32 * 1)()) == -1
     assert lib.mk_query(None, ctypes.byref(ctypes.c_int32())) == -1
     assert lib.mk_decode(None, 4, None, None, None, 0x20) == -1
