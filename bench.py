@@ -97,21 +97,39 @@ def stream_ceiling(torch, gib: int = 2, runs: int = 5) -> dict:
     return out
 
 
-def cpu_baseline(shape, n_prompt, n_steps, budget_s=12.0):
-    """The oracle (float64 numpy) timed on this host on a bounded sample of the same workload.
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
-    The sample replays the timed workload (prefill untimed, then n_steps decode steps)
-    until about budget_s seconds of decode steps have run; steps/s over those steps."""
+
+def blas_info():
+    """(library, threads) of the BLAS numpy calls, from threadpoolctl."""
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            return pools[0].get("internal_api", "blas"), max(int(i.get("num_threads", 1)) for i in pools)
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown", os.cpu_count() or 1
+
+
+def oracle_steps_per_s(shape, n_prompt, n_steps, dtype, budget_s):
+    """The oracle timed on this host on a bounded sample of the workload: the timed
+    workload (prefill untimed, then n_steps decode steps) is replayed until about
+    budget_s seconds of decode steps have run.  (steps/s, steps, passes, seconds)."""
     from oracle import Decoder as OracleDecoder
     from oracle import embed_sum17
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     weights = wl.make_weights(shape)
-    dec = OracleDecoder.from_shape(shape, weights)
+    dec = OracleDecoder.from_shape(shape, weights, dtype=dtype)
     kv0 = shape.kv_prefill
     kv = wl.make_kv_prefill(shape) if kv0 else None
     if shape.inputs == "talker":
@@ -146,9 +164,22 @@ def cpu_baseline(shape, n_prompt, n_steps, budget_s=12.0):
             if time.perf_counter() - t0 + el >= budget_s:
                 break
         el += time.perf_counter() - t0
-    return {"value": done / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode steps of {shape.name} ({passes} pass(es) over the {n_steps}-step workload after "
-                      f"an untimed {n_prompt}-position prefill; float64 numpy oracle), {el:.1f} s"}
+    return done / el, done, passes, el
+
+
+def cpu_baseline(shape, n_prompt, n_steps, budget_s=10.0):
+    """The oracle as it stands, timed on this host's cores: the float64 leg (the oracle
+    the parity tests use) is `value`; the same code with float32 arrays is the `fp32`
+    leg, the rate a plain single-precision CPU implementation of the step reaches."""
+    blas, threads = blas_info()
+    v64, n64, p64, t64 = oracle_steps_per_s(shape, n_prompt, n_steps, np.float64, budget_s)
+    v32, n32, p32, t32 = oracle_steps_per_s(shape, n_prompt, n_steps, np.float32, budget_s)
+    what = f"decode steps of {shape.name} over the {n_steps}-step workload after an untimed {n_prompt}-position prefill"
+    return {"value": v64, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n64} {what} ({p64} pass(es); float64 numpy oracle), {t64:.1f} s",
+            "cpu_model": cpu_model(), "blas": blas, "blas_threads": int(threads),
+            "fp32": {"value": v32, "unit": "steps/s",
+                     "sample": f"{n32} {what} ({p32} pass(es); the oracle with float32 arrays), {t32:.1f} s"}}
 
 
 CSRC = os.path.join(ROOT, "persistent_megakernel_loop_amd", "csrc")
@@ -156,7 +187,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 # The decode kernel's sources: its code and the parameter block the host fills in.
-DECODE_SOURCES = ("mk_internal.h", "mk_kernel.hip")
+DECODE_SOURCES = ("mk_internal.h", "mk_device.h", "mk_kernel.hip")
 
 
 def csrc_digest() -> str:
@@ -176,21 +207,27 @@ def counters_path(workload: str) -> str:
     return os.path.join(PROFILES, f"decode_kernel_{workload}_hbm_counters.txt")
 
 
-def load_traffic(workload: str, steps: int):
-    """HBM bytes per decode launch from the committed counter summary, or None when it is
-    absent, was taken for another step count, or the kernel sources changed since."""
+def load_traffic(workload: str, steps: int, algo: int):
+    """HBM bytes per decode launch from the committed counter summary, with where they come
+    from: the measured bytes when the counters were taken at this step count, else the
+    measured ratio of HBM bytes to algorithmic bytes times this launch's algorithmic bytes.
+    (None, reason) when the summary is absent or the kernel sources changed since."""
     path = counters_path(workload)
     if not os.path.exists(path):
-        return None
+        return None, "no counter summary"
     kv = {}
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.split()[0] if v.split() else ""
-    if kv.get("steps") != str(steps) or kv.get("csrc_sha256") != csrc_digest():
-        return None
-    return int(kv["traffic_bytes_per_launch"])
+    if kv.get("csrc_sha256") != csrc_digest():
+        return None, "kernel sources changed since the counters were taken"
+    if kv.get("steps") == str(steps):
+        return int(kv["traffic_bytes_per_launch"]), f"FETCH_SIZE + WRITE_SIZE at {steps} steps"
+    ratio = float(kv["traffic_over_algorithmic"])
+    return int(round(ratio * algo)), (f"ratio {ratio:.4f} of HBM to algorithmic bytes measured at {kv.get('steps')} "
+                                      f"steps, times this launch's algorithmic bytes")
 
 
 def _pmc_mean(csv_path: str, prefix: str):
@@ -244,6 +281,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--repeats", type=int, default=5, help="timed launches of --steps steps; the median is reported")
     ap.add_argument("--workload", default="talker-0.6b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="leave out the read-stream ceiling measurement")
@@ -320,19 +358,24 @@ def main():
         decode()
     torch.cuda.synchronize()
     dec.check()
-    # timed: one decode launch of K steps, events on the launch stream
-    prepare()
+    # timed: --repeats decode launches of K steps each, every one after the same untimed
+    # prompt, events on the launch stream; the median launch is the measurement
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    decode()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - w0) * 1e3
-    dec.check()
-    launch_ms = e0.elapsed_time(e1)
+    launches, walls = [], []
+    for _ in range(args.repeats):
+        prepare()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        decode()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        walls.append((time.perf_counter() - w0) * 1e3)
+        dec.check()
+        launches.append(e0.elapsed_time(e1))
+    launch_ms = float(np.median(launches))
+    wall_ms = float(np.median(walls))
     ms_step = launch_ms / K
     first_pos = shape.kv_prefill + P
     algo = step_bytes(shape, first_pos, K)
@@ -427,6 +470,7 @@ def main():
     # read-stream ceiling: the bandwidth a plain streaming read reaches on this device
     ceiling = {} if args.no_ceiling else stream_ceiling(torch)
 
+    traffic, traffic_src = load_traffic(shape.name, K, algo)
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms_step, 2),
@@ -442,7 +486,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": shape.name, "layers": shape.n_layers, "hidden": shape.hidden, "vocab": shape.vocab,
                    "prompt_positions": P, "kv_prefill": shape.kv_prefill, "decode_steps": K, "batch": 1,
-                   "weights": "bf16 N(0,0.02) random", "kv_cache": shape.kv_dtype, "launches_timed": 1},
+                   "weights": "bf16 N(0,0.02) random", "kv_cache": shape.kv_dtype,
+                   "launches_timed": args.repeats, "reported": "median launch"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "ttfc_ms": ttfc,
@@ -454,12 +499,17 @@ def main():
         "barrier_share_p99": round(share_p99, 4),
         "stream_ceiling": dict(ceiling, decode_frac_of_ceiling=round(gbps / max(ceiling.values()), 4)) if ceiling else {},
         "wall_ms_timed_launch": round(wall_ms, 3),
+        "launch_ms_all": [round(v, 4) for v in launches],
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": load_traffic(shape.name, K),
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
                      "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(launch_ms, 4)},
     }
+    # release every device resource before the interpreter exits: the handle (arena, cache,
+    # exchange buffers, pinned progress word and id mirror) and every tensor
     dec.close()
-    del inp
+    del dec, inp, kv, out, first, trace
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(shape, P, K)

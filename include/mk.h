@@ -289,14 +289,21 @@ int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal,
 
 /* Stress test of the tagged-word exchange every hop of the decode kernel uses (its own
  * publish and gather code): one cooperative launch of the persistent grid runs `iters`
- * rounds; in each, every workgroup publishes 64 words and gathers all 256 x 64 words of
- * the round, checking every value against what its writer stored.  result (host,
- * [3]): [0] words read with the right tag but a wrong value (stale or torn: must be 0),
- * [1] workgroups whose wait gave up, [2] the device error word.  spin_limit as in
- * mk_set_spin_limit (0: the default); a small limit forces the give-up path.
- * Allocates and frees its buffers; synchronizes `stream`.  MK_ERR_ARG for iters <= 0 or
- * a NULL result; MK_ERR_COOP if the grid cannot be launched co-resident. */
-int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, uint32_t* result, void* stream);
+ * rounds; in each, every workgroup publishes 64 words and gathers the round's words of
+ * its partners, checking every value against what its writer stored.
+ *   xcd_local == 0: all to all (256 x 64 words a round), every word written through to
+ *                   the device coherence point: the decode kernel's cross-XCD hops;
+ *   xcd_local != 0: each workgroup with the 32 of its XCD (workgroups b with the same
+ *                   b % 8; 32 x 64 words a round), and, when a placement check finds
+ *                   every workgroup b on XCD b % 8, with plain stores that stay in that
+ *                   XCD's L2: the decode kernel's local hops.
+ * result (host, [4]): [0] words read with the right tag but a wrong value (stale or
+ * torn: must be 0), [1] workgroups whose wait gave up, [2] the device error word, [3] 1
+ * if the plain stores were used (xcd_local only).  spin_limit as in mk_set_spin_limit
+ * (0: the default); a small limit forces the give-up path.  Allocates and frees its
+ * buffers; synchronizes `stream`.  MK_ERR_ARG for iters <= 0 or a NULL result;
+ * MK_ERR_COOP if the grid cannot be launched co-resident. */
+int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, int32_t xcd_local, uint32_t* result, void* stream);
 
 /* Number of workgroups of the persistent grid (one per CU). */
 int mk_grid_size(mk_handle* h, int32_t* n);

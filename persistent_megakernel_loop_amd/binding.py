@@ -81,7 +81,7 @@ def lib():
     L.mk_error_info.argtypes = [vp, pi32]
     L.mk_selftest_lds_dma.argtypes = [vp, vp, i32, i32, vp]
     L.mk_selftest_gemm.argtypes = [vp, i32, i32, vp, i32, vp, vp]
-    L.mk_selftest_exchange.argtypes = [i32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_uint32), vp]
+    L.mk_selftest_exchange.argtypes = [i32, ctypes.c_uint32, i32, ctypes.POINTER(ctypes.c_uint32), vp]
     L.mk_bench_stream_read.argtypes = [vp, ctypes.c_uint64, i32, vp, i32, vp]
     L.mk_grid_size.argtypes = [vp, pi32]
     L.mk_embed_sum.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, vp, vp, vp]
@@ -323,10 +323,12 @@ def selftest_gemm(w, x, y=None, stream=None):
     return y
 
 
-def selftest_exchange(iters: int, spin_limit: int = 0, stream=None):
-    """Stress test of the exchange protocol: (mismatched words, workgroups that gave up, device error word)."""
-    res = (ctypes.c_uint32 * 3)()
-    _check(lib().mk_selftest_exchange(iters, spin_limit, res, _stream_handle(stream)), "mk_selftest_exchange")
+def selftest_exchange(iters: int, spin_limit: int = 0, xcd_local: bool = False, stream=None):
+    """Stress test of the exchange protocol: (mismatched words, workgroups that gave up,
+    device error word, 1 if XCD-local plain stores were used)."""
+    res = (ctypes.c_uint32 * 4)()
+    _check(lib().mk_selftest_exchange(iters, spin_limit, int(xcd_local), res, _stream_handle(stream)),
+           "mk_selftest_exchange")
     return tuple(int(v) for v in res)
 
 

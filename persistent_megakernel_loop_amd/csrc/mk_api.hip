@@ -707,10 +707,10 @@ int mk_bench_stream_read(const void* d_src, uint64_t bytes, int32_t nontemporal,
              : MK_OK;
 }
 
-int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, uint32_t* result, void* stream) {
+int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, int32_t xcd_local, uint32_t* result, void* stream) {
   if (iters <= 0 || !result) return MK_ERR_ARG;
   hipStream_t st = (hipStream_t)stream;
-  const size_t n_words = 2 * (size_t)mk::kGrid * 64;
+  const size_t n_words = 2 * (size_t)mk::kGrid * 64 + mk::kGrid;  // two rounds' words, then the placement words
   unsigned long long* words = nullptr;
   uint32_t* ctl = nullptr;
   if (hipMalloc((void**)&words, n_words * 8) != hipSuccess) return MK_ERR_OOM;
@@ -727,14 +727,17 @@ int mk_selftest_exchange(int32_t iters, uint32_t spin_limit, uint32_t* result, v
   P.err = ctl;
   P.abort_flag = ctl + 1;
   P.xq = words;
-  uint32_t* bad = ctl + 16;  // [0] mismatched words, [1] workgroups whose wait gave up
-  if (e == MK_OK && mk::launch_exchange_stress(P, words, iters, bad, st)) e = MK_ERR_COOP;
-  uint32_t host[18] = {0};
+  uint32_t* bad = ctl + 16;  // [0] mismatched words, [1] workgroups whose wait gave up, [2] plain stores used
+  if (e == MK_OK && mk::launch_exchange_stress(P, words, words + 2 * (size_t)mk::kGrid * 64, iters, xcd_local != 0,
+                                               bad, st))
+    e = MK_ERR_COOP;
+  uint32_t host[19] = {0};
   if (hipStreamSynchronize(st) != hipSuccess || hipMemcpy(host, ctl, sizeof host, hipMemcpyDeviceToHost) != hipSuccess)
     e = MK_ERR_HIP;
   result[0] = host[16];
   result[1] = host[17];
   result[2] = host[0];
+  result[3] = host[18];
   hipFree(words);
   hipFree(ctl);
   return e;

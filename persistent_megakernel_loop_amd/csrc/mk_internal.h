@@ -94,7 +94,9 @@ int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* t
                      int hidden, int bf16, const int32_t* ids, int n, float* rows, int32_t* bad, void* stream);
 int launch_widen(const void* src, float* dst, int n, int bf16, void* stream);
 int launch_lds_dma_selftest(const void* src, void* dst, int n_chunks, int offset_bytes, void* stream);
-// Cooperative stress test of the exchange protocol (p supplies tag0, spin_limit, err, abort_flag, xq).
-int launch_exchange_stress(const Params& p, unsigned long long* words, int iters, uint32_t* bad, void* stream);
+// Cooperative stress test of the exchange protocol (p supplies tag0, spin_limit, err, abort_flag, xq);
+// local != 0: XCD-local exchanges with plain stores (place: kGrid words for the placement check).
+int launch_exchange_stress(const Params& p, unsigned long long* words, unsigned long long* place, int iters, int local,
+                           uint32_t* bad, void* stream);
 
 }  // namespace mk

@@ -186,8 +186,8 @@ def test_selftest_and_embed_sum_argument_checks(lib):
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 9217, 0, None) == -1
     assert lib.mk_selftest_lds_dma(0x10, 0x20, 1, 144 * 1024 - 8, None) == -1
     # exchange stress test: positive rounds, a result array
-    assert lib.mk_selftest_exchange(0, 0, (ctypes.c_uint32 * 3)(), None) == -1
-    assert lib.mk_selftest_exchange(10, 0, None, None) == -1
+    assert lib.mk_selftest_exchange(0, 0, 0, (ctypes.c_uint32 * 4)(), None) == -1
+    assert lib.mk_selftest_exchange(10, 0, 1, None, None) == -1
     # read-stream measurement kernel: non-null buffers, bytes a positive multiple of 16, 1..65536 blocks
     assert lib.mk_bench_stream_read(None, 1024, 0, 0x10, 64, None) == -1
     assert lib.mk_bench_stream_read(0x10, 1000, 0, 0x20, 64, None) == -1
