@@ -454,6 +454,23 @@ def main():
                     "over_persistent": round(per / ms_step, 2), "steps": n_abl,
                     "launches_per_step": 9 * shape.n_layers + 3}
 
+    # the streaming loop: prompt, then the K frames of one launch handed to the stub codec in
+    # chunks of 4 as they are published; talker-only RTF from its clock
+    speech = {}
+    if args.ttfc_trials > 0:
+        from persistent_megakernel_loop_amd.codec import StubCodec, speak
+        dec.reset()
+        if kv is not None:
+            dec.load_kv(kv, shape.kv_prefill)
+        torch.cuda.synchronize()
+        st = speak(dec, K, inp["step_ids"], inp["step_rows"], inp["step_pos3"],
+                   prompt=(inp["prompt_ids"], inp["prompt_rows"], inp["prompt_pos3"]) if P else None, chunk=4,
+                   codec=StubCodec(codebook_size=shape.vocab), batched_prefill=batched_ok)
+        torch.cuda.synchronize()
+        dec.check()
+        speech = {"rtf": round(st.rtf, 5), "ttfc_ms": round(st.ttfc_ms, 3), "total_ms": round(st.total_ms, 3),
+                  "frames": st.frames, "audio_s": round(st.audio_s, 3), "chunk": 4, "codec": "stub (tone per code)"}
+
     # barrier share: in-kernel wait ticks over position ticks, one separate traced run
     prepare()
     trace = torch.zeros((K, dec.grid_size(), 2), dtype=torch.int64, device="cuda")
@@ -494,7 +511,9 @@ def main():
         "ttfc_ms_per_position_prefill": ttfc_pp,
         "prefill_ms": pf_ms,
         "launch_per_phase": ablation,
-        "rtf_talker_only": round(ms_step / FRAME_MS, 5),
+        "rtf_talker_only": speech.get("rtf"),
+        "rtf_kernel_only": round(ms_step / FRAME_MS, 5),
+        "speech": speech,
         "barrier_share": round(share, 4),
         "barrier_share_p99": round(share_p99, 4),
         "stream_ceiling": dict(ceiling, decode_frac_of_ceiling=round(gbps / max(ceiling.values()), 4)) if ceiling else {},

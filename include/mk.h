@@ -51,6 +51,10 @@ extern "C" {
 #define MK_ERR_TIMEOUT     -8   /* device error word: a cross-workgroup wait timed out */
 #define MK_ERR_STATE       -9   /* call order: e.g. feedback decode with no previous id */
 #define MK_ERR_SCRATCH    -10   /* the shape needs more than MK_STATIC_SCRATCH_BYTES of scratch */
+#define MK_ERR_OVERRUN    -11   /* the id ring moved past ids not yet read            */
+
+/* Entries of the pinned id ring that mk_read_ids reads (4096). */
+#define MK_ID_RING 4096
 
 /* Size of the fixed device array mk_prefill_batched_noalloc works in (48 MiB); every
  * device the library runs on holds one from its first handle until the process ends. */
@@ -100,9 +104,10 @@ typedef struct mk_handle mk_handle;
  * What's the Catch with These Megakernels?", has the rotary frequency tables computed on
  * the host; both are what this call does before any decode.
  * Validate cfg, allocate the arena, KV cache, exchange buffers, the pinned
- * progress word and the pinned id mirror (for calls of up to 4096 ids; a larger call
- * grows it, with a stream synchronization), pack the weights, build the rotary cos/sin table (computed in
+ * progress word and the pinned id ring (MK_ID_RING entries, reused by every call: no
+ * call ever grows it), pack the weights, build the rotary cos/sin table (computed in
  * double, stored as float) and check that one workgroup per CU fits co-resident.
+ * MK_ERR_ARG if max_seq >= 2^26 (the ring's entries number slots below that).
  * The first handle on a device also looks up that device's address of the fixed
  * scratch array of mk_prefill_batched_noalloc (MK_ERR_HIP if that fails).
  * stream: a hipStream_t (NULL = the null stream).  Synchronous.
@@ -127,7 +132,7 @@ int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const in
  * pass over the weights (matrix-core products over the packed weight tiles, causal
  * attention over the cache, the cache written as mk_prefill writes it), then the LM
  * head over the last position and its greedy id (ties: lowest index), published as
- * mk_prefill publishes it (d_out_first[0], the feedback id, the pinned mirror and the
+ * mk_prefill publishes it (d_out_first[0], the feedback id, the pinned id ring and the
  * progress word).  The time to the first id is where per-position work costs most
  * (the dev.to article "Porting a 1200-line persistent CUDA megakernel to Qwen3-TTS",
  * "Making it talk end-to-end"), and a batch is the case a one-position-per-pass
@@ -147,7 +152,7 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
  * kernels and results (bit for bit) as mk_prefill_batched; its scratch is a fixed
  * array of MK_STATIC_SCRATCH_BYTES per device instead of a buffer the handle allocates,
- * and it calls no allocating routine (the pinned mirror entry it publishes into was
+ * and it calls no allocating routine (the pinned ring entry it publishes into was
  * allocated by mk_create).  Every call on a device shares that device's array and
  * leaves its contents behind; each word a call reads it has written first, so nothing
  * needs clearing.  Calls that overlap on one device, from any handle or stream, race
@@ -171,7 +176,8 @@ int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* 
  *   d_ids[s] >= 0 : embed[d_ids[s]];
  *   d_ids[s] <  0 : row s of d_embed_buf ([n_steps][hidden] float32).
  * d_pos3 as in mk_prefill.  d_out_ids [n_steps] int32 receives the greedy ids
- * (ties: lowest index).  The pinned progress word advances after every step. */
+ * (ties: lowest index); each id also goes to the pinned id ring (see mk_read_ids) and
+ * the pinned progress word advances after every step. */
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
               const int32_t* d_pos3, int32_t* d_out_ids);
 
@@ -235,12 +241,16 @@ int mk_progress(mk_handle* h, int64_t* steps_done);
  * 1200-line persistent CUDA megakernel to Qwen3-TTS", "Making it talk end-to-end":
  * audio tokens leave chunk by chunk, and the first chunk cannot wait for the rest).
  * Copies ids [first, first + count) of the most recently enqueued
- * prefill/decode call from the pinned mirror into host_out, without synchronizing.
- * Each mirror entry carries the call that wrote it; an entry the progress word already
- * counts but that has not arrived yet (the device does not order the two stores) is read
- * again until it does.
- * MK_ERR_ARG if fewer than first + count ids are published yet (see mk_progress) or
- * an argument is out of range; MK_ERR_TIMEOUT if a counted entry never arrives. */
+ * prefill/decode call from the pinned id ring into host_out, without synchronizing.
+ * The ring holds MK_ID_RING entries: id s of a call goes to entry s % MK_ID_RING,
+ * tagged with its call and its lap s / MK_ID_RING, so a call of any length streams
+ * through it with no synchronization, as long as the reader stays fewer than
+ * MK_ID_RING ids behind the kernel.  An entry the progress word already counts but
+ * that has not arrived yet (the device does not order the two stores) is read again
+ * until it does.  MK_ERR_ARG if fewer than first + count ids are published yet (see
+ * mk_progress) or an argument is out of range; MK_ERR_OVERRUN if a later lap has
+ * already overwritten an entry asked for (the ids stay in the call's d_out_ids);
+ * MK_ERR_TIMEOUT if a counted entry never arrives. */
 int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out);
 
 /* *idle = 1 if the handle's stream has finished everything enqueued on it, else 0;

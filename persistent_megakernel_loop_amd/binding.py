@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmk.so"
 
 MK_F32, MK_BF16 = 0, 1
+MK_ERR_OVERRUN = -11
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_prefill_batched_noalloc", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
            "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
@@ -253,9 +254,10 @@ class Decoder:
 
     def stream(self, n_steps: int, ids=None, rows=None, pos3=None, chunk: int = 4, out=None):
         """Enqueue one decode launch of n_steps steps and yield its ids as numpy chunks of
-        `chunk` (the last may be shorter) while the kernel runs, read from the pinned
-        mirror as the progress word advances.  Raises MkError if the launch ends early
-        with a device error."""
+        `chunk` (the last may be shorter) while the kernel runs, read from the pinned id
+        ring as the progress word advances.  A reader that falls more than the ring's
+        4096 ids behind gets the rest from the launch's device output once it ends.
+        Raises MkError if the launch ends early with a device error."""
         if chunk < 1:
             raise ValueError("chunk must be at least 1")
         # the launch writes its ids into `out` until it ends: the tensor stays referenced
@@ -264,17 +266,24 @@ class Decoder:
         done = 0
         while done < n_steps:
             p = self.progress()
-            if p - done >= chunk or p == n_steps:
-                yield self.read_ids(done, p - done)
+            if p - done >= chunk or p == n_steps or (p > done and self.idle()):
+                try:
+                    got = self.read_ids(done, p - done)
+                except MkError as e:
+                    if e.code != MK_ERR_OVERRUN:
+                        raise
+                    break
+                yield got
                 done = p
-            elif self.idle():
-                p = self.progress()
-                if p > done:
-                    yield self.read_ids(done, p - done)
-                    done = p
-                if done < n_steps:
-                    self.check()
-                    raise RuntimeError(f"decode ended after {done} of {n_steps} ids")
+            elif self.idle() and self.progress() == done:
+                self.check()
+                raise RuntimeError(f"decode ended after {done} of {n_steps} ids")
+        if done < n_steps:  # overrun: the rest from the device output
+            import torch
+            torch.cuda.synchronize(out.device)
+            rest = out[done:].cpu().numpy()
+            for k in range(0, len(rest), chunk):
+                yield rest[k:k + chunk]
         self.check()
 
     def status(self) -> int:

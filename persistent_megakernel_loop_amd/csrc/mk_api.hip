@@ -16,6 +16,8 @@
 #include "mk_internal.h"
 #include "mk_prefill.h"
 
+static_assert(MK_ID_RING == mk::kIdRing, "id ring size in mk.h");
+
 using mk::LayerLayout;
 using mk::Params;
 
@@ -48,8 +50,7 @@ struct mk_handle {
   uint32_t* ctl = nullptr;  // [0] err, [1] abort, [2] last id
   // pinned
   unsigned long long* progress = nullptr;
-  unsigned long long* pinned_ids = nullptr;  // entries (call_seq << 32) | id
-  int32_t pinned_cap = 0;
+  unsigned long long* pinned_ids = nullptr;  // id ring [mk::kIdRing], entries mk::ring_entry
   // state
   int32_t pos = 0;
   bool have_last = false;
@@ -99,6 +100,7 @@ int validate_cfg(const mk_cfg* c) {
   if (sum != c->head_dim / 2) return MK_ERR_ARG;
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return MK_ERR_ARG;
   if (c->vocab >= (1 << 18)) return MK_ERR_UNSUPPORTED;
+  if (c->max_seq >= (1 << 26)) return MK_ERR_ARG;  // id ring entries hold slots below 2^26
   if ((long long)c->max_seq * c->n_layers * c->n_kv_heads * c->head_dim > (1ll << 40)) return MK_ERR_ARG;
   return MK_OK;
 }
@@ -209,25 +211,11 @@ int device_status(mk_handle* h, bool clear) {
   return MK_OK;
 }
 
-int ensure_pinned(mk_handle* h, int32_t n) {
-  if (n <= h->pinned_cap) return MK_OK;
-  HIPCK(hipStreamSynchronize(h->stream));
-  if (h->pinned_ids) hipHostFree(h->pinned_ids);
-  h->pinned_ids = nullptr;
-  h->pinned_cap = 0;
-  if (hipHostMalloc((void**)&h->pinned_ids, sizeof(unsigned long long) * (size_t)n, hipHostMallocCoherent) != hipSuccess)
-    return MK_ERR_OOM;
-  h->pinned_cap = n;
-  return MK_OK;
-}
-
 int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const int32_t* pos3, int32_t* out,
         int logits_from, int feedback, bool prompt) {
   if (n <= 0) return MK_ERR_ARG;
   if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
   if (feedback && !h->have_last) return MK_ERR_STATE;
-  int e = ensure_pinned(h, n - logits_from);
-  if (e) return e;
   Params P{};
   P.layers = h->arena;
   P.lay = h->lay;
@@ -495,9 +483,13 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
   if ((size_t)(p - h->xbuf) > h->xbuf_words) { free_handle(h); return MK_ERR_ARG; }
   if (hipHostMalloc((void**)&h->progress, 64, hipHostMallocCoherent) != hipSuccess) { free_handle(h); return MK_ERR_OOM; }
   *(volatile unsigned long long*)h->progress = 0;
-  // the pinned id mirror for calls of up to 4096 ids, so that a first call does not pay
-  // for the allocation (larger calls grow it)
-  if (ensure_pinned(h, std::min(cfg->max_seq, 4096))) { free_handle(h); return MK_ERR_OOM; }
+  if (hipHostMalloc((void**)&h->pinned_ids, sizeof(unsigned long long) * mk::kIdRing, hipHostMallocCoherent) !=
+      hipSuccess) {
+    h->pinned_ids = nullptr;
+    free_handle(h);
+    return MK_ERR_OOM;
+  }
+  std::memset(h->pinned_ids, 0, sizeof(unsigned long long) * mk::kIdRing);
 
   hipStream_t s = h->stream;
   if (hipMemsetAsync(h->xbuf, 0, h->xbuf_words * 8, s) != hipSuccess || hipMemsetAsync(h->ctl, 0, 256, s) != hipSuccess) {
@@ -542,8 +534,6 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   PfScratch S;
   int e = prefill_batched_args(h, d_ids, n, d_out_first, &S);
   if (e) return e;
-  e = ensure_pinned(h, 1);
-  if (e) return e;
   if (!h->pf_buf && hipMalloc((void**)&h->pf_buf, S.bytes) != hipSuccess) {
     h->pf_buf = nullptr;
     return MK_ERR_OOM;
@@ -557,7 +547,6 @@ int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* 
   int e = prefill_batched_args(h, d_ids, n, d_out_first, &S);
   if (e) return e;
   if (S.bytes > kStaticScratchBytes) return MK_ERR_SCRATCH;
-  if (h->pinned_cap < 1) return MK_ERR_STATE;  // mk_create sizes the mirror for at least one id
   uint8_t* buf = scratch_ptr(h->device);
   if (!buf) return MK_ERR_STATE;  // mk_create looks the address up on the handle's device
   return prefill_batched(h, buf, S, d_ids, d_rows, d_pos3, n, d_out_first);
@@ -637,18 +626,24 @@ int mk_read_ids(mk_handle* h, int32_t first, int32_t count, int32_t* host_out) {
   if (!h || !host_out || first < 0 || count < 0) return MK_ERR_ARG;
   int64_t done = 0;
   mk_progress(h, &done);
-  if ((int64_t)first + count > done || first + count > h->pinned_cap) return MK_ERR_ARG;
-  // every entry carries the call that wrote it: an entry still behind the progress word
-  // (the two stores are not ordered on the device) is read again until it arrives
+  if ((int64_t)first + count > done) return MK_ERR_ARG;
+  // every entry carries its call and lap: an entry still behind the progress word (the two
+  // stores are not ordered on the device) is read again until it arrives; one of a later
+  // lap means the ring has already moved past it
   std::atomic_thread_fence(std::memory_order_acquire);
   const volatile unsigned long long* m = h->pinned_ids;
   for (int32_t i = 0; i < count; ++i) {
-    unsigned long long v = m[first + i];
-    for (int spin = 0; (uint32_t)(v >> 32) != h->call_seq; ++spin) {
+    const int32_t s = first + i;
+    const unsigned long long want = mk::ring_entry(h->call_seq, s, 0) >> 18;  // call and lap
+    for (int spin = 0;; ++spin) {
+      const unsigned long long v = m[s & (mk::kIdRing - 1)];
+      if ((v >> 18) == want) {
+        host_out[i] = (int32_t)(v & 0x3ffff);
+        break;
+      }
+      if ((v >> 32) == h->call_seq && (v >> 18) > want) return MK_ERR_OVERRUN;
       if (spin == 10000000) return MK_ERR_TIMEOUT;
-      v = m[first + i];
     }
-    host_out[i] = (int32_t)(uint32_t)v;
   }
   return MK_OK;
 }
@@ -776,6 +771,7 @@ const char* mk_strerror(int code) {
     case MK_ERR_TIMEOUT: return "device wait timed out";
     case MK_ERR_STATE: return "no previous id for feedback decode";
     case MK_ERR_SCRATCH: return "shape needs more scratch than the fixed array holds";
+    case MK_ERR_OVERRUN: return "the id ring moved past ids not yet read";
   }
   return "unknown error";
 }

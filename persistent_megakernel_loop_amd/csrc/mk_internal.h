@@ -70,7 +70,7 @@ struct Params {
   const float* rows;         // [n_pos][H] or NULL
   const int32_t* pos3;       // [n_pos][3] or NULL
   int32_t* out_ids;          // [n_pos - logits_from] or NULL
-  unsigned long long* pinned_ids;  // host-pinned mirror of out_ids, entries (call_seq << 32) | id, or NULL
+  unsigned long long* pinned_ids;  // host-pinned id ring [kIdRing] (ring_entry), or NULL
   unsigned long long* progress;  // host-pinned step counter
   float* dbg_hidden;         // [n_pos][L+1][H] or NULL
   unsigned long long* dbg_trace; // [n_pos][grid][2] or NULL
@@ -81,6 +81,18 @@ struct Params {
   uint32_t call_seq;         // high half of the progress word
   uint32_t spin_limit;       // polls before a wait gives up
 };
+
+// Pinned id ring: the s-th id of a call goes to entry s % kIdRing as
+// (call_seq << 32) | ((s / kIdRing) << 18) | id, so the host tells the entry it waits for
+// from an older one (an earlier call, or an earlier lap of this call) and from a newer lap
+// that has already overwritten it.  Ids are below 2^18 (the vocabulary limit) and slots
+// below 2^26 (the position limit), so the lap fits its 14 bits.
+constexpr int kIdRingLog2 = 12;
+constexpr int kIdRing = 1 << kIdRingLog2;
+__host__ __device__ inline unsigned long long ring_entry(uint32_t call_seq, int slot, int id) {
+  return ((unsigned long long)call_seq << 32) | ((unsigned long long)((uint32_t)slot >> kIdRingLog2) << 18) |
+         (uint32_t)(id & 0x3ffff);
+}
 
 // Tags used by one position: kPhasesPerLayer per layer plus two.  A launch also uses one
 // tag (its first) for the placement check.

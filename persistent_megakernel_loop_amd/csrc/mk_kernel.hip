@@ -1484,15 +1484,16 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
     *out_id = 0x3ffff - (int)(best & 0x3ffffu);
     return true;
   };
-  // position t's id to the outputs and the pinned progress word (workgroup 0 only).  Each
-  // mirror entry carries the call it belongs to, so the host tells an entry that is still
-  // behind the progress word from a stale one and the two stores need no wait between them.
+  // position t's id to the outputs, the pinned id ring and the pinned progress word
+  // (workgroup 0 only).  Each ring entry carries its call and lap, so the host tells an
+  // entry that is still behind the progress word from a stale one and the two stores need
+  // no wait between them.
   auto publish = [&](int t, int id) {
     if (lane == 0) {
       const int slot = t - P.logits_from;
       if (P.out_ids) P.out_ids[slot] = id;
       if (P.pinned_ids)
-        __hip_atomic_store(P.pinned_ids + slot, ((u64)P.call_seq << 32) | (uint32_t)id, __ATOMIC_RELAXED,
+        __hip_atomic_store(P.pinned_ids + (slot & (kIdRing - 1)), ring_entry(P.call_seq, slot, id), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
       __hip_atomic_store(P.progress, ((u64)P.call_seq << 32) | (u64)(slot + 1), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);

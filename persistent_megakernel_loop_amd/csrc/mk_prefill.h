@@ -47,7 +47,7 @@ struct LmArgs {
   int32_t* blk_idx;
   int32_t* out_first;        // [1] device
   int32_t* last_id;          // feedback id for the next decode call
-  unsigned long long* pinned_ids;  // host-pinned mirror, entries (call_seq << 32) | id, or NULL
+  unsigned long long* pinned_ids;  // host-pinned id ring (ring_entry), or NULL
   unsigned long long* progress;  // host-pinned progress word
   uint32_t call_seq;
 };

@@ -821,8 +821,7 @@ __global__ __launch_bounds__(256) void pf_argmax_kernel(LmArgs M, int n_blk) {
     M.out_first[0] = id;
     *M.last_id = id;
     if (M.pinned_ids)
-      __hip_atomic_store(M.pinned_ids, ((unsigned long long)M.call_seq << 32) | (uint32_t)id, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(M.pinned_ids, ring_entry(M.call_seq, 0, id), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __threadfence_system();
     __hip_atomic_store(M.progress, ((unsigned long long)M.call_seq << 32) | 1ull, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_SYSTEM);

@@ -77,7 +77,7 @@ def test_struct_layout_matches_header(tmp_path):
 def test_error_strings(lib):
     codes = header_codes()
     errs = {k: v for k, v in codes.items() if k.startswith("MK_ERR") or k == "MK_OK"}
-    assert errs["MK_OK"] == 0 and len(errs) == 11
+    assert errs["MK_OK"] == 0 and len(errs) == 12
     seen = set()
     for name, code in errs.items():
         s = lib.mk_strerror(code).decode()
