@@ -374,6 +374,7 @@ def main():
         walls.append((time.perf_counter() - w0) * 1e3)
         dec.check()
         launches.append(e0.elapsed_time(e1))
+    ref_ids = out.clone()  # the persistent kernel's ids of the timed workload
     launch_ms = float(np.median(launches))
     wall_ms = float(np.median(walls))
     ms_step = launch_ms / K
@@ -429,30 +430,32 @@ def main():
         ttfc_pp = ttfc_run(False)
         pf_ms = {"batched": prefill_ms(True) if batched_ok else None, "per_position": prefill_ms(False)}
 
-    # launch-per-phase ablation: the same decode steps, each as one launch per phase (the
-    # batched prefill's kernels at one position: input, 9 per layer, LM head, argmax),
-    # after the same prompt; greedy workloads feed each call's id to the next call
+    # launch-per-phase ablation: the same decode steps with the persistent kernel's own phase
+    # bodies, one kernel launch per phase (7 per layer and the LM head; mk_decode_phased),
+    # after the same prompt and on the same inputs; its ids must equal the persistent ones
     ablation = {}
     n_abl = min(args.ablation_steps, K)
-    if P and n_abl > 0 and batched_ok:
+    if P and n_abl > 0 and shape.hidden <= 1024 and batched_ok:
         prepare()
         torch.cuda.synchronize()
+        ids_ab = inp["step_ids"][:n_abl] if inp["step_ids"] is not None else None
+        rows_ab = inp["step_rows"][:n_abl] if inp["step_rows"] is not None else None
+        pos_ab = inp["step_pos3"][:n_abl] if inp["step_pos3"] is not None else None
+        out_ab = torch.empty(n_abl, dtype=torch.int32, device="cuda")
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record(stream)
-        for st in range(n_abl):
-            ids = inp["step_ids"][st:st + 1] if inp["step_ids"] is not None else first
-            rows = inp["step_rows"][st:st + 1] if inp["step_rows"] is not None else None
-            pos3 = inp["step_pos3"][st:st + 1] if inp["step_pos3"] is not None else None
-            dec.prefill(ids, rows, pos3, out=first, batched=True)
+        dec.decode_phased(n_abl, ids_ab, rows_ab, pos_ab, out=out_ab)
         b.record(stream)
         torch.cuda.synchronize()
         host = (time.perf_counter() - t0) * 1e3 / n_abl
         dec.check()
         per = a.elapsed_time(b) / n_abl
+        same = bool(torch.equal(out_ab, ref_ids[:n_abl]))
         ablation = {"ms_per_step": round(per, 4), "host_ms_per_step": round(host, 4),
                     "over_persistent": round(per / ms_step, 2), "steps": n_abl,
-                    "launches_per_step": 9 * shape.n_layers + 3}
+                    "launches_per_step": 7 * shape.n_layers + 1, "ids_equal_persistent": same,
+                    "kernels": "the persistent kernel's phase bodies (mk_decode_phased)"}
 
     # the streaming loop: prompt, then the K frames of one launch handed to the stub codec in
     # chunks of 4 as they are published; talker-only RTF from its clock
@@ -527,7 +530,7 @@ def main():
     # release every device resource before the interpreter exits: the handle (arena, cache,
     # exchange buffers, pinned progress word and id mirror) and every tensor
     dec.close()
-    del dec, inp, kv, out, first, trace
+    del dec, inp, kv, out, first, trace, ref_ids
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

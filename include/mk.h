@@ -181,6 +181,20 @@ int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
               const int32_t* d_pos3, int32_t* d_out_ids);
 
+/* The launch tax, measured (the dev.to article "Porting a 1,200-line persistent CUDA
+ * megakernel to Qwen3-TTS", "What I took away": every kernel launch of a step costs
+ * latency; the theaicatchup article, "Why Does a Single Kernel Even Matter for TTS?":
+ * a normal forward pass launches hundreds of kernels).  mk_decode's computation with
+ * the persistent kernel's own phase bodies (same grid, tiles, LDS copies, arithmetic
+ * and exchange buffers), but one kernel launch per phase: 7 per layer and one for the
+ * LM head per step (197 at 28 layers), each launch reading the words the one before
+ * published.  Same arguments and results as mk_decode, bit for bit (ids, cache,
+ * hidden states); the barrier trace and phase timeline are not written.  Measurement
+ * only.  MK_ERR_UNSUPPORTED for any body other than the hidden-1024 bf16 one; other
+ * errors as mk_decode.  Stream-ordered on the handle's stream. */
+int mk_decode_phased(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
+                     const int32_t* d_pos3, int32_t* d_out_ids);
+
 /* A cache that already holds n_pos positions: the conversation history a later decode
  * attends over (the dev.to article, "The idea: one kernel that never exits": attention at
  * each step reads every cached position; the long-context workloads start from such a

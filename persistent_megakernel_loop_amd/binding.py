@@ -18,7 +18,7 @@ _LIB_NAME = "libmk.so"
 MK_F32, MK_BF16 = 0, 1
 MK_ERR_OVERRUN = -11
 
-EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_prefill_batched_noalloc", "mk_decode", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
+EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_prefill_batched_noalloc", "mk_decode", "mk_decode_phased", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
            "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
@@ -69,6 +69,7 @@ def lib():
     L.mk_prefill_batched.argtypes = [vp, vp, vp, vp, i32, vp]
     L.mk_prefill_batched_noalloc.argtypes = [vp, vp, vp, vp, i32, vp]
     L.mk_decode.argtypes = [vp, i32, vp, vp, vp, vp]
+    L.mk_decode_phased.argtypes = [vp, i32, vp, vp, vp, vp]
     L.mk_load_kv.argtypes = [vp, vp, i32]
     L.mk_reset.argtypes = [vp]
     L.mk_position.argtypes = [vp, pi32]
@@ -213,6 +214,14 @@ class Decoder:
         if out is None:
             out = self._empty(n_steps, device if ids is None else ids.device)
         _check(lib().mk_decode(self.handle, n_steps, _ptr(ids), _ptr(rows), _ptr(pos3), _ptr(out)), "mk_decode")
+        return out
+
+    def decode_phased(self, n_steps: int, ids=None, rows=None, pos3=None, out=None, device="cuda"):
+        """mk_decode_phased: decode's computation, one kernel launch per phase (measurement)."""
+        if out is None:
+            out = self._empty(n_steps, device if ids is None else ids.device)
+        _check(lib().mk_decode_phased(self.handle, n_steps, _ptr(ids), _ptr(rows), _ptr(pos3), _ptr(out)),
+               "mk_decode_phased")
         return out
 
     def load_kv(self, kv, n_pos: int):

@@ -212,7 +212,7 @@ int device_status(mk_handle* h, bool clear) {
 }
 
 int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const int32_t* pos3, int32_t* out,
-        int logits_from, int feedback, bool prompt) {
+        int logits_from, int feedback, bool prompt, bool phased = false) {
   if (n <= 0) return MK_ERR_ARG;
   if ((long long)h->pos + n > h->cfg.max_seq) return MK_ERR_CAPACITY;
   if (feedback && !h->have_last) return MK_ERR_STATE;
@@ -268,7 +268,13 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.tag0 = h->tag;
   P.lm_seq0 = h->lm_seq;
   P.spin_limit = h->spin_limit;
-  if (mk::launch_decode(h->body, P, prompt, h->stream)) return MK_ERR_HIP;
+  if (phased) {
+    const int e = mk::launch_phased(h->body, P, h->stream);
+    if (e == -2) return MK_ERR_UNSUPPORTED;
+    if (e) return MK_ERR_HIP;
+  } else if (mk::launch_decode(h->body, P, prompt, h->stream)) {
+    return MK_ERR_HIP;
+  }
   h->tag += need;
   h->lm_seq = (h->lm_seq + (uint32_t)(n - logits_from)) & 0x3fffu;
   h->pos += n;
@@ -556,6 +562,13 @@ int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* 
               int32_t* d_out_ids) {
   if (!h || n_steps <= 0 || !d_out_ids) return MK_ERR_ARG;
   return run(h, n_steps, d_ids, d_embed_buf, d_pos3, d_out_ids, 0, d_ids == nullptr, false);
+}
+
+int mk_decode_phased(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf,
+                     const int32_t* d_pos3, int32_t* d_out_ids) {
+  if (!h || n_steps <= 0 || !d_out_ids) return MK_ERR_ARG;
+  if (h->body != mk::BODY_Q06) return MK_ERR_UNSUPPORTED;
+  return run(h, n_steps, d_ids, d_embed_buf, d_pos3, d_out_ids, 0, d_ids == nullptr, false, true);
 }
 
 int mk_load_kv(mk_handle* h, const void* d_kv, int32_t n_pos) {

@@ -102,6 +102,9 @@ __host__ __device__ inline uint32_t tags_per_position(int n_layers) { return (ui
 // Host-side launcher implemented next to the kernel.
 int launch_decode(int body, const Params& p, bool prompt, void* stream);  // prompt: prefill_kernel
 int coop_ok(int body, int* blocks_per_cu);
+// The same decode as launch_decode, one kernel launch per phase (measurement only).  -2:
+// the body or call has no phased form.
+int launch_phased(int body, const Params& p, void* stream);
 int launch_embed_sum(const void* codebooks, int n_cb, int cb_size, const void* text, int text_vocab,
                      int hidden, int bf16, const int32_t* ids, int n, float* rows, int32_t* bad, void* stream);
 int launch_widen(const void* src, float* dst, int n, int bf16, void* stream);

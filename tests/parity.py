@@ -59,7 +59,8 @@ class GpuRun:
     trace: Optional[np.ndarray] = None
 
 
-def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batched: bool = False) -> GpuRun:
+def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batched: bool = False,
+            phased: bool = False) -> GpuRun:
     import torch
     from persistent_megakernel_loop_amd.binding import Decoder, to_device
 
@@ -82,7 +83,7 @@ def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batc
         dec.check()
         first = int(out.cpu()[0])
     dec.set_debug(hid[P:], tr)
-    ids = dec.decode(n, t(inp.step_ids), t(inp.step_rows), t(inp.step_pos3))
+    ids = (dec.decode_phased if phased else dec.decode)(n, t(inp.step_ids), t(inp.step_rows), t(inp.step_pos3))
     dec.check()
     torch.cuda.synchronize()
     res = GpuRun(first, ids.cpu().numpy().astype(np.int32), hid.cpu().numpy(),
