@@ -345,7 +345,6 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       }
       mark(1);
       wsync();
-      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);  // slot A is free
       if (gather(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
                  r * B::T_QKV, (r + 1) * B::T_QKV)) {
         if constexpr (B::BF16) qk_part<B>(S, S.G[gc & 1] + B::H, S.G[gc & 1] + B::H + B::D, P.rms_eps, P.kv_bf16, wave, lane);
@@ -353,8 +352,11 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       wsync();  // q rotated, k/v of position p in LDS
       if (S.abort_) return;
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
-      // attention over the chunk (its cache rows were loaded at the start of the layer; a
-      // copy issued before it would be waited for with them)
+      // gate/up part 0 (slot A is free): issued after the q/k/v gather rather than ahead of
+      // it, where it held back that gather's polls in this CU's memory queue (measured: 1 %
+      // per step); the copy waves' attention shares end by waiting for it
+      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);
+      // attention over the chunk (its cache rows were loaded at the start of the layer)
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
       wsync();
