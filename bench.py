@@ -187,7 +187,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 # The decode kernel's sources: its code and the parameter block the host fills in.
-DECODE_SOURCES = ("mk_internal.h", "mk_device.h", "mk_kernel.hip")
+DECODE_SOURCES = ("mk_internal.h", "mk_device.h", "mk_body.h", "mk_kernel.hip")
 
 
 def csrc_digest() -> str:
