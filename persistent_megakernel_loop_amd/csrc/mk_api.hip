@@ -268,6 +268,7 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
   P.tag0 = h->tag;
   P.lm_seq0 = h->lm_seq;
   P.spin_limit = h->spin_limit;
+  P.whole = mk::whole_call(h->body, h->pos, n) ? 1 : 0;
   if (phased) {
     const int e = mk::launch_phased(h->body, P, h->stream);
     if (e == -2) return MK_ERR_UNSUPPORTED;

@@ -80,7 +80,16 @@ struct Params {
   uint32_t lm_seq0;          // argmax key sequence of the first LM head of this launch (14 bits used)
   uint32_t call_seq;         // high half of the progress word
   uint32_t spin_limit;       // polls before a wait gives up
+  int32_t whole;             // 1: every rank of an XCD runs the whole attention (see whole_call)
 };
+
+// Short contexts: a launch whose positions all lie below kWholeKeys runs, on the
+// hidden-1024 bf16 body, a form of the kernel in which every workgroup of the group's XCD
+// computes the group's whole attention itself (its worker waves share the positions, one
+// 8-position batch each at most), so no chunk partial goes through an exchange.  A
+// separate kernel, so the chunked form's code is untouched.
+constexpr int kWholeKeys = 56;
+inline bool whole_call(int body, int pos0, int n) { return body == BODY_Q06 && pos0 + n <= kWholeKeys; }
 
 // Pinned id ring: the s-th id of a call goes to entry s % kIdRing as
 // (call_seq << 32) | ((s / kIdRing) << 18) | id, so the host tells the entry it waits for

@@ -243,7 +243,7 @@ __device__ __forceinline__ constexpr int dma_part_count(int ni, int nparts, int 
 // slot B the O tile, then down.  Each tile is copied (LDS DMA, all seven worker waves)
 // as soon as its slot is free, two exchanges before its dot product, and every wave
 // confirms its own copies have landed before the barrier that precedes the dot.
-template <class B>
+template <class B, bool WHOLE>
 __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* slotA, u4* slotB, int x, int r, int wave,
                                 int lane) {
   using TQKV = Tile<B, B::T_QKV, B::H>;
@@ -321,11 +321,12 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const uint32_t tg0 = tbase + (uint32_t)l * kPhasesPerLayer;
       const int ln = (l + 1 < L) ? l + 1 : 0;
       const bool lm_now = lm && l + 1 == L;
-      // this rank's chunk of cache positions: its first batch is loaded now
-      const int nc = n_chunks<B>(p);
+      // this rank's chunk of cache positions (all of them in the whole-attention form): its
+      // first batch is loaded now
+      const int nc = WHOLE ? 1 : n_chunks<B>(p);
       const int csz = (p + 1 + nc - 1) / nc;
-      const bool attn = grp && r < nc;
-      const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
+      const bool attn = grp && (WHOLE || r < nc);
+      const int c0 = WHOLE ? 0 : r * csz, c1 = WHOLE ? p + 1 : min(p + 1, r * csz + csz);
       KvBatch<B> kb;
       if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // this layer's O tile, behind the cache rows (slot B has been free since the last
@@ -360,6 +361,16 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
       mark(1);
       wsync();
+      if constexpr (WHOLE) {
+        // the whole attention in this workgroup: the control wave merges the waves' partials
+        // into chunk 0 (no exchange), then every wave takes its share of the output
+        if (wave < kDmaWaves) wait_vmem<0>();  // the O tile and gate/up part 0 have landed
+        mark(0);
+        __syncthreads();
+        dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
+        dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 2, wave, lane);
+        if (grp) combine_part<B>(S, 1, wave, lane);
+      } else
       // the attention chunks, polled by every wave: no copy in flight (the O tile and gate/up
       // part 0 have landed), then the copy waves issue gate/up parts 1 and 2
       {
@@ -438,7 +449,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
 }
 
 // ------------------------------------------------------------------ control wave
-template <class B>
+template <class B, bool WHOLE>
 __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u4* slotA, const u4* slotB, int x, int r,
                                              int lane) {
   const TileAddr<B> A{P, x, r};
@@ -673,7 +684,28 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       if (!sync()) return;
       // ------------------------------------------------------------ attention combine
       if (!sync()) return;
-      {
+      if constexpr (WHOLE) {
+        // every rank ran the whole attention: its waves' partials merged are the result
+        float cM[B::QPG], cL[B::QPG], ca[B::QPG][B::DPL];
+#pragma unroll
+        for (int h = 0; h < B::QPG; ++h) {
+          cM[h] = cL[h] = 0.f;
+#pragma unroll
+          for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
+        }
+        if (grp) merge_wave_partials<B>(S, lane, cM, cL, ca);
+#pragma unroll
+        for (int h = 0; h < B::QPG; ++h) {
+#pragma unroll
+          for (int k = 0; k < B::DPL; ++k) S.part[0][h][2 + lane + 64 * k] = ca[h][k];
+          if (lane == 0) {
+            S.part[0][h][0] = cM[h];
+            S.part[0][h][1] = cL[h];
+          }
+        }
+        __syncthreads();
+        if (grp) combine_part<B>(S, 1, kWorkerWaves, lane);
+      } else {
         const int nc = n_chunks<B>(p);
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
         // this rank's chunk partial: the worker waves' partials merged in a fixed order
@@ -856,7 +888,7 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
   }
 }
 
-template <class B>
+template <class B, bool WHOLE>
 __device__ __forceinline__ void persistent_body(const Params& P) {
   __shared__ __align__(16) u4 slotA[slot_a_bytes<B>() / 16];
   __shared__ __align__(16) u4 slotB[slot_b_bytes<B>() / 16];
@@ -864,24 +896,28 @@ __device__ __forceinline__ void persistent_body(const Params& P) {
   const int b = blockIdx.x, x = b % kXcds, r = b / kXcds;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x == 0) S.abort_ = 0;
-  if (wave == kWorkerWaves) control_loop<B>(P, S, slotA, slotB, x, r, lane);
-  else if constexpr (lds_tiles<B>()) worker_loop_lds<B>(P, S, slotA, slotB, x, r, wave, lane);
+  if (wave == kWorkerWaves) control_loop<B, WHOLE>(P, S, slotA, slotB, x, r, lane);
+  else if constexpr (lds_tiles<B>()) worker_loop_lds<B, WHOLE>(P, S, slotA, slotB, x, r, wave, lane);
   else worker_loop_regs<B>(P, S, x, r, wave, lane);
 }
 
 // The same persistent body under two names, so that a profile tells decode launches
 // (the LM head at every step) from prompt launches (the LM head at the last position).
+template <class B, bool WHOLE>
+__global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) { persistent_body<B, WHOLE>(P); }
+template <class B, bool WHOLE>
+__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(Params P) { persistent_body<B, WHOLE>(P); }
+
+// Bodies with a whole-attention form (whole_call).
 template <class B>
-__global__ void __launch_bounds__(kThreads, 1) decode_kernel(Params P) { persistent_body<B>(P); }
-template <class B>
-__global__ void __launch_bounds__(kThreads, 1) prefill_kernel(Params P) { persistent_body<B>(P); }
+constexpr bool has_whole() { return lds_tiles<B>() && B::BF16 && B::D == 128; }
 
 // Dynamic LDS added to the kernel's static LDS so that a workgroup takes more than half
 // of a CU's 160 KB: the grid then places exactly one workgroup on each CU.
 template <class B>
 static int lds_padding() {
   hipFuncAttributes a;
-  if (hipFuncGetAttributes(&a, (const void*)decode_kernel<B>) != hipSuccess) return -1;
+  if (hipFuncGetAttributes(&a, (const void*)decode_kernel<B, false>) != hipSuccess) return -1;
   const int need = 80 * 1024 + 1024 - (int)a.sharedSizeBytes;
   return need > 0 ? need : 0;
 }
@@ -892,7 +928,12 @@ static int launch_t(const Params& p, bool prompt, void* stream) {
   void* args[] = {&pp};
   const int pad = lds_padding<B>();
   if (pad < 0) return -1;
-  const void* fn = prompt ? (const void*)prefill_kernel<B> : (const void*)decode_kernel<B>;
+  const void* fn = prompt ? (const void*)prefill_kernel<B, false> : (const void*)decode_kernel<B, false>;
+  if constexpr (has_whole<B>()) {
+    if (p.whole) fn = prompt ? (const void*)prefill_kernel<B, true> : (const void*)decode_kernel<B, true>;
+  } else if (p.whole) {
+    return -1;
+  }
   hipError_t e = hipLaunchCooperativeKernel(fn, dim3(kGrid), dim3(kThreads), args, (unsigned)pad, (hipStream_t)stream);
   return e == hipSuccess ? 0 : -1;
 }
@@ -901,13 +942,20 @@ template <class B>
 static int coop_t(int* blocks) {
   const int pad = lds_padding<B>();
   if (pad < 0) return -1;
-  int nb[2] = {0, 0};
-  const void* fns[2] = {(const void*)decode_kernel<B>, (const void*)prefill_kernel<B>};
-  for (int k = 0; k < 2; ++k) {
+  int nb[4] = {0, 0, 0, 0};
+  const void* fns[4] = {(const void*)decode_kernel<B, false>, (const void*)prefill_kernel<B, false>, nullptr, nullptr};
+  if constexpr (has_whole<B>()) {
+    fns[2] = (const void*)decode_kernel<B, true>;
+    fns[3] = (const void*)prefill_kernel<B, true>;
+  }
+  int best = 1 << 30;
+  for (int k = 0; k < 4; ++k) {
+    if (!fns[k]) continue;
     if (pad > 0 && hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, pad) != hipSuccess) return -1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb[k], fns[k], kThreads, pad) != hipSuccess) return -1;
+    best = nb[k] < best ? nb[k] : best;
   }
-  *blocks = nb[0] < nb[1] ? nb[0] : nb[1];
+  *blocks = best;
   return 0;
 }
 

@@ -154,7 +154,9 @@ __global__ void __launch_bounds__(kThreads, 1) phase_kernel(Params P, int t, int
       qk_part<B>(S, S.G[0] + B::H, S.G[0] + B::H + B::D, eps, P.kv_bf16, wave, lane);
       __syncthreads();
       if (r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
-      const int nc = n_chunks<B>(p);
+      // the whole-attention form (P.whole): every rank of the persistent kernel runs all the
+      // positions; rank 0 does it here and publishes it as the one chunk
+      const int nc = P.whole ? 1 : n_chunks<B>(p);
       const int csz = (p + 1 + nc - 1) / nc;
       const bool attn = r < nc;
       const int c0 = r * csz, c1 = min(p + 1, r * csz + csz);
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(kThreads, 1) phase_kernel(Params P, int t, int
       break;
     }
     case PH_O: {
-      const int nc = n_chunks<B>(p);
+      const int nc = P.whole ? 1 : n_chunks<B>(p);
       copy_tile<TO::TOTAL>(A.o(l), slotB, wave, lane);
       if (!gather_all<NC>(P, S, P.xatt + (size_t)x * NC, nc * B::QPG * (B::D + 2), tg0 + 1, pp, wave, lane)) return;
       combine_part<B>(S, nc, wave, lane);

@@ -146,3 +146,28 @@ def test_seeded_shape_sweep(name, prompt_len, kv_prefill, n_steps, batched):
     inp = make_inputs(shape)
     gpu = run_gpu(shape, weights_to_device(weights), inp, batched=batched)
     print(f"[case] {name}: {compare(gpu, run_oracle(shape, weights, inp, gpu))}", flush=True)
+
+
+def test_whole_attention_form_equals_chunked_below_56():
+    """A decode launch whose positions all lie below 56 runs the whole-attention form of
+    the hidden-1024 body (every workgroup of an XCD computes the group's attention; no
+    chunk exchange).  Below 56 positions the chunked form has exactly one chunk, so both
+    forms compute the same sums in the same order: the first 20 steps of a 30-step launch
+    (which crosses 56 and runs the chunked form) must equal a 20-step launch (the whole
+    form) bit for bit, ids and every layer's hidden state; both follow the oracle."""
+    from persistent_megakernel_loop_amd.binding import weights_to_device
+
+    shape = wl.TALKER_0P6B.replace(name="talker-2l-whole", n_layers=2, prompt_len=32, steps=30)
+    print(f"[case] {shape.name}: 20 steps (whole-attention form) against the first 20 of 30 (chunked)", flush=True)
+    weights = wl.make_weights(shape)
+    dw = weights_to_device(weights)
+    inp = make_inputs(shape)
+    chunked = run_gpu(shape, dw, inp)
+    short = inp.__class__(**{**inp.__dict__, "step_ids": inp.step_ids[:20], "step_rows": inp.step_rows[:20],
+                             "step_pos3": inp.step_pos3[:20], "n_steps": 20})
+    whole = run_gpu(shape, dw, short)
+    del dw
+    assert np.array_equal(whole.ids, chunked.ids[:20])
+    assert np.array_equal(whole.hidden.view(np.uint32), chunked.hidden[:32 + 20].view(np.uint32))
+    summary = compare(chunked, run_oracle(shape, weights, inp, chunked))
+    print(f"[case] {shape.name}: {summary}", flush=True)
