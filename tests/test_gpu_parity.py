@@ -118,8 +118,10 @@ def test_full_talker_long_context():
 
 
 def test_full_talker_1p7b():
-    """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions: one launch of 12 steps."""
-    _case(wl.TALKER_1P7B, n_steps=12)
+    """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions: one launch of 64
+    steps, every step's id and every layer's hidden state against the oracle."""
+    _, summary = _case(wl.TALKER_1P7B, n_steps=64)
+    assert summary["ids_checked"] == 64
 
 
 def _sweep_cases():
