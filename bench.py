@@ -203,24 +203,33 @@ def csrc_digest() -> str:
     return h.hexdigest()
 
 
-def counters_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"decode_kernel_{workload}_hbm_counters.txt")
+def counters_path(workload: str, steps: int = 256) -> str:
+    """The counter summary of one launch of `steps` steps (256: the default run)."""
+    tail = "" if steps == 256 else f"_{steps}steps"
+    return os.path.join(PROFILES, f"decode_kernel_{workload}{tail}_hbm_counters.txt")
 
 
-def load_traffic(workload: str, steps: int, algo: int):
-    """HBM bytes per decode launch from the committed counter summary, with where they come
-    from: the measured bytes when the counters were taken at this step count, else the
-    measured ratio of HBM bytes to algorithmic bytes times this launch's algorithmic bytes.
-    (None, reason) when the summary is absent or the kernel sources changed since."""
-    path = counters_path(workload)
-    if not os.path.exists(path):
-        return None, "no counter summary"
+def _read_counters(path: str) -> dict:
     kv = {}
     with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.split()[0] if v.split() else ""
+    return kv
+
+
+def load_traffic(workload: str, steps: int, algo: int):
+    """HBM bytes per decode launch from the committed counter summaries, with where they
+    come from: the measured bytes when counters were taken at this step count, else the
+    measured ratio of HBM bytes to algorithmic bytes of the default (256-step) run times
+    this launch's algorithmic bytes.  (None, reason) when no summary applies or the kernel
+    sources changed since."""
+    exact = counters_path(workload, steps)
+    path = exact if os.path.exists(exact) else counters_path(workload)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    kv = _read_counters(path)
     if kv.get("csrc_sha256") != csrc_digest():
         return None, "kernel sources changed since the counters were taken"
     if kv.get("steps") == str(steps):
@@ -236,30 +245,34 @@ def _pmc_mean(csv_path: str, prefix: str):
     return (sum(vals) / len(vals), vals) if vals else (None, vals)
 
 
-def hbm_summary(outdir: str, workload: str, steps: int, copy_mib: int) -> str:
-    """Summary text of the four counter passes under outdir (decode launches and a plain copy, FETCH_SIZE
-    and WRITE_SIZE in KiB per dispatch): each decode figure is scaled by known/measured of the copy."""
+def hbm_summary(outdir: str, workload: str, steps: int, copy_mib: int, copy_dir: str = "", warmup: int = 2) -> str:
+    """Summary text of the four counter passes (decode launches under outdir, a plain copy
+    under copy_dir or outdir; FETCH_SIZE and WRITE_SIZE in KiB per dispatch): each decode
+    figure is scaled by known/measured of the copy."""
+    copy_dir = copy_dir or outdir
     copy_kib = copy_mib * 1024
     f_dec, f_all = _pmc_mean(os.path.join(outdir, "pmc_FETCH_SIZE", "p_counter_collection.csv"), "void mk::decode_kernel")
     w_dec, w_all = _pmc_mean(os.path.join(outdir, "pmc_WRITE_SIZE", "p_counter_collection.csv"), "void mk::decode_kernel")
-    f_cp, _ = _pmc_mean(os.path.join(outdir, "pmccopy_FETCH_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
-    w_cp, _ = _pmc_mean(os.path.join(outdir, "pmccopy_WRITE_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    f_cp, _ = _pmc_mean(os.path.join(copy_dir, "pmccopy_FETCH_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    w_cp, _ = _pmc_mean(os.path.join(copy_dir, "pmccopy_WRITE_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
     fs, ws = copy_kib / f_cp, copy_kib / w_cp
     fetch_b, write_b = f_dec * fs * 1024, w_dec * ws * 1024
     shape = wl.BY_NAME[workload]
     algo = step_bytes(shape, shape.kv_prefill + shape.prompt_len, steps)
     base = "--ttfc-trials 0 --ablation-steps 0 --no-ceiling --no-cpu-baseline" + (
         "" if workload == "talker-0.6b" else f" --workload {workload}")
-    if steps != 256:
-        base += f" --steps {steps}"
+    if steps != 256 or warmup != 2:
+        base = f"--steps {steps} --warmup {warmup} " + base
     lines = [
         f"# HBM counters of decode_kernel on {workload}: one launch of {steps} decode steps after the prompt",
         "# commands (repository root, TMPDIR=/tmp), one counter per pass:",
         f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir}/pmc_FETCH_SIZE -o p --output-format csv -- python3 bench.py {base}",
         f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir}/pmc_WRITE_SIZE -o p --output-format csv -- python3 bench.py {base}",
-        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir}/pmccopy_FETCH_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
-        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir}/pmccopy_WRITE_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
-        f"# summarised by: python3 bench.py --hbm-summary {outdir}" + ("" if workload == "talker-0.6b" else f" --workload {workload}"),
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {copy_dir}/pmccopy_FETCH_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {copy_dir}/pmccopy_WRITE_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"# summarised by: python3 bench.py --hbm-summary {outdir}" + ("" if workload == "talker-0.6b" else f" --workload {workload}")
+        + ("" if copy_dir == outdir else f" --copy-dir {copy_dir}") + ("" if steps == 256 else f" --steps {steps}")
+        + ("" if warmup == 2 else f" --warmup {warmup}"),
         f"workload: {workload}",
         f"steps: {steps}",
         f"csrc_sha256: {csrc_digest()}",
@@ -291,11 +304,13 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 3 times (known bytes for scaling HBM counters) and exit")
     ap.add_argument("--hbm-summary", metavar="DIR", help="only print the HBM counter summary of the passes under DIR")
+    ap.add_argument("--copy-dir", default="", metavar="DIR",
+                    help="with --hbm-summary: where the copy-calibration passes are (default: DIR)")
     ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
                     help="only run the workload's prompt N times through the batched prefill (for profiling) and exit")
     args = ap.parse_args()
     if args.hbm_summary:
-        sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024))
+        sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024, args.copy_dir, args.warmup))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
