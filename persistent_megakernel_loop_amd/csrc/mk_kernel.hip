@@ -407,7 +407,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (wave < kDmaWaves) wait_vmem_rt(dma_part_count(NI_D, 2, 0, wave));  // gate/up tile landed
       gather(true, std::integral_constant<int, B::H>{}, P.xxa + (size_t)x * B::H, B::H, tg0 + 3, S.xs, r * B::T_O,
              (r + 1) * B::T_O);
-      wsync();  // residual after attention, normalised
+      if constexpr (B::BF16) ++ph;  // residual after attention: the gather's barrier is the only one
+      else wsync();               // (the fp32 body's control wave normalises after the gather)
       if (S.abort_) return;
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
       // the next layer's gains: their buffer held those of the layer before this one, last
@@ -421,7 +422,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (wave < kDmaWaves) wait_vmem_rt(dma_count(NI_GA, wave));  // down tile landed
       gather(true, std::integral_constant<int, B::IX>{}, P.xm + (size_t)x * B::IX, B::IX, tg0 + 4, S.mv,
              r * (B::T_GU / 2), (r + 1) * (B::T_GU / 2));
-      wsync();  // SwiGLU slice of the XCD
+      if constexpr (B::BF16) ++ph;  // SwiGLU slice of the XCD: the gather's barrier is the only one
+      else wsync();
       if (S.abort_) return;
       dma_copy<TQKV::TOTAL>(A.qkv(ln), slotA, wave, lane);  // the next q/k/v tile: slot A is free
       // down partial (slot B)
@@ -433,7 +435,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (!lm_now && wave < kDmaWaves) wait_vmem<0>();  // next gains and q/k/v tile landed
       gather(true, std::integral_constant<int, B::H>{}, P.xxb + (size_t)x * B::H, B::H, tg0 + 6, S.xs, r * B::T_D,
              (r + 1) * B::T_D);
-      wsync();  // residual after the MLP, normalised for the next layer or the head
+      // residual after the MLP; after the last layer a second barrier publishes the control
+      // wave's final norm to the LM head
+      if (!B::BF16 || l + 1 == L) wsync();
+      else ++ph;
       if (!lm && l + 1 == L) dma_copy<TO::TOTAL>(A.o(0), slotB, wave, lane);  // the next position's layer 0
       ++gc;
       if (S.abort_) return;
@@ -809,7 +814,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
           }
         }
       }
-      if (!sync()) return;
+      if constexpr (kDots) {  // nothing since the gather's barrier: no second one
+        ++ph;
+        n_marks = 0;
+        if (S.abort_) return;
+      } else if (!sync()) {
+        return;
+      }
       // ------------------------------------------------------------ SwiGLU slice
       if constexpr (kDots) tile_dot2<B::T_GU, B::H, In::kF32Norm>(slotA, S.xs, S.G[gc & 1], eps, S.res, kWorkerWaves, lane);
       if (!sync()) return;
@@ -826,7 +837,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
                          if (lane < HALF) S.mv[r * HALF + lane] = mm;
                        });
       }
-      if (!sync()) return;
+      if constexpr (kDots) {  // nothing since the gather's barrier: no second one
+        ++ph;
+        n_marks = 0;
+        if (S.abort_) return;
+      } else if (!sync()) {
+        return;
+      }
       // ------------------------------------------------------------ down partials -> residual
       if constexpr (kDots) tile_dot2<B::T_D, B::IX, In::kF32>(slotB, S.mv, nullptr, 0.f, S.res, kWorkerWaves, lane);
       if (!sync()) return;
@@ -863,7 +880,13 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
         }
       }
       ++gc;
-      if (!sync()) return;
+      if (!kDots || l + 1 == L) {
+        if (!sync()) return;
+      } else {  // nothing since the gather's barrier: no second one
+        ++ph;
+        n_marks = 0;
+        if (S.abort_) return;
+      }
     }  // layers
 
     // ---------------------------------------------------------------- argmax key of this workgroup
