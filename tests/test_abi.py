@@ -165,6 +165,7 @@ def test_null_handle_calls(lib):
     assert lib.mk_read_ids(None, 0, 1, (ctypes.c_int32 * 1)()) == -1
     assert lib.mk_query(None, ctypes.byref(ctypes.c_int32())) == -1
     assert lib.mk_decode(None, 4, None, None, None, 0x20) == -1
+    assert lib.mk_decode_phased(None, 4, None, None, None, 0x20) == -1
     assert lib.mk_load_kv(None, 0x10, 4) == -1
     assert lib.mk_reset(None) == -1
     assert lib.mk_position(None, ctypes.byref(i32)) == -1
