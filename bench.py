@@ -313,7 +313,7 @@ def main():
         sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024, args.copy_dir, args.warmup))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the decode path runs on a single MI355X; "
+        print(json.dumps({"error": "one GPU only: the decode path runs on a single MI355X; "
                                    "run with --gpus 1"}))
         sys.exit(2)
 
