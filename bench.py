@@ -517,11 +517,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": shape.weight_dtype,
         "data": "synthetic",
         "config": {"workload": shape.name, "layers": shape.n_layers, "hidden": shape.hidden, "vocab": shape.vocab,
                    "prompt_positions": P, "kv_prefill": shape.kv_prefill, "decode_steps": K, "batch": 1,
-                   "weights": "bf16 N(0,0.02) random", "kv_cache": shape.kv_dtype,
+                   "weights": f"{shape.weight_dtype} N(0,0.02) random", "kv_cache": shape.kv_dtype,
                    "launches_timed": args.repeats, "reported": "median launch"},
         "hbm_gbps": round(gbps, 1),
         "hbm_frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
