@@ -127,13 +127,15 @@ int mk_create(const mk_weights* w, const mk_cfg* cfg, void* stream, mk_handle** 
 int mk_prefill(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
                int32_t n, int32_t* d_out_first);
 
-/* Same contract and arguments as mk_prefill, with the prompt run as a batch through
- * ordinary per-layer kernels instead of the persistent kernel: up to 64 positions per
- * pass over the weights (matrix-core products over the packed weight tiles, causal
- * attention over the cache, the cache written as mk_prefill writes it), then the LM
- * head over the last position and its greedy id (ties: lowest index), published as
- * mk_prefill publishes it (d_out_first[0], the feedback id, the pinned id ring and the
- * progress word).  The time to the first id is where per-position work costs most
+/* Same contract and arguments as mk_prefill, with the prompt run as a batch: up to 64
+ * positions per pass over the weights (matrix-core products over the packed weight
+ * tiles, causal attention over the cache, the cache written as mk_prefill writes it),
+ * then the LM head over the last position and its greedy id (ties: lowest index),
+ * published as mk_prefill publishes it (d_out_first[0], the feedback id, the pinned id
+ * ring and the progress word).  A chunk of positions runs in one of two forms (see
+ * mk_set_prefill_path): one persistent launch for all layers, whose phases hand over
+ * through flagged buffers (hidden 1024 with intermediate 3072, contexts up to 2048
+ * positions), or a chain of ordinary per-layer kernels (every supported shape).  The time to the first id is where per-position work costs most
  * (the dev.to article "Porting a 1200-line persistent CUDA megakernel to Qwen3-TTS",
  * "Making it talk end-to-end"), and a batch is the case a one-position-per-pass
  * persistent loop does not serve well (same article, "What I took away").  Results
@@ -236,6 +238,18 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
  * workgroup: d_phase is then [n][grid][2 + 10*n_layers][8].
  * MK_ERR_ARG if wg is not in [-1, grid). */
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
+
+/* Which form mk_prefill_batched and mk_prefill_batched_noalloc run a call in:
+ *   MK_PREFILL_AUTO        the persistent form where the call has it, else the chain;
+ *   MK_PREFILL_CHAIN       the per-layer kernel chain;
+ *   MK_PREFILL_PERSISTENT  the persistent form; calls without it (another shape, or a
+ *                          context past 2048 positions) return MK_ERR_UNSUPPORTED.
+ * Both forms compute the same sums in different rounding orders.  MK_ERR_ARG for a NULL
+ * handle or another value. */
+#define MK_PREFILL_AUTO 0
+#define MK_PREFILL_CHAIN 1
+#define MK_PREFILL_PERSISTENT 2
+int mk_set_prefill_path(mk_handle* h, int32_t path);
 
 /* Poll rounds after which a wait for other workgroups' words gives up, for the following
  * prefill/decode calls (polls == 0 restores the default, 2^22, about a second).  A wait

@@ -17,9 +17,10 @@ _LIB_NAME = "libmk.so"
 
 MK_F32, MK_BF16 = 0, 1
 MK_ERR_OVERRUN = -11
+PREFILL_AUTO, PREFILL_CHAIN, PREFILL_PERSISTENT = 0, 1, 2  # mk_set_prefill_path
 
 EXPORTS = ("mk_create", "mk_prefill", "mk_prefill_batched", "mk_prefill_batched_noalloc", "mk_decode", "mk_decode_phased", "mk_load_kv", "mk_reset", "mk_position", "mk_set_debug",
-           "mk_set_phase_trace", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
+           "mk_set_phase_trace", "mk_set_prefill_path", "mk_set_spin_limit", "mk_progress", "mk_read_ids", "mk_query", "mk_status", "mk_error_info", "mk_selftest_lds_dma", "mk_selftest_gemm", "mk_selftest_exchange", "mk_bench_stream_read", "mk_grid_size",
            "mk_embed_sum", "mk_strerror", "mk_destroy")
 
 
@@ -76,6 +77,7 @@ def lib():
     L.mk_set_debug.argtypes = [vp, vp, vp]
     L.mk_set_phase_trace.argtypes = [vp, vp, i32]
     L.mk_set_spin_limit.argtypes = [vp, ctypes.c_uint32]
+    L.mk_set_prefill_path.argtypes = [vp, i32]
     L.mk_progress.argtypes = [vp, ctypes.POINTER(ctypes.c_int64)]
     L.mk_read_ids.argtypes = [vp, i32, i32, pi32]
     L.mk_query.argtypes = [vp, pi32]
@@ -244,6 +246,10 @@ class Decoder:
 
     def set_spin_limit(self, polls: int = 0):
         _check(lib().mk_set_spin_limit(self.handle, polls), "mk_set_spin_limit")
+
+    def set_prefill_path(self, path: int = 0):
+        """PREFILL_AUTO, PREFILL_CHAIN or PREFILL_PERSISTENT (mk_set_prefill_path)."""
+        _check(lib().mk_set_prefill_path(self.handle, path), "mk_set_prefill_path")
 
     def progress(self) -> int:
         v = ctypes.c_int64()

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmk.so")
-SOURCES = ["mk_kernel.hip", "mk_phased.hip", "mk_aux.hip", "mk_prefill.hip", "mk_bench.hip", "mk_api.hip"]
+SOURCES = ["mk_kernel.hip", "mk_phased.hip", "mk_aux.hip", "mk_prefill.hip", "mk_pprefill.hip", "mk_bench.hip", "mk_api.hip"]
 ARCH = "gfx950"
 
 

@@ -64,6 +64,8 @@ struct mk_handle {
   uint32_t spin_limit = kDefaultSpinLimit;
   // batched prefill scratch, allocated by the first mk_prefill_batched call
   uint8_t* pf_buf = nullptr;
+  uint32_t pf_tag = 1;   // next flag tag of the persistent prefill on pf_buf
+  int32_t pf_path = 0;   // MK_PREFILL_AUTO / _CHAIN / _PERSISTENT
 };
 
 namespace {
@@ -287,7 +289,11 @@ int run(mk_handle* h, int32_t n, const int32_t* ids, const float* rows, const in
 // Byte offsets of the batched prefill's scratch regions (activations, their bf16 split,
 // queries, sums of squares, LM-head block maxima, attention and product partials) for a
 // handle's shape; `bytes` is the whole.  0 bytes: the shape is not supported.
-struct PfScratch { size_t x, xs, q, ss, blk_val, blk_idx, att, part, bytes; };
+// The persistent form's regions (pp[1..9], after its flag words pp[0]) overlay the
+// chain's (xs .. part): a chunk runs one form or the other.  The flag words come first
+// and nothing else is ever written there, and x, which the LM head reads after either
+// form, lies outside the overlay.
+struct PfScratch { size_t flags, x, blk_val, blk_idx, xs, q, ss, att, part, pp[10], bytes; bool pp_ok; };
 
 PfScratch pf_scratch(const mk_cfg* c) {
   PfScratch r{};
@@ -300,14 +306,24 @@ PfScratch pf_scratch(const mk_cfg* c) {
   const size_t n_blk = (size_t)(c->vocab + mk::kLmRowsPerBlock - 1) / mk::kLmRowsPerBlock;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += align_up(bytes, 256); return at; };
+  size_t pp[10];
+  const size_t pp_total = mk::pp_layout(c->hidden, c->n_q_heads, c->n_kv_heads, c->head_dim, c->intermediate, pp);
+  r.pp_ok = pp_total > 0;
+  r.flags = take((size_t)mk::kPpKinds * mk::kGrid * 8);
   r.x = take(ch * H * 4);
+  r.blk_val = take(n_blk * 4);
+  r.blk_idx = take(n_blk * 4);
+  const size_t overlay = off;
   r.xs = take(2 * K * ch * 2);
   r.q = take(ch * c->n_q_heads * c->head_dim * 4);
   r.ss = take(ch * (H / 512) * 4);
-  r.blk_val = take(n_blk * 4);
-  r.blk_idx = take(n_blk * 4);
   r.att = take((size_t)c->n_kv_heads * mk::kFlashRanges * 2 * ch * (c->head_dim + 2) * 4);
   r.part = take(part * 4);
+  if (r.pp_ok) {
+    r.pp[0] = r.flags;
+    for (int k = 1; k < 10; ++k) r.pp[k] = overlay + (pp[k] - pp[1]);
+    off = std::max(off, overlay + align_up(pp_total - pp[1], 256));
+  }
   r.bytes = off;
   return r;
 }
@@ -315,9 +331,34 @@ PfScratch pf_scratch(const mk_cfg* c) {
 // Every batched prefill step on scratch `buf` (pf_scratch(&h->cfg).bytes bytes of device
 // memory).  Each scratch word the launches read was written earlier in the same call, so
 // the buffer needs no clearing.  Allocates nothing.
+// Which form runs a call: the persistent one where the handle allows it and every chunk
+// qualifies (the shape has the form, and the context ends at or below kPpMaxKeys), else
+// the kernel chain.  -1: the handle asks for the persistent form and the call has none.
+int prefill_form(const mk_handle* h, const PfScratch& S, int32_t n) {
+  const bool fits = S.pp_ok && (long long)h->pos + n <= mk::kPpMaxKeys;
+  if (h->pf_path == MK_PREFILL_CHAIN) return 0;
+  if (h->pf_path == MK_PREFILL_PERSISTENT) return fits ? 1 : -1;
+  return fits ? 1 : 0;
+}
+
 int prefill_batched(mk_handle* h, uint8_t* buf, const PfScratch& S, const int32_t* d_ids, const float* d_rows,
-                    const int32_t* d_pos3, int32_t n, int32_t* d_out_first) {
+                    const int32_t* d_pos3, int32_t n, int32_t* d_out_first, uint32_t* tag) {
   const mk_cfg* c = &h->cfg;
+  const int form = prefill_form(h, S, n);
+  if (form < 0) return MK_ERR_UNSUPPORTED;
+  mk::PpBufs B{};
+  if (form == 1) {
+    B.flags = (unsigned long long*)(buf + S.pp[0]);
+    B.xb = (uint16_t*)(buf + S.pp[1]);
+    B.xp = (uint16_t*)(buf + S.pp[2]);
+    B.ss = (float*)(buf + S.pp[3]);
+    B.ss2 = (float*)(buf + S.pp[4]);
+    B.qr = (float*)(buf + S.pp[5]);
+    B.at = (uint16_t*)(buf + S.pp[6]);
+    B.op = (float*)(buf + S.pp[7]);
+    B.hs = (uint16_t*)(buf + S.pp[8]);
+    B.dp = (float*)(buf + S.pp[9]);
+  }
   const int ch = mk::kPrefillChunk;
   const size_t H = c->hidden;
   mk::PfArgs A{};
@@ -348,7 +389,20 @@ int prefill_batched(mk_handle* h, uint8_t* buf, const PfScratch& S, const int32_
     A.rows = d_rows ? d_rows + (size_t)t0 * H : nullptr;
     A.pos3 = d_pos3 ? d_pos3 + (size_t)t0 * 3 : nullptr;
     A.dbg_hidden = h->dbg_hidden ? h->dbg_hidden + (size_t)t0 * (c->n_layers + 1) * H : nullptr;
-    if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) return MK_ERR_HIP;
+    if (form == 1) {
+      // flag tags of this launch: (L + 1) * kPpKinds, all above every tag the words hold;
+      // past the top of the range the words are cleared (stream-ordered) and tags restart
+      const uint32_t need = (uint32_t)(c->n_layers + 1) * mk::kPpKinds;
+      if ((unsigned long long)*tag + need >= 0xFFFFFF00ull) {
+        if (mk::launch_pp_clear(B.flags, h->stream)) return MK_ERR_HIP;
+        *tag = 1;
+      }
+      if (mk::launch_prefill_persistent(A, B, h->arena, h->lay, *tag, h->spin_limit, h->ctl + 1, h->stream))
+        return MK_ERR_HIP;
+      *tag += need;
+    } else if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) {
+      return MK_ERR_HIP;
+    }
   }
   // the last chunk's residual stream is still in place: its last row gives the first id
   const uint8_t* last_layer = h->arena + (size_t)(c->n_layers - 1) * h->lay.stride;
@@ -380,6 +434,7 @@ static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 uint8_t* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device; NULL before set-up
+uint32_t g_scratch_tag[kMaxDevices];  // next flag tag of the persistent prefill on each device's `scratch`
 
 // Looks up the address of `scratch` on `dev`, which must be the current device; once
 // per device.
@@ -393,6 +448,7 @@ int scratch_setup(int dev) {
     return MK_ERR_HIP;
   }
   g_scratch_ptr[dev] = (uint8_t*)ptr;
+  g_scratch_tag[dev] = 1;  // the array starts zeroed, like every device variable without initializer
   return MK_OK;
 }
 
@@ -541,11 +597,16 @@ int mk_prefill_batched(mk_handle* h, const int32_t* d_ids, const float* d_rows, 
   PfScratch S;
   int e = prefill_batched_args(h, d_ids, n, d_out_first, &S);
   if (e) return e;
-  if (!h->pf_buf && hipMalloc((void**)&h->pf_buf, S.bytes) != hipSuccess) {
-    h->pf_buf = nullptr;
-    return MK_ERR_OOM;
+  if (!h->pf_buf) {
+    if (hipMalloc((void**)&h->pf_buf, S.bytes) != hipSuccess) {
+      h->pf_buf = nullptr;
+      return MK_ERR_OOM;
+    }
+    // the persistent form's flag words start at zero, below every tag
+    if (mk::launch_pp_clear((unsigned long long*)(h->pf_buf + S.flags), h->stream)) return MK_ERR_HIP;
+    h->pf_tag = 1;
   }
-  return prefill_batched(h, h->pf_buf, S, d_ids, d_rows, d_pos3, n, d_out_first);
+  return prefill_batched(h, h->pf_buf, S, d_ids, d_rows, d_pos3, n, d_out_first, &h->pf_tag);
 }
 
 int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* d_rows, const int32_t* d_pos3,
@@ -556,7 +617,8 @@ int mk_prefill_batched_noalloc(mk_handle* h, const int32_t* d_ids, const float* 
   if (S.bytes > kStaticScratchBytes) return MK_ERR_SCRATCH;
   uint8_t* buf = scratch_ptr(h->device);
   if (!buf) return MK_ERR_STATE;  // mk_create looks the address up on the handle's device
-  return prefill_batched(h, buf, S, d_ids, d_rows, d_pos3, n, d_out_first);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);  // the device's tag counter
+  return prefill_batched(h, buf, S, d_ids, d_rows, d_pos3, n, d_out_first, &g_scratch_tag[h->device]);
 }
 
 int mk_decode(mk_handle* h, int32_t n_steps, const int32_t* d_ids, const float* d_embed_buf, const int32_t* d_pos3,
@@ -613,6 +675,12 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace) {
   if (!h) return MK_ERR_ARG;
   h->dbg_hidden = d_hidden;
   h->dbg_trace = (unsigned long long*)d_trace;
+  return MK_OK;
+}
+
+int mk_set_prefill_path(mk_handle* h, int32_t path) {
+  if (!h || path < MK_PREFILL_AUTO || path > MK_PREFILL_PERSISTENT) return MK_ERR_ARG;
+  h->pf_path = path;
   return MK_OK;
 }
 

@@ -52,6 +52,38 @@ struct LmArgs {
   uint32_t call_seq;
 };
 size_t prefill_part_floats(int H, int NQ, int NKV, int D, int I);  // 0: shape not supported
+
+// The same chunk as one persistent launch (mk_pprefill.hip): every workgroup stays
+// resident for all layers and the phases hand over through flagged buffers instead of
+// kernel boundaries.  Hidden 1024, intermediate 3072, head_dim 128, 16 query and 8 KV
+// heads (the hidden-1024 talker and text bodies), chunks whose context ends at or below
+// kPpMaxKeys.  Exchange regions, per XCD replica where marked; NPP is the chunk's column
+// count (a multiple of 16, at most kPrefillChunk):
+constexpr int kPpMaxKeys = 2048;
+constexpr int kPpKinds = 8;  // flag words per workgroup: one per hand-over kind
+struct PpBufs {
+  unsigned long long* flags;  // [kPpKinds][kGrid] tagged words {0, tag}, zero before the first use
+  uint16_t* xb;  // [8][2][H/8][NPP][8] bf16 high, then low parts: input-norm gains * x, the q/k/v operand
+  uint16_t* xp;  // [8][2][H/8][NPP][8] post-attention-norm gains * x, the gate/up operand
+  float* ss;     // [8][32][NPP] sums of squares of x over each owner's 32 columns (input norm)
+  float* ss2;    // [8][32][NPP] the same after attention
+  float* qr;     // [8][NPP][512] q/k/v of the group, times the input norm's 1/rms
+  uint16_t* at;  // [8][2][32][NPP][8] attention outputs of the group, split, the O operand
+  float* op;     // [8 XCDs][32][NPP][32] O partials of each XCD's KV block, by owner
+  uint16_t* hs;  // [8][2][48][NPP][8] SwiGLU outputs of the XCD's MLP slice, split, the down operand
+  float* dp;     // [8][32][NPP][32] down partials of each XCD's MLP slice, by owner
+};
+// Byte offsets of the regions above (relative to a base) for chunks of up to
+// kPrefillChunk positions; returns the total.  0: the shape has no persistent form.
+size_t pp_layout(int H, int NQ, int NKV, int D, int I, size_t offs[10]);
+// The chunk in A, layer weights at `layers`: every layer of the chunk, leaving the final
+// residual of its positions in A.x for launch_prefill_lm.  tag0: first of the
+// (L + 1) * 8 flag tags this launch uses, all above any tag the flag words hold.
+int launch_prefill_persistent(const PfArgs& A, const PpBufs& B, const uint8_t* layers, const LayerLayout& lay,
+                              uint32_t tag0, uint32_t spin_limit, uint32_t* abort_flag, void* stream);
+bool pp_supported(int H, int NQ, int NKV, int D, int I);
+// Zeroes the kPpKinds * kGrid flag words (a kernel, so the call may sit in a captured graph).
+int launch_pp_clear(unsigned long long* flags, void* stream);
 int launch_prefill_lm(const PfArgs& a, const LmArgs& lm, void* stream);
 int launch_prefill_chunk(const PfArgs& a, const uint8_t* layers, const LayerLayout& lay, void* stream);
 // Read-stream ceiling (a measurement kernel, not part of the decode path).

@@ -737,15 +737,23 @@ __global__ __launch_bounds__(64) void pf_swiglu_kernel(PfArgs A, int ks) {
 // Logits of the last prompt position: the final-norm row (gains * x * 1/rms) in LDS,
 // 16 vocabulary rows per wave, 64 per workgroup, each row a 64-lane dot product over
 // 16-byte weight loads; the workgroup's largest logit (ties: lowest row) goes to
-// blk_val/blk_idx.  H is 1024 or 2048 here.
+// blk_val/blk_idx.  The row's sum of squares is taken from the row itself, so the
+// kernel serves both prefill forms (only the residual row is common to them).  H is
+// 1024 or 2048 here.
 __global__ __launch_bounds__(256) void pf_lm_kernel(PfArgs A, LmArgs M) {
   constexpr int RPW = kLmRowsPerBlock / 4;
   __shared__ float xn[2048];
   __shared__ float bv[4];
   __shared__ int bi[4];
+  __shared__ float sqw[4];
   const int H = A.H, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float rs = row_rs(A, M.n_last);
   const float* x = A.x + (size_t)M.n_last * H;
+  float sq = 0.f;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sq = fmaf(x[i], x[i], sq);
+  sq = wsum(sq);
+  if (lane == 0) sqw[wv] = sq;
+  __syncthreads();
+  const float rs = rsqrtf((sqw[0] + sqw[1] + sqw[2] + sqw[3]) / (float)H + A.eps);
   for (int i = threadIdx.x; i < H; i += blockDim.x) xn[i] = M.g_final[i] * (x[i] * rs);
   __syncthreads();
   const int r0 = blockIdx.x * kLmRowsPerBlock + wv * RPW;

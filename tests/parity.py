@@ -60,7 +60,7 @@ class GpuRun:
 
 
 def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batched: bool = False,
-            phased: bool = False) -> GpuRun:
+            phased: bool = False, prefill_path: Optional[int] = None) -> GpuRun:
     import torch
     from persistent_megakernel_loop_amd.binding import Decoder, to_device
 
@@ -68,6 +68,8 @@ def run_gpu(shape, dev_weights, inp: Inputs, trace: bool = False, dec=None, batc
     own = dec is None
     if own:
         dec = Decoder(shape, dev_weights)
+    if prefill_path is not None:
+        dec.set_prefill_path(prefill_path)
     L, H = shape.n_layers, shape.hidden
     P = 0 if inp.prompt_ids is None else len(inp.prompt_ids)
     n = inp.n_steps
