@@ -235,7 +235,13 @@ int mk_set_debug(mk_handle* h, float* d_hidden, uint64_t* d_trace);
  * arrived at the barrier, and last, for the first wait of the segment, its poll rounds
  * (bits 56..63), the ticks of its first round (bits 32..55) and all its ticks (bits
  * 0..31) (0 where an event does not occur).  wg = -1 traces every
- * workgroup: d_phase is then [n][grid][2 + 10*n_layers][8].
+ * workgroup: d_phase is then [n][grid][2 + 10*n_layers][8].  The persistent form of
+ * mk_prefill_batched writes instead, for each chunk it runs (each overwriting the one
+ * before), [grid][n_layers + 1][8][2]: for each hand-over kind (q/k/v, attention, O
+ * partials, residual after attention, SwiGLU, down partials, residual after the MLP,
+ * and in slot 0 the launch's placement check) produced in layer l (slot l + 1; slot 0
+ * also holds the input rows' residual), the 100 MHz ticks at which the workgroup's wait
+ * for it completed and at which the workgroup raised its own flag of that kind.
  * MK_ERR_ARG if wg is not in [-1, grid). */
 int mk_set_phase_trace(mk_handle* h, uint64_t* d_phase, int32_t wg);
 

@@ -397,7 +397,8 @@ int prefill_batched(mk_handle* h, uint8_t* buf, const PfScratch& S, const int32_
         if (mk::launch_pp_clear(B.flags, h->stream)) return MK_ERR_HIP;
         *tag = 1;
       }
-      if (mk::launch_prefill_persistent(A, B, h->arena, h->lay, *tag, h->spin_limit, h->ctl + 1, h->stream))
+      if (mk::launch_prefill_persistent(A, B, h->arena, h->lay, *tag, h->spin_limit, h->ctl + 1, h->dbg_phase,
+                                        h->stream))
         return MK_ERR_HIP;
       *tag += need;
     } else if (mk::launch_prefill_chunk(A, h->arena, h->lay, h->stream)) {

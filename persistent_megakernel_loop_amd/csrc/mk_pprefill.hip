@@ -67,6 +67,7 @@ struct PpK {
   uint32_t tag0;
   uint32_t spin_limit;
   uint32_t* abort_flag;
+  unsigned long long* dbg;  // phase timeline [grid][L + 1][kPpKinds][2], or NULL
 };
 
 __device__ __forceinline__ uint32_t pp_tag(uint32_t tag0, int l, int kind) {
@@ -130,7 +131,13 @@ __device__ void pp_timeout(const PpK& k, uint32_t where, uint32_t tag, uint32_t 
 // Wave 0 polls the flags of n workgroups (flag index base + i * step, i < n <= 64) until
 // each carries `tag`; then the workgroup meets at a barrier.  Returns false on every
 // thread if the wait gave up (spin limit) or another workgroup's wait did.
-__device__ bool wg_wait(const PpK& k, int tid, int kind, int base, int step, int n, uint32_t tag, int* stop) {
+// Timeline record of hand-over `kind` produced in layer pl (-1: the input rows):
+// e = 0 when this workgroup's wait for it completed, e = 1 when it raised its own flag.
+__device__ __forceinline__ void stamp(const PpK& k, int pl, int kind, int e) {
+  if (k.dbg) k.dbg[(((size_t)blockIdx.x * (k.A.L + 1) + pl + 1) * kPpKinds + kind) * 2 + e] = wall_clock64();
+}
+
+__device__ bool wg_wait(const PpK& k, int tid, int kind, int base, int step, int n, uint32_t tag, int* stop, int pl) {
   if (tid < 64) {
     const int lane = tid;
     const uint32_t idx = (uint32_t)(kind * kGrid + base + min(lane, n - 1) * step);
@@ -151,14 +158,18 @@ __device__ bool wg_wait(const PpK& k, int tid, int kind, int base, int step, int
     if (lane == 0) *stop = all_ok ? 0 : 1;
   }
   __syncthreads();
+  if (tid == 0) stamp(k, pl, kind, 0);
   return *stop == 0;
 }
 
 // Every wave waits for its own stores, the workgroup meets, and thread 0 raises the flag.
-__device__ __forceinline__ void wg_publish(const PpK& k, int kind, uint32_t tag, bool plain) {
+__device__ __forceinline__ void wg_publish(const PpK& k, int kind, uint32_t tag, bool plain, int pl) {
   vmem_drain();
   __syncthreads();
-  if (threadIdx.x == 0) st_local(k.B.flags + kind * kGrid + blockIdx.x, 0.f, tag, plain);
+  if (threadIdx.x == 0) {
+    st_local(k.B.flags + kind * kGrid + blockIdx.x, 0.f, tag, plain);
+    stamp(k, pl, kind, 1);
+  }
 }
 
 // acc[nt] += A (16 rows x 64 columns) * B (the same 64 columns x 16 positions of tile nt).
@@ -261,15 +272,34 @@ __device__ __forceinline__ void add_partials(float (&xres)[NPP][kCw], const Buf&
   }
 }
 
-// Rotary of pair i (elements i and i + 64) at the position stream its section reads.
-__device__ __forceinline__ void rotate(const PfArgs& A, int n, int i, float& a0, float& a1) {
-  const int sct = i < A.sec_end0 ? 0 : (i < A.sec_end1 ? 1 : 2);
-  int ps = A.pos3 ? A.pos3[n * 3 + sct] : A.pos0 + n;
-  ps = (ps < 0 || ps >= A.rope_positions) ? 0 : ps;
-  const float c = A.rope_cos[(size_t)ps * (kD / 2) + i], sn = A.rope_sin[(size_t)ps * (kD / 2) + i];
-  const float o0 = a0 * c - a1 * sn, o1 = a1 * c + a0 * sn;
-  a0 = o0;
-  a1 = o1;
+// The rotary table of the chunk's positions: pair i (elements i and i + 64) of position
+// n at the position stream its section reads (a stream value outside the table reads
+// row 0, as it is flagged), gathered into LDS once per launch.
+template <int NPP>
+__device__ __forceinline__ void rope_table(const PfArgs& A, float (&rc)[NPP][kD / 2], float (&rsn)[NPP][kD / 2]) {
+  for (int u = threadIdx.x; u < NPP * (kD / 2); u += kPpThreads) {
+    const int n = u / (kD / 2), i = u % (kD / 2);
+    float c = 1.f, sn = 0.f;
+    if (n < A.m) {
+      const int sct = i < A.sec_end0 ? 0 : (i < A.sec_end1 ? 1 : 2);
+      int ps = A.pos3 ? A.pos3[n * 3 + sct] : A.pos0 + n;
+      ps = (ps < 0 || ps >= A.rope_positions) ? 0 : ps;
+      c = A.rope_cos[(size_t)ps * (kD / 2) + i];
+      sn = A.rope_sin[(size_t)ps * (kD / 2) + i];
+    }
+    rc[n][i] = c;
+    rsn[n][i] = sn;
+  }
+}
+
+// RMSNorm over the head (gains gn) and the rotary of pair i, for a lane holding elements
+// i and i + 64 of the head; returns them in a0, a1.
+__device__ __forceinline__ void norm_rotate(const float* gn, float eps, float c, float sn, int i, float& a0, float& a1) {
+  const float sq = wave_sum(fmaf(a1, a1, a0 * a0));
+  const float r = rsqrtf(sq / (float)kD + eps);
+  const float n0 = gn[i] * (a0 * r), n1 = gn[i + 64] * (a1 * r);
+  a0 = n0 * c - n1 * sn;
+  a1 = n1 * c + n0 * sn;
 }
 
 // LDS of the attention phase.
@@ -281,6 +311,61 @@ struct AttLds {
   float mw[8][kQpg], lw[8][kQpg];
   float aw[8][kQpg][kD];
 };
+
+// Scores of key row tt against both query heads of slot s: the row from the cache below
+// pos0, else the chunk's own from LDS.  The row is read in two halves of 64 dims (a
+// half's loads all in flight at once), and the queries from LDS (one broadcast read per
+// 4 dims) inside the loop: an offset the compiler cannot see through keeps it from
+// holding all 256 in registers.
+__device__ __forceinline__ void score_row(const PfArgs& A, const AttLds& S, int s, size_t cbase, int tt, int pos0,
+                                          float (&sc)[kQpg]) {
+  sc[0] = sc[1] = 0.f;
+  int qo = 0;
+  asm volatile("" : "+v"(qo));
+  const float* qsp = &S.qs[s][0][0] + qo;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint4 kr[kD / 16];
+    if (tt < pos0) {
+#pragma unroll
+      for (int j8 = 0; j8 < kD / 16; ++j8)
+        kr[j8] = *reinterpret_cast<const uint4*>(A.kcache + cbase + (size_t)tt * kD + 64 * half + 8 * j8);
+    } else {
+#pragma unroll
+      for (int j8 = 0; j8 < kD / 16; ++j8)
+        kr[j8] = *reinterpret_cast<const uint4*>(&S.kl[tt - pos0][64 * half + 8 * j8]);
+    }
+#pragma unroll
+    for (int j8 = 0; j8 < kD / 16; ++j8) {
+      const uint32_t wd[4] = {kr[j8].x, kr[j8].y, kr[j8].z, kr[j8].w};
+      const int d0 = 64 * half + 8 * j8;
+#pragma unroll
+      for (int h = 0; h < kQpg; ++h) {
+        const float4 qa = *reinterpret_cast<const float4*>(qsp + h * kD + d0);
+        const float4 qb = *reinterpret_cast<const float4*>(qsp + h * kD + d0 + 4);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc[h] = fmaf(qv[2 * e], bf16lo(wd[e]), sc[h]);
+          sc[h] = fmaf(qv[2 * e + 1], bf16hi(wd[e]), sc[h]);
+        }
+      }
+      if (j8 & 1) __builtin_amdgcn_sched_barrier(0);  // at most 4 query reads in flight per head
+    }
+  }
+}
+
+// Head h's attention output for position n (dims 2 lane, 2 lane + 1), split into the O
+// product's operand.
+template <int NPP>
+__device__ __forceinline__ void store_att(const Buf& at, bool plain, int n, int h, int lane, float o0, float o1) {
+  const uint16_t h0 = to_bf(o0), h1 = to_bf(o1);
+  const uint16_t l0 = to_bf(o0 - from_bf(h0)), l1 = to_bf(o1 - from_bf(h1));
+  const int c = h * kD + 2 * lane;
+  const uint32_t off = (uint32_t)((((c >> 3) * NPP + n) * 8 + (c & 7)) * 2);
+  at.st4(off, (uint32_t)h0 | ((uint32_t)h1 << 16), plain);
+  at.st4(off + (uint32_t)(kQpg * kD * NPP * 2), (uint32_t)l0 | ((uint32_t)l1 << 16), plain);
+}
 
 // Causal attention of position n (query slot s of the workgroup) for group g over keys
 // 0..pos0+n: keys below pos0 from the cache, the chunk's own from LDS.  Wave w takes the
@@ -294,6 +379,11 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int p = A.pos0 + n, nkeys = p + 1, pos0 = A.pos0;
   const size_t cbase = ((size_t)l * kXcds + g) * A.max_seq * kD;
+  // A context of one block (up to 64 keys): wave 0 scores it and normalises the weights,
+  // then all waves share the value sum, 8 rows each.  Longer: every wave runs its own
+  // blocks with a running maximum and sum, merged across waves at the end.  (One call
+  // site of score_row: two inlined copies made the register allocation spill.)
+  const bool one_block = nkeys <= 64;
   float M[kQpg], Ls[kQpg], acc[kQpg][2];
 #pragma unroll
   for (int h = 0; h < kQpg; ++h) { M[h] = -INFINITY; Ls[h] = 0.f; acc[h][0] = acc[h][1] = 0.f; }
@@ -302,42 +392,17 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
     const int t = kb * 64 + lane;
     const bool valid = t < nkeys;
     const int tt = valid ? t : p;
-    float sc[kQpg] = {0.f, 0.f};
-    // The key row in two halves of 64 dims (a half's loads all in flight at once), and
-    // the queries read from LDS (one broadcast read per 4 dims) inside the loop: an
-    // offset the compiler cannot see through keeps it from holding all 256 in registers.
-    int qo = 0;
-    asm volatile("" : "+v"(qo));
-    const float* qsp = &S.qs[s][0][0] + qo;
+    float sc[kQpg];
+    score_row(A, S, s, cbase, tt, pos0, sc);
+    if (one_block) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint4 kr[kD / 16];
-      if (tt < pos0) {
-#pragma unroll
-        for (int j8 = 0; j8 < kD / 16; ++j8)
-          kr[j8] = *reinterpret_cast<const uint4*>(A.kcache + cbase + (size_t)tt * kD + 64 * half + 8 * j8);
-      } else {
-#pragma unroll
-        for (int j8 = 0; j8 < kD / 16; ++j8)
-          kr[j8] = *reinterpret_cast<const uint4*>(&S.kl[tt - pos0][64 * half + 8 * j8]);
+      for (int h = 0; h < kQpg; ++h) {
+        const float sv = valid ? sc[h] : -INFINITY;
+        const float mx = wave_max(sv);
+        const float pr = valid ? __expf(sv - mx) : 0.f;
+        S.pw[0][h][lane] = pr / wave_sum(pr);
       }
-#pragma unroll
-      for (int j8 = 0; j8 < kD / 16; ++j8) {
-        const uint32_t wd[4] = {kr[j8].x, kr[j8].y, kr[j8].z, kr[j8].w};
-        const int d0 = 64 * half + 8 * j8;
-#pragma unroll
-        for (int h = 0; h < kQpg; ++h) {
-          const float4 qa = *reinterpret_cast<const float4*>(qsp + h * kD + d0);
-          const float4 qb = *reinterpret_cast<const float4*>(qsp + h * kD + d0 + 4);
-          const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[h] = fmaf(qv[2 * e], bf16lo(wd[e]), sc[h]);
-            sc[h] = fmaf(qv[2 * e + 1], bf16hi(wd[e]), sc[h]);
-          }
-        }
-        if (j8 & 1) __builtin_amdgcn_sched_barrier(0);  // at most 4 query reads in flight per head
-      }
+      break;
     }
 #pragma unroll
     for (int h = 0; h < kQpg; ++h) {
@@ -373,6 +438,37 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
     }
     __builtin_amdgcn_wave_barrier();
   }
+  if (one_block) {
+    __syncthreads();
+    const int r0 = 8 * w, r1 = min(r0 + 8, nkeys);
+    for (int row = r0; row < r1; ++row) {
+      const uint32_t vv = row < pos0 ? *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)row * kD + 2 * lane)
+                                     : *reinterpret_cast<const uint32_t*>(&S.vl[row - pos0][2 * lane]);
+#pragma unroll
+      for (int h = 0; h < kQpg; ++h) {
+        acc[h][0] = fmaf(S.pw[0][h][row], bf16lo(vv), acc[h][0]);
+        acc[h][1] = fmaf(S.pw[0][h][row], bf16hi(vv), acc[h][1]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kQpg; ++h) {
+      S.aw[w][h][2 * lane] = acc[h][0];
+      S.aw[w][h][2 * lane + 1] = acc[h][1];
+    }
+    __syncthreads();
+    if (w < kQpg) {
+      const int h = w;
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        o0 += S.aw[v][h][2 * lane];
+        o1 += S.aw[v][h][2 * lane + 1];
+      }
+      store_att<NPP>(at, plain, n, h, lane, o0, o1);
+    }
+    __syncthreads();
+    return;
+  }
 #pragma unroll
   for (int h = 0; h < kQpg; ++h) {
     if (lane == 0) { S.mw[w][h] = M[h]; S.lw[w][h] = Ls[h]; }
@@ -398,14 +494,7 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
       o0 = fmaf(f[v], S.aw[v][h][2 * lane], o0);
       o1 = fmaf(f[v], S.aw[v][h][2 * lane + 1], o1);
     }
-    o0 *= inv;
-    o1 *= inv;
-    const uint16_t h0 = to_bf(o0), h1 = to_bf(o1);
-    const uint16_t l0 = to_bf(o0 - from_bf(h0)), l1 = to_bf(o1 - from_bf(h1));
-    const int c = h * kD + 2 * lane;
-    const uint32_t off = (uint32_t)((((c >> 3) * NPP + n) * 8 + (c & 7)) * 2);
-    at.st4(off, (uint32_t)h0 | ((uint32_t)h1 << 16), plain);
-    at.st4(off + (uint32_t)(kQpg * kD * NPP * 2), (uint32_t)l0 | ((uint32_t)l1 << 16), plain);
+    store_att<NPP>(at, plain, n, h, lane, o0 * inv, o1 * inv);
   }
   __syncthreads();  // the LDS partials are reused by the workgroup's next position
 }
@@ -418,6 +507,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
   __shared__ __align__(16) float xres[NPP][kCw];
   __shared__ __align__(16) float gu[NPP][2 * kHalf];
   __shared__ float rs[NPP];
+  __shared__ float rc[NPP][kD / 2], rsn[NPP][kD / 2];  // the chunk's rotary table
   __shared__ int stop, placed_s;
   __shared__ __align__(16) u4 big[kBig / 16];
   f4* red = reinterpret_cast<f4*>(big);
@@ -441,11 +531,13 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
   const Buf dp(k.B.dp, (uint32_t)(kXcds * kPerXcd * NPP * kCw * 4));
 
   // ---------------------------------------------------------------- placement
+  if (threadIdx.x == 0) stamp(k, -1, KPLACE, 0);
   if (threadIdx.x == 0) {
     uint32_t xcc;
     asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
     st_tag(k.B.flags + KPLACE * kGrid + b, __uint_as_float(xcc & 0xfu), pp_tag(k.tag0, -1, KPLACE));
   }
+  rope_table<NPP>(A, rc, rsn);  // read after the barrier that ends the placement check
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const uint32_t tag = pp_tag(k.tag0, -1, KPLACE);
@@ -477,6 +569,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     }
   }
   __syncthreads();
+  if (threadIdx.x == 0) stamp(k, -1, KPLACE, 1);
   if (stop) return;
   const bool plain = placed_s != 0;  // XCD-local blocks and flags may stay in the XCD's L2
 
@@ -522,7 +615,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     }
     __syncthreads();
     publish_residual<NPP>(xres, A.in_norm0, j, xb, ss, plain, (int)threadIdx.x);
-    wg_publish(k, KR2, pp_tag(k.tag0, -1, KR2), plain);
+    wg_publish(k, KR2, pp_tag(k.tag0, -1, KR2), plain, -1);
   }
 
 #pragma nounroll
@@ -544,7 +637,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
       const uint16_t* wqp = opaque(wq);
 #pragma unroll
       for (int s = 0; s < 2; ++s) load_a(wqp, (size_t)x * kQRows + 16 * j + li, kH, 128 * w + 64 * s, lane, a[s]);
-      if (!wg_wait(k, tid, KR2, x, kXcds, kPerXcd, pp_tag(k.tag0, l - 1, KR2), &stop)) return;
+      if (!wg_wait(k, tid, KR2, x, kXcds, kPerXcd, pp_tag(k.tag0, l - 1, KR2), &stop, l - 1)) return;
       rms_of<NPP>(ss, A.eps, rs, tid);
       f4 acc[NT];
 #pragma unroll
@@ -570,12 +663,12 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
                         __float_as_uint(o[3] * sc)};
         qr.st16((uint32_t)((n * kQRows + r0) * 4), val, plain);
       }
-      wg_publish(k, KQ, pp_tag(k.tag0, l, KQ), plain);
+      wg_publish(k, KQ, pp_tag(k.tag0, l, KQ), plain, l);
     }
 
     // ------------------------------------------------------------ attention
     {
-      if (!wg_wait(k, tid, KQ, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KQ), &stop)) return;
+      if (!wg_wait(k, tid, KQ, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KQ), &stop, l)) return;
       const int na = j, nb2 = j + kPerXcd;
       const bool va = na < m, vb = NPP > kPerXcd && nb2 < m;
       // padding positions of the O operand read zeros
@@ -589,52 +682,62 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
       }
       const int nmax = vb ? nb2 : (va ? na : -1);
       if (nmax >= 0) {
+        // Wave w prepares the chunk's key and value rows w, w + 8, ... up to nmax (every
+        // load issued before the first row's arithmetic), and waves 0..3 also query head
+        // h = w & 1 of slot w >> 1: RMSNorm, rotary from the launch's table, bf16 rounding
+        // of keys and values as the cache holds them.
+        constexpr int RPW = NPP / 8;  // rows per wave at most
         const float* kn = G + kH + kD;
-#pragma nounroll
-        for (int n = w; n <= nmax; n += 8) {
-          float k0 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + 2 * kD + lane) * 4)));
-          float k1 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + 2 * kD + lane + 64) * 4)));
-          const float v0 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + 3 * kD + lane) * 4)));
-          const float v1 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + 3 * kD + lane + 64) * 4)));
-          const float sq = wave_sum(fmaf(k1, k1, k0 * k0));
-          const float r = rsqrtf(sq / (float)kD + A.eps);
-          k0 = kn[lane] * (k0 * r);
-          k1 = kn[lane + 64] * (k1 * r);
-          rotate(A, n, lane, k0, k1);
-          const uint16_t kb0 = to_bf(k0), kb1 = to_bf(k1), vb0 = to_bf(v0), vb1 = to_bf(v1);
-          S.kl[n][lane] = kb0;
-          S.kl[n][lane + 64] = kb1;
-          S.vl[n][lane] = vb0;
-          S.vl[n][lane + 64] = vb1;
-          if (n == na || n == nb2) {
-            const size_t crow = (((size_t)l * kXcds + x) * A.max_seq + A.pos0 + n) * kD;
-            A.kcache[crow + lane] = kb0;
-            A.kcache[crow + lane + 64] = kb1;
-            A.vcache[crow + lane] = vb0;
-            A.vcache[crow + lane + 64] = vb1;
+        float kv[RPW][4];
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+          const int n = w + 8 * u;
+          const uint32_t o = (uint32_t)((n * kQRows + 2 * kD + lane) * 4);
+          if (n <= nmax) {
+            kv[u][0] = __uint_as_float(qr.ld4(o));
+            kv[u][1] = __uint_as_float(qr.ld4(o + 64 * 4));
+            kv[u][2] = __uint_as_float(qr.ld4(o + kD * 4));
+            kv[u][3] = __uint_as_float(qr.ld4(o + (kD + 64) * 4));
           }
         }
-        if (w < 4) {  // wave 2s + h: query head h of slot s
-          const int s = w >> 1, h = w & 1, n = s ? nb2 : na;
-          if (s ? vb : va) {
-            const float* qn = G + kH;
-            float a0 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + h * kD + lane) * 4)));
-            float a1 = __uint_as_float(qr.ld4((uint32_t)((n * kQRows + h * kD + lane + 64) * 4)));
-            const float sq = wave_sum(fmaf(a1, a1, a0 * a0));
-            const float r = rsqrtf(sq / (float)kD + A.eps);
-            a0 = qn[lane] * (a0 * r);
-            a1 = qn[lane + 64] * (a1 * r);
-            rotate(A, n, lane, a0, a1);
-            const float qscale = rsqrtf((float)kD);
-            S.qs[s][h][lane] = a0 * qscale;
-            S.qs[s][h][lane + 64] = a1 * qscale;
+        const int qs_slot = w >> 1, qh = w & 1, qn_pos = qs_slot ? nb2 : na;
+        const bool has_q = w < 4 && (qs_slot ? vb : va);
+        float q0 = 0.f, q1 = 0.f;
+        if (has_q) {
+          q0 = __uint_as_float(qr.ld4((uint32_t)((qn_pos * kQRows + qh * kD + lane) * 4)));
+          q1 = __uint_as_float(qr.ld4((uint32_t)((qn_pos * kQRows + qh * kD + lane + 64) * 4)));
+        }
+#pragma unroll
+        for (int u = 0; u < RPW; ++u) {
+          const int n = w + 8 * u;
+          if (n <= nmax) {
+            float k0 = kv[u][0], k1 = kv[u][1];
+            norm_rotate(kn, A.eps, rc[n][lane], rsn[n][lane], lane, k0, k1);
+            const uint16_t kb0 = to_bf(k0), kb1 = to_bf(k1), vb0 = to_bf(kv[u][2]), vb1 = to_bf(kv[u][3]);
+            S.kl[n][lane] = kb0;
+            S.kl[n][lane + 64] = kb1;
+            S.vl[n][lane] = vb0;
+            S.vl[n][lane + 64] = vb1;
+            if (n == na || n == nb2) {
+              const size_t crow = (((size_t)l * kXcds + x) * A.max_seq + A.pos0 + n) * kD;
+              A.kcache[crow + lane] = kb0;
+              A.kcache[crow + lane + 64] = kb1;
+              A.vcache[crow + lane] = vb0;
+              A.vcache[crow + lane + 64] = vb1;
+            }
           }
+        }
+        if (has_q) {
+          norm_rotate(G + kH, A.eps, rc[qn_pos][lane], rsn[qn_pos][lane], lane, q0, q1);
+          const float qscale = rsqrtf((float)kD);
+          S.qs[qs_slot][qh][lane] = q0 * qscale;
+          S.qs[qs_slot][qh][lane + 64] = q1 * qscale;
         }
         __syncthreads();
         if (va) attend<NPP>(k, S, l, x, na, 0, at, plain, tid);
         if (vb) attend<NPP>(k, S, l, x, nb2, 1, at, plain, tid);
       }
-      wg_publish(k, KA, pp_tag(k.tag0, l, KA), plain);
+      wg_publish(k, KA, pp_tag(k.tag0, l, KA), plain, l);
     }
 
     // ------------------------------------------------------------ O product (partial of KV block x)
@@ -642,7 +745,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
       const int rt = w & 1, s = w >> 1;
       bf16x8 a[2];
       load_a(opaque(wo) + (size_t)x * kH * (kQpg * kD), (size_t)(kCw * j + 16 * rt + li), kQpg * kD, 64 * s, lane, a);
-      if (!wg_wait(k, tid, KA, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KA), &stop)) return;
+      if (!wg_wait(k, tid, KA, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KA), &stop, l)) return;
       f4 acc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -662,16 +765,16 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
         const u4 val = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
         op.st16((uint32_t)((((x * kPerXcd + j) * NPP + n) * kCw + r0) * 4), val, false);
       }
-      wg_publish(k, KO, pp_tag(k.tag0, l, KO), false);
+      wg_publish(k, KO, pp_tag(k.tag0, l, KO), false, l);
     }
 
     // ------------------------------------------------------------ residual after attention
     {
-      if (!wg_wait(k, tid, KO, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KO), &stop)) return;
+      if (!wg_wait(k, tid, KO, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KO), &stop, l)) return;
       add_partials<NPP>(xres, op, j, tid);
       __syncthreads();
       publish_residual<NPP>(xres, G, j, xp, ss2, plain, tid);
-      wg_publish(k, KR1, pp_tag(k.tag0, l, KR1), plain);
+      wg_publish(k, KR1, pp_tag(k.tag0, l, KR1), plain, l);
     }
 
     // ------------------------------------------------------------ gate/up product and SwiGLU
@@ -690,7 +793,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
             a[rt][s][1] = as_bf8(u4{0u, 0u, 0u, 0u});
           }
         }
-      if (!wg_wait(k, tid, KR1, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KR1), &stop)) return;
+      if (!wg_wait(k, tid, KR1, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KR1), &stop, l)) return;
       rms_of<NPP>(ss2, A.eps, rs, tid);
       f4 acc[2][NT];
 #pragma unroll
@@ -733,7 +836,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
         hs.st2(off, hh, plain);
         hs.st2(off + (uint32_t)(kIx * NPP * 2), hl, plain);
       }
-      wg_publish(k, KG, pp_tag(k.tag0, l, KG), plain);
+      wg_publish(k, KG, pp_tag(k.tag0, l, KG), plain, l);
     }
 
     // ------------------------------------------------------------ down product (partial of slice x)
@@ -745,7 +848,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
       const uint16_t* wblk = opaque(wdn) + (size_t)x * kH * kIx;
       load_a(wblk, (size_t)(kCw * j + 16 * rt + li), kIx, 64 * sg, lane, a[0]);
       if (two) load_a(wblk, (size_t)(kCw * j + 16 * rt + li), kIx, 64 * (sg + 4), lane, a[1]);
-      if (!wg_wait(k, tid, KG, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KG), &stop)) return;
+      if (!wg_wait(k, tid, KG, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KG), &stop, l)) return;
       f4 acc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -772,12 +875,12 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
         const u4 val = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
         dp.st16((uint32_t)((((x * kPerXcd + j) * NPP + n) * kCw + r0) * 4), val, false);
       }
-      wg_publish(k, KD, pp_tag(k.tag0, l, KD), false);
+      wg_publish(k, KD, pp_tag(k.tag0, l, KD), false, l);
     }
 
     // ------------------------------------------------------------ residual after the MLP
     {
-      if (!wg_wait(k, tid, KD, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KD), &stop)) return;
+      if (!wg_wait(k, tid, KD, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KD), &stop, l)) return;
       add_partials<NPP>(xres, dp, j, tid);
       __syncthreads();
       const int t = tid;
@@ -794,7 +897,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
       }
       if (l + 1 < L) {
         publish_residual<NPP>(xres, G + kH + 2 * kD, j, xb, ss, plain, tid);
-        wg_publish(k, KR2, pp_tag(k.tag0, l, KR2), plain);
+        wg_publish(k, KR2, pp_tag(k.tag0, l, KR2), plain, l);
       }
     }
   }
@@ -854,11 +957,12 @@ int launch_pp_clear(unsigned long long* flags, void* stream) {
 }
 
 int launch_prefill_persistent(const PfArgs& A, const PpBufs& B, const uint8_t* layers, const LayerLayout& lay,
-                              uint32_t tag0, uint32_t spin_limit, uint32_t* abort_flag, void* stream) {
+                              uint32_t tag0, uint32_t spin_limit, uint32_t* abort_flag, unsigned long long* dbg_phase,
+                              void* stream) {
   if (!pp_supported(A.H, A.NQ, A.NKV, A.D, A.I) || A.m <= 0 || A.m > A.npp || A.npp % 16 || A.npp > kPrefillChunk ||
       A.pos0 + A.m > kPpMaxKeys)
     return -1;
-  PpK k{A, B, layers, lay, tag0, spin_limit, abort_flag};
+  PpK k{A, B, layers, lay, tag0, spin_limit, abort_flag, dbg_phase};
   hipStream_t st = (hipStream_t)stream;
   switch (A.npp / 16) {
     case 1: return launch_nt<1>(k, st);

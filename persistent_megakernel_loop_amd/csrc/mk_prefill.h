@@ -79,8 +79,13 @@ size_t pp_layout(int H, int NQ, int NKV, int D, int I, size_t offs[10]);
 // The chunk in A, layer weights at `layers`: every layer of the chunk, leaving the final
 // residual of its positions in A.x for launch_prefill_lm.  tag0: first of the
 // (L + 1) * 8 flag tags this launch uses, all above any tag the flag words hold.
+// dbg_phase, if not NULL, receives [grid][L + 1][kPpKinds][2] 100 MHz ticks: for each
+// hand-over kind produced in layer l (slot l + 1; slot 0: the input rows and the launch's
+// placement check), when the workgroup's wait for it completed and when it raised its
+// own flag of that kind.
 int launch_prefill_persistent(const PfArgs& A, const PpBufs& B, const uint8_t* layers, const LayerLayout& lay,
-                              uint32_t tag0, uint32_t spin_limit, uint32_t* abort_flag, void* stream);
+                              uint32_t tag0, uint32_t spin_limit, uint32_t* abort_flag, unsigned long long* dbg_phase,
+                              void* stream);
 bool pp_supported(int H, int NQ, int NKV, int D, int I);
 // Zeroes the kPpKinds * kGrid flag words (a kernel, so the call may sit in a captured graph).
 int launch_pp_clear(unsigned long long* flags, void* stream);
