@@ -230,9 +230,17 @@ __device__ __forceinline__ void rms_of(const Buf& ss, float eps, float* rs, int 
 
 // Owner j publishes its residual columns for a product: gains * x split into the
 // operand layout, and the sums of squares of x over its columns per position.
+// The 8 gains of the columns thread tid publishes (they do not depend on the position),
+// loaded ahead of the phase's other memory round trips.
+__device__ __forceinline__ void load_gains(const float* g, int j, int tid, float (&g8)[8]) {
+  const int col = kCw * j + 8 * (tid % (kCw / 8));
+  const float4 a = *reinterpret_cast<const float4*>(g + col), b = *reinterpret_cast<const float4*>(g + col + 4);
+  g8[0] = a.x; g8[1] = a.y; g8[2] = a.z; g8[3] = a.w; g8[4] = b.x; g8[5] = b.y; g8[6] = b.z; g8[7] = b.w;
+}
+
 template <int NPP>
-__device__ __forceinline__ void publish_residual(const float (&xres)[NPP][kCw], const float* g, int j, const Buf& dst,
-                                                 const Buf& ss, bool plain, int tid) {
+__device__ __forceinline__ void publish_residual(const float (&xres)[NPP][kCw], const float (&g8)[8], int j,
+                                                 const Buf& dst, const Buf& ss, bool plain, int tid) {
   const int t = tid;
   if (t < NPP * (kCw / 8)) {
     const int n = t / (kCw / 8), c8 = t % (kCw / 8), col = kCw * j + 8 * c8;
@@ -240,7 +248,7 @@ __device__ __forceinline__ void publish_residual(const float (&xres)[NPP][kCw], 
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       v[e] = xres[n][8 * c8 + e];
-      gv[e] = g[col + e] * v[e];
+      gv[e] = g8[e] * v[e];
       sq = fmaf(v[e], v[e], sq);
     }
     u4 hi, lo;
@@ -308,6 +316,7 @@ struct AttLds {
   uint16_t kl[kPrefillChunk][kKRow];  // the chunk's keys after norm and rotary, bf16
   uint16_t vl[kPrefillChunk][kD];     // the chunk's values, bf16
   float pw[8][kQpg][64];              // a block's softmax weights, per wave
+  float sl[kQpg][64];                 // scores of a one-block context
   float mw[8][kQpg], lw[8][kQpg];
   float aw[8][kQpg][kD];
 };
@@ -379,11 +388,90 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int p = A.pos0 + n, nkeys = p + 1, pos0 = A.pos0;
   const size_t cbase = ((size_t)l * kXcds + g) * A.max_seq * kD;
-  // A context of one block (up to 64 keys): wave 0 scores it and normalises the weights,
-  // then all waves share the value sum, 8 rows each.  Longer: every wave runs its own
-  // blocks with a running maximum and sum, merged across waves at the end.  (One call
-  // site of score_row: two inlined copies made the register allocation spill.)
+  // A context of one block (up to 64 keys): every wave scores 8 keys (8 lanes per key,
+  // 16 dims per lane, summed over the 8 lanes), wave 0 normalises the weights, and all
+  // waves share the value sum, 8 rows each.  Longer: every wave runs its own blocks with
+  // a running maximum and sum, merged across waves at the end.
   const bool one_block = nkeys <= 64;
+  if (one_block) {
+    const int kk = lane >> 3, d16 = lane & 7, t = 8 * w + kk;
+    const bool valid = t < nkeys;
+    const int tt = valid ? t : p;
+    uint4 kr[2];
+    if (tt < pos0) {
+      kr[0] = *reinterpret_cast<const uint4*>(A.kcache + cbase + (size_t)tt * kD + 16 * d16);
+      kr[1] = *reinterpret_cast<const uint4*>(A.kcache + cbase + (size_t)tt * kD + 16 * d16 + 8);
+    } else {
+      kr[0] = *reinterpret_cast<const uint4*>(&S.kl[tt - pos0][16 * d16]);
+      kr[1] = *reinterpret_cast<const uint4*>(&S.kl[tt - pos0][16 * d16 + 8]);
+    }
+#pragma unroll
+    for (int h = 0; h < kQpg; ++h) {
+      float sc = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float4 qa = *reinterpret_cast<const float4*>(&S.qs[s][h][16 * d16 + 8 * c]);
+        const float4 qb = *reinterpret_cast<const float4*>(&S.qs[s][h][16 * d16 + 8 * c + 4]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const uint32_t wd[4] = {kr[c].x, kr[c].y, kr[c].z, kr[c].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc = fmaf(qv[2 * e], bf16lo(wd[e]), sc);
+          sc = fmaf(qv[2 * e + 1], bf16hi(wd[e]), sc);
+        }
+      }
+      sc = group_sum<8>(sc);
+      if (d16 == 7) S.sl[h][t] = valid ? sc : -INFINITY;
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int h = 0; h < kQpg; ++h) {
+        const bool vl = lane < nkeys;
+        const float sv = vl ? S.sl[h][lane] : -INFINITY;
+        const float mx = wave_max(sv);
+        const float pr = vl ? __expf(sv - mx) : 0.f;
+        S.pw[0][h][lane] = pr / wave_sum(pr);
+      }
+    }
+    __syncthreads();
+    float acc[kQpg][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    if (8 * w < nkeys) {
+      uint32_t vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int row = min(8 * w + u, nkeys - 1);
+        vv[u] = row < pos0 ? *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)row * kD + 2 * lane)
+                           : *reinterpret_cast<const uint32_t*>(&S.vl[row - pos0][2 * lane]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int h = 0; h < kQpg; ++h) {
+          const float pu = 8 * w + u < nkeys ? S.pw[0][h][8 * w + u] : 0.f;
+          acc[h][0] = fmaf(pu, bf16lo(vv[u]), acc[h][0]);
+          acc[h][1] = fmaf(pu, bf16hi(vv[u]), acc[h][1]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < kQpg; ++h) {
+      S.aw[w][h][2 * lane] = acc[h][0];
+      S.aw[w][h][2 * lane + 1] = acc[h][1];
+    }
+    __syncthreads();
+    if (w < kQpg) {
+      const int h = w;
+      float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        o0 += S.aw[v][h][2 * lane];
+        o1 += S.aw[v][h][2 * lane + 1];
+      }
+      store_att<NPP>(at, plain, n, h, lane, o0, o1);
+    }
+    __syncthreads();
+    return;
+  }
   float M[kQpg], Ls[kQpg], acc[kQpg][2];
 #pragma unroll
   for (int h = 0; h < kQpg; ++h) { M[h] = -INFINITY; Ls[h] = 0.f; acc[h][0] = acc[h][1] = 0.f; }
@@ -394,16 +482,6 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
     const int tt = valid ? t : p;
     float sc[kQpg];
     score_row(A, S, s, cbase, tt, pos0, sc);
-    if (one_block) {
-#pragma unroll
-      for (int h = 0; h < kQpg; ++h) {
-        const float sv = valid ? sc[h] : -INFINITY;
-        const float mx = wave_max(sv);
-        const float pr = valid ? __expf(sv - mx) : 0.f;
-        S.pw[0][h][lane] = pr / wave_sum(pr);
-      }
-      break;
-    }
 #pragma unroll
     for (int h = 0; h < kQpg; ++h) {
       const float sv = valid ? sc[h] : -INFINITY;
@@ -438,37 +516,6 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
     }
     __builtin_amdgcn_wave_barrier();
   }
-  if (one_block) {
-    __syncthreads();
-    const int r0 = 8 * w, r1 = min(r0 + 8, nkeys);
-    for (int row = r0; row < r1; ++row) {
-      const uint32_t vv = row < pos0 ? *reinterpret_cast<const uint32_t*>(A.vcache + cbase + (size_t)row * kD + 2 * lane)
-                                     : *reinterpret_cast<const uint32_t*>(&S.vl[row - pos0][2 * lane]);
-#pragma unroll
-      for (int h = 0; h < kQpg; ++h) {
-        acc[h][0] = fmaf(S.pw[0][h][row], bf16lo(vv), acc[h][0]);
-        acc[h][1] = fmaf(S.pw[0][h][row], bf16hi(vv), acc[h][1]);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < kQpg; ++h) {
-      S.aw[w][h][2 * lane] = acc[h][0];
-      S.aw[w][h][2 * lane + 1] = acc[h][1];
-    }
-    __syncthreads();
-    if (w < kQpg) {
-      const int h = w;
-      float o0 = 0.f, o1 = 0.f;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        o0 += S.aw[v][h][2 * lane];
-        o1 += S.aw[v][h][2 * lane + 1];
-      }
-      store_att<NPP>(at, plain, n, h, lane, o0, o1);
-    }
-    __syncthreads();
-    return;
-  }
 #pragma unroll
   for (int h = 0; h < kQpg; ++h) {
     if (lane == 0) { S.mw[w][h] = M[h]; S.lw[w][h] = Ls[h]; }
@@ -497,6 +544,49 @@ __device__ void attend(const PpK& k, AttLds& S, int l, int g, int n, int s, cons
     store_att<NPP>(at, plain, n, h, lane, o0 * inv, o1 * inv);
   }
   __syncthreads();  // the LDS partials are reused by the workgroup's next position
+}
+
+// The weight tiles of each product for wave w, from layer l's tiles.  (The layer pointer
+// goes through opaque() so that the compiler keeps each load where it is written.)
+__device__ __forceinline__ const uint16_t* layer_tiles(const PpK& k, int l, size_t off) {
+  return opaque(reinterpret_cast<const uint16_t*>(k.layers + (size_t)l * k.lay.stride + off));
+}
+// q/k/v: rows 16j .. 16j + 15 of group x, columns 128w .. 128w + 127 in two steps.
+__device__ __forceinline__ void ld_q(const PpK& k, int l, int x, int j, int w, int lane, bf16x8 (&a)[2][2]) {
+  const uint16_t* wq = layer_tiles(k, l, k.lay.qkv);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) load_a(wq, (size_t)x * kQRows + 16 * j + (lane & 15), kH, 128 * w + 64 * s, lane, a[s]);
+}
+// O (waves 0..3): rows 32j .. 32j + 31 of KV block x as two row tiles, columns 64w .. +63:
+// each operand step is read by one wave only.
+__device__ __forceinline__ void ld_o(const PpK& k, int l, int x, int j, int w, int lane, bf16x8 (&a)[2][2]) {
+  const uint16_t* wo = layer_tiles(k, l, k.lay.o) + (size_t)x * kH * (kQpg * kD);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) load_a(wo, (size_t)(kCw * j + 16 * rt + (lane & 15)), kQpg * kD, 64 * w, lane, a[rt]);
+}
+// gate/up: rows 24j .. 24j + 23 of slice x (two row tiles, the second half empty),
+// columns 128w .. 128w + 127 in two steps.
+__device__ __forceinline__ void ld_g(const PpK& k, int l, int x, int j, int w, int lane, bf16x8 (&a)[2][2][2]) {
+  const uint16_t* wg = layer_tiles(k, l, k.lay.gu);
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int rl = 16 * rt + (lane & 15);
+      if (rl < 2 * kHalf) {
+        load_a(wg, (size_t)x * 2 * kIx + 2 * kHalf * j + rl, kH, 128 * w + 64 * s, lane, a[rt][s]);
+      } else {
+        a[rt][s][0] = as_bf8(u4{0u, 0u, 0u, 0u});
+        a[rt][s][1] = as_bf8(u4{0u, 0u, 0u, 0u});
+      }
+    }
+}
+// down (waves 0..5): rows 32j .. 32j + 31 of slice x as two row tiles, columns 64w .. +63
+// of the slice's 384: each operand step is read by one wave only.
+__device__ __forceinline__ void ld_d(const PpK& k, int l, int x, int j, int w, int lane, bf16x8 (&a)[2][2]) {
+  const uint16_t* wd = layer_tiles(k, l, k.lay.down) + (size_t)x * kH * kIx;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) load_a(wd, (size_t)(kCw * j + 16 * rt + (lane & 15)), kIx, 64 * w, lane, a[rt]);
 }
 
 template <int NT>
@@ -613,10 +703,18 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xres[n][8 * c8 + e] = v[e];
     }
+    float g8[8];
+    load_gains(A.in_norm0, j, threadIdx.x, g8);
     __syncthreads();
-    publish_residual<NPP>(xres, A.in_norm0, j, xb, ss, plain, (int)threadIdx.x);
+    publish_residual<NPP>(xres, g8, j, xb, ss, plain, (int)threadIdx.x);
     wg_publish(k, KR2, pp_tag(k.tag0, -1, KR2), plain, -1);
   }
+  // The products' weight tiles, loaded by every wave right before the phase's wait, so
+  // that they arrive while it waits.  Two other placements were slower: loading them a
+  // phase earlier put them ahead of the operand loads of the phase in between, in the
+  // same in-order memory queue; and letting wave 0, which polls the flags, load its share
+  // only after the poll exposed the whole load latency to its product.
+  bf16x8 aQ[2][2], aO[2][2], aG[2][2][2], aD[2][2];
 
 #pragma nounroll
   for (int l = 0; l < L; ++l) {
@@ -625,28 +723,31 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     // phases' offsets would stay live (in registers) at once.
     const int tid = opaque((int)threadIdx.x), lane = tid & 63, li = lane & 15;
     const uint8_t* base = k.layers + (size_t)l * k.lay.stride;
-    const uint16_t* wq = reinterpret_cast<const uint16_t*>(base + k.lay.qkv);
-    const uint16_t* wo = reinterpret_cast<const uint16_t*>(base + k.lay.o);
-    const uint16_t* wgu = reinterpret_cast<const uint16_t*>(base + k.lay.gu);
-    const uint16_t* wdn = reinterpret_cast<const uint16_t*>(base + k.lay.down);
     const float* G = reinterpret_cast<const float*>(base + k.lay.gains);
 
     // ------------------------------------------------------------ q/k/v product
     {
-      bf16x8 a[2][2];  // wave w: columns 128w .. 128w + 127 in two steps
-      const uint16_t* wqp = opaque(wq);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) load_a(wqp, (size_t)x * kQRows + 16 * j + li, kH, 128 * w + 64 * s, lane, a[s]);
+      ld_q(k, l, x, j, w, lane, aQ);
       if (!wg_wait(k, tid, KR2, x, kXcds, kPerXcd, pp_tag(k.tag0, l - 1, KR2), &stop, l - 1)) return;
-      rms_of<NPP>(ss, A.eps, rs, tid);
       f4 acc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NT <= 2) {  // both steps' operands in flight before the norm's loads (wave 0)
+        bf16x8 bh[2][NT][2], bl[2][NT][2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 bh[NT][2], bl[NT][2];
-        load_b<NT>(xb, kH, 16 * w + 8 * s, lane, bh, bl);
-        mfma_step<NT>(a[s], bh, bl, acc);
+        for (int s = 0; s < 2; ++s) load_b<NT>(xb, kH, 16 * w + 8 * s, lane, bh[s], bl[s]);
+        rms_of<NPP>(ss, A.eps, rs, tid);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) mfma_step<NT>(aQ[s], bh[s], bl[s], acc);
+      } else {  // one step's operands in registers at a time
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 bh[NT][2], bl[NT][2];
+          load_b<NT>(xb, kH, 16 * w + 8 * s, lane, bh, bl);
+          if (s == 0) rms_of<NPP>(ss, A.eps, rs, tid);
+          mfma_step<NT>(aQ[s], bh, bl, acc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) red[(w * NT + nt) * 64 + lane] = acc[nt];
@@ -686,20 +787,9 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
         // load issued before the first row's arithmetic), and waves 0..3 also query head
         // h = w & 1 of slot w >> 1: RMSNorm, rotary from the launch's table, bf16 rounding
         // of keys and values as the cache holds them.
-        constexpr int RPW = NPP / 8;  // rows per wave at most
+        constexpr int RPW = NPP / 8;          // rows per wave at most
+        constexpr int RB = RPW < 4 ? RPW : 4;  // rows per batch of loads
         const float* kn = G + kH + kD;
-        float kv[RPW][4];
-#pragma unroll
-        for (int u = 0; u < RPW; ++u) {
-          const int n = w + 8 * u;
-          const uint32_t o = (uint32_t)((n * kQRows + 2 * kD + lane) * 4);
-          if (n <= nmax) {
-            kv[u][0] = __uint_as_float(qr.ld4(o));
-            kv[u][1] = __uint_as_float(qr.ld4(o + 64 * 4));
-            kv[u][2] = __uint_as_float(qr.ld4(o + kD * 4));
-            kv[u][3] = __uint_as_float(qr.ld4(o + (kD + 64) * 4));
-          }
-        }
         const int qs_slot = w >> 1, qh = w & 1, qn_pos = qs_slot ? nb2 : na;
         const bool has_q = w < 4 && (qs_slot ? vb : va);
         float q0 = 0.f, q1 = 0.f;
@@ -708,8 +798,22 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
           q1 = __uint_as_float(qr.ld4((uint32_t)((qn_pos * kQRows + qh * kD + lane + 64) * 4)));
         }
 #pragma unroll
-        for (int u = 0; u < RPW; ++u) {
-          const int n = w + 8 * u;
+        for (int b0 = 0; b0 < RPW; b0 += RB) {
+        float kv[RB][4];
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int n = w + 8 * (b0 + u);
+          const uint32_t o = (uint32_t)((n * kQRows + 2 * kD + lane) * 4);
+          if (n <= nmax) {
+            kv[u][0] = __uint_as_float(qr.ld4(o));
+            kv[u][1] = __uint_as_float(qr.ld4(o + 64 * 4));
+            kv[u][2] = __uint_as_float(qr.ld4(o + kD * 4));
+            kv[u][3] = __uint_as_float(qr.ld4(o + (kD + 64) * 4));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < RB; ++u) {
+          const int n = w + 8 * (b0 + u);
           if (n <= nmax) {
             float k0 = kv[u][0], k1 = kv[u][1];
             norm_rotate(kn, A.eps, rc[n][lane], rsn[n][lane], lane, k0, k1);
@@ -727,6 +831,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
             }
           }
         }
+        }
         if (has_q) {
           norm_rotate(G + kH, A.eps, rc[qn_pos][lane], rsn[qn_pos][lane], lane, q0, q1);
           const float qscale = rsqrtf((float)kD);
@@ -742,25 +847,32 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
 
     // ------------------------------------------------------------ O product (partial of KV block x)
     {
-      const int rt = w & 1, s = w >> 1;
-      bf16x8 a[2];
-      load_a(opaque(wo) + (size_t)x * kH * (kQpg * kD), (size_t)(kCw * j + 16 * rt + li), kQpg * kD, 64 * s, lane, a);
+      constexpr int kSteps = kQpg * kD / 64;  // 4: waves 0..3, one operand step each
+      const bool act = w < kSteps;
+      if (act) ld_o(k, l, x, j, w, lane, aO);
       if (!wg_wait(k, tid, KA, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KA), &stop, l)) return;
-      f4 acc[NT];
+      if (act) {
+        f4 acc[2][NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 bh[NT][2], bl[NT][2];
-      load_b<NT>(at, kQpg * kD, 8 * s, lane, bh, bl);
-      mfma_step<NT>(a, bh, bl, acc);
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) red[(w * NT + nt) * 64 + lane] = acc[nt];
+          for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 bh[NT][2], bl[NT][2];
+        load_b<NT>(at, kQpg * kD, 8 * w, lane, bh, bl);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) mfma_step<NT>(aO[rt], bh, bl, acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) red[((w * 2 + rt) * NT + nt) * 64 + lane] = acc[rt][nt];
+      }
       __syncthreads();
       const int t = tid;
       if (t < 2 * NT * 64) {
         const int rr = t / (NT * 64), nt = (t >> 6) % NT, ln = t & 63;
-        f4 o = red[(rr * NT + nt) * 64 + ln];
+        f4 o = red[((0 * 2 + rr) * NT + nt) * 64 + ln];
 #pragma unroll
-        for (int v = 1; v < 4; ++v) o += red[((rr + 2 * v) * NT + nt) * 64 + ln];
+        for (int v = 1; v < kSteps; ++v) o += red[((v * 2 + rr) * NT + nt) * 64 + ln];
         const int n = 16 * nt + (ln & 15), r0 = 16 * rr + 4 * (ln >> 4);
         const u4 val = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
         op.st16((uint32_t)((((x * kPerXcd + j) * NPP + n) * kCw + r0) * 4), val, false);
@@ -771,41 +883,42 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     // ------------------------------------------------------------ residual after attention
     {
       if (!wg_wait(k, tid, KO, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KO), &stop, l)) return;
+      float g8[8];
+      load_gains(G, j, tid, g8);  // in flight with the partials' loads
       add_partials<NPP>(xres, op, j, tid);
       __syncthreads();
-      publish_residual<NPP>(xres, G, j, xp, ss2, plain, tid);
+      publish_residual<NPP>(xres, g8, j, xp, ss2, plain, tid);
       wg_publish(k, KR1, pp_tag(k.tag0, l, KR1), plain, l);
     }
 
     // ------------------------------------------------------------ gate/up product and SwiGLU
     {
-      bf16x8 a[2][2][2];  // [row tile][step]: rows 24j .. 24j + 23 of slice x, columns 128w ..
-      const uint16_t* wgup = opaque(wgu);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int rl = 16 * rt + li;
-          if (rl < 2 * kHalf) {
-            load_a(wgup, (size_t)x * 2 * kIx + 2 * kHalf * j + rl, kH, 128 * w + 64 * s, lane, a[rt][s]);
-          } else {
-            a[rt][s][0] = as_bf8(u4{0u, 0u, 0u, 0u});
-            a[rt][s][1] = as_bf8(u4{0u, 0u, 0u, 0u});
-          }
-        }
+      ld_g(k, l, x, j, w, lane, aG);
       if (!wg_wait(k, tid, KR1, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KR1), &stop, l)) return;
-      rms_of<NPP>(ss2, A.eps, rs, tid);
       f4 acc[2][NT];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (NT <= 2) {  // both steps' operands in flight before the norm's loads
+        bf16x8 bh[2][NT][2], bl[2][NT][2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 bh[NT][2], bl[NT][2];
-        load_b<NT>(xp, kH, 16 * w + 8 * s, lane, bh, bl);
+        for (int s = 0; s < 2; ++s) load_b<NT>(xp, kH, 16 * w + 8 * s, lane, bh[s], bl[s]);
+        rms_of<NPP>(ss2, A.eps, rs, tid);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) mfma_step<NT>(a[rt][s], bh, bl, acc[rt]);
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) mfma_step<NT>(aG[rt][s], bh[s], bl[s], acc[rt]);
+      } else {  // one step's operands in registers at a time
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bf16x8 bh[NT][2], bl[NT][2];
+          load_b<NT>(xp, kH, 16 * w + 8 * s, lane, bh, bl);
+          if (s == 0) rms_of<NPP>(ss2, A.eps, rs, tid);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) mfma_step<NT>(aG[rt][s], bh, bl, acc[rt]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -841,36 +954,32 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
 
     // ------------------------------------------------------------ down product (partial of slice x)
     {
-      constexpr int kSteps = kIx / 64;  // 6
-      const int rt = w & 1, sg = w >> 1;
-      const bool two = sg + 4 < kSteps;
-      bf16x8 a[2][2];
-      const uint16_t* wblk = opaque(wdn) + (size_t)x * kH * kIx;
-      load_a(wblk, (size_t)(kCw * j + 16 * rt + li), kIx, 64 * sg, lane, a[0]);
-      if (two) load_a(wblk, (size_t)(kCw * j + 16 * rt + li), kIx, 64 * (sg + 4), lane, a[1]);
+      constexpr int kSteps = kIx / 64;  // 6: waves 0..5, one operand step each
+      const bool act = w < kSteps;
+      if (act) ld_d(k, l, x, j, w, lane, aD);
       if (!wg_wait(k, tid, KG, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KG), &stop, l)) return;
-      f4 acc[NT];
+      if (act) {
+        f4 acc[2][NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
-      {
-        bf16x8 bh[NT][2], bl[NT][2];
-        load_b<NT>(hs, kIx, 8 * sg, lane, bh, bl);
-        mfma_step<NT>(a[0], bh, bl, acc);
-      }
-      if (two) {
-        bf16x8 bh[NT][2], bl[NT][2];
-        load_b<NT>(hs, kIx, 8 * (sg + 4), lane, bh, bl);
-        mfma_step<NT>(a[1], bh, bl, acc);
-      }
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) red[(w * NT + nt) * 64 + lane] = acc[nt];
+          for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 bh[NT][2], bl[NT][2];
+        load_b<NT>(hs, kIx, 8 * w, lane, bh, bl);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) mfma_step<NT>(aD[rt], bh, bl, acc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) red[((w * 2 + rt) * NT + nt) * 64 + lane] = acc[rt][nt];
+      }
       __syncthreads();
       const int t = tid;
       if (t < 2 * NT * 64) {
         const int rr = t / (NT * 64), nt = (t >> 6) % NT, ln = t & 63;
-        f4 o = red[(rr * NT + nt) * 64 + ln];
+        f4 o = red[((0 * 2 + rr) * NT + nt) * 64 + ln];
 #pragma unroll
-        for (int v = 1; v < 4; ++v) o += red[((rr + 2 * v) * NT + nt) * 64 + ln];
+        for (int v = 1; v < kSteps; ++v) o += red[((v * 2 + rr) * NT + nt) * 64 + ln];
         const int n = 16 * nt + (ln & 15), r0 = 16 * rr + 4 * (ln >> 4);
         const u4 val = {__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
         dp.st16((uint32_t)((((x * kPerXcd + j) * NPP + n) * kCw + r0) * 4), val, false);
@@ -881,6 +990,8 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     // ------------------------------------------------------------ residual after the MLP
     {
       if (!wg_wait(k, tid, KD, kXcds * j, 1, kXcds, pp_tag(k.tag0, l, KD), &stop, l)) return;
+      float g8[8];
+      load_gains(G + kH + 2 * kD, j, tid, g8);  // in flight with the partials' loads
       add_partials<NPP>(xres, dp, j, tid);
       __syncthreads();
       const int t = tid;
@@ -896,7 +1007,7 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
         }
       }
       if (l + 1 < L) {
-        publish_residual<NPP>(xres, G + kH + 2 * kD, j, xb, ss, plain, tid);
+        publish_residual<NPP>(xres, g8, j, xb, ss, plain, tid);
         wg_publish(k, KR2, pp_tag(k.tag0, l, KR2), plain, l);
       }
     }
