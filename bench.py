@@ -17,6 +17,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -188,15 +189,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # The decode kernel's sources: its code and the parameter block the host fills in.
 DECODE_SOURCES = ("mk_internal.h", "mk_device.h", "mk_body.h", "mk_kernel.hip")
+# The batched prefill's kernels (both forms).
+PREFILL_SOURCES = ("mk_internal.h", "mk_device.h", "mk_prefill.h", "mk_prefill.hip", "mk_pprefill.hip")
 
 
-def csrc_digest() -> str:
-    """sha256 over the code of the decode kernel's sources (line comments and blank lines
+def csrc_digest(sources=DECODE_SOURCES) -> str:
+    """sha256 over the code of the given kernel sources (line comments and blank lines
     dropped): names the kernel build HBM counters were taken on."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for n in DECODE_SOURCES:
+    for n in sources:
         with open(os.path.join(CSRC, n)) as f:
             code = [re.sub(r"//.*", "", ln).rstrip() for ln in f]
         h.update(n.encode() + b"\0" + "\n".join(ln for ln in code if ln).encode())
@@ -289,6 +292,65 @@ def hbm_summary(outdir: str, workload: str, steps: int, copy_mib: int, copy_dir:
     return "\n".join(lines) + "\n"
 
 
+PREFILL_PATHS = {"auto": 0, "chain": 1, "persistent": 2}
+
+
+def prefill_summary(outdir: str, workload: str, calls: int, path: str, copy_mib: int, copy_dir: str = "") -> str:
+    """Summary text of the counter passes of `calls` batched prompt calls (--prefill-only)
+    under outdir: FETCH_SIZE and WRITE_SIZE per kernel, summed over the calls' dispatches
+    and divided by the call count, each scaled by known/measured of the plain copy."""
+    import csv
+    copy_dir = copy_dir or outdir
+    copy_kib = copy_mib * 1024
+    f_cp, _ = _pmc_mean(os.path.join(copy_dir, "pmccopy_FETCH_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    w_cp, _ = _pmc_mean(os.path.join(copy_dir, "pmccopy_WRITE_SIZE", "p_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+    fs, ws = copy_kib / f_cp, copy_kib / w_cp
+    per = {}
+    order = []
+    for counter, scale, col in (("FETCH_SIZE", fs, 0), ("WRITE_SIZE", ws, 1)):
+        for r in csv.DictReader(open(os.path.join(outdir, f"pfpmc_{counter}", "p_counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            if not (name.startswith("mk::") or name.startswith("void mk::")) or "widen_kernel" in name \
+                    or "embed_sum" in name or "pp_clear" in name:
+                continue
+            short = re.sub(r"^void ", "", name)
+            short = re.sub(r"mk::\(anonymous namespace\)::|mk::", "", short)
+            short = re.sub(r"\(.*$", "", short)
+            if short not in per:
+                per[short] = [0.0, 0.0]
+                order.append(short)
+            per[short][col] += float(r["Counter_Value"]) * scale * 1024 / calls
+    shape = wl.BY_NAME[workload]
+    algo = weight_bytes_per_step(shape)
+    base = f"--prefill-only {calls}" + ("" if path == "auto" else f" --prefill-path {path}") + (
+        "" if workload == "talker-0.6b" else f" --workload {workload}")
+    lines = [
+        f"# HBM counters of the batched prompt prefill on {workload}: one {shape.prompt_len}-position prompt call ({path} form)",
+        "# commands (repository root, TMPDIR=/tmp), one counter per pass:",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {outdir}/pfpmc_FETCH_SIZE -o p --output-format csv -- python3 bench.py {base}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {outdir}/pfpmc_WRITE_SIZE -o p --output-format csv -- python3 bench.py {base}",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {copy_dir}/pmccopy_FETCH_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {copy_dir}/pmccopy_WRITE_SIZE -o p --output-format csv -- python3 bench.py --copy-calibration {copy_mib}",
+        f"# summarised by: python3 bench.py --prefill-summary {outdir} --prefill-only {calls}"
+        + ("" if path == "auto" else f" --prefill-path {path}") + ("" if workload == "talker-0.6b" else f" --workload {workload}")
+        + ("" if copy_dir == outdir else f" --copy-dir {copy_dir}"),
+        f"fetch_scale: {fs:.4f}",
+        f"write_scale: {ws:.4f}",
+        f"csrc_sha256: {csrc_digest(PREFILL_SOURCES)} (the prefill kernels' sources)",
+        "kernel | fetch MB per call | write MB per call",
+    ]
+    tf = tw = 0.0
+    for k in order:
+        f, w = per[k]
+        tf += f
+        tw += w
+        lines.append(f"{k} | {f / 1e6:.1f} | {w / 1e6:.1f}")
+    lines += [f"total | {tf / 1e6:.1f} | {tw / 1e6:.1f}",
+              f"algorithmic_bytes_per_call: {algo} (one pass over the layer weights and the LM head; the cache rows are under 1 MB)",
+              f"traffic_over_algorithmic: {(tf + tw) / algo:.2f}"]
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,7 +370,15 @@ def main():
                     help="with --hbm-summary: where the copy-calibration passes are (default: DIR)")
     ap.add_argument("--prefill-only", type=int, default=0, metavar="N",
                     help="only run the workload's prompt N times through the batched prefill (for profiling) and exit")
+    ap.add_argument("--prefill-path", choices=sorted(PREFILL_PATHS), default="auto",
+                    help="form of the batched prefill (mk_set_prefill_path) in every run of it")
+    ap.add_argument("--prefill-summary", metavar="DIR",
+                    help="only print the HBM counter summary of the --prefill-only passes under DIR")
     args = ap.parse_args()
+    if args.prefill_summary:
+        sys.stdout.write(prefill_summary(args.prefill_summary, args.workload, args.prefill_only or 5, args.prefill_path,
+                                         1024, args.copy_dir))
+        return
     if args.hbm_summary:
         sys.stdout.write(hbm_summary(args.hbm_summary, args.workload, args.steps, 1024, args.copy_dir, args.warmup))
         return
@@ -336,6 +406,7 @@ def main():
     weights = wl.make_weights(shape)
     dw = weights_to_device(weights)
     dec = Decoder(shape, dw)
+    dec.set_prefill_path(PREFILL_PATHS[args.prefill_path])
     del dw
     torch.cuda.empty_cache()
     inp = gpu_inputs(shape, P, K, torch)
