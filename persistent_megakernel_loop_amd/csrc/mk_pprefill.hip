@@ -605,7 +605,6 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
 
   const PfArgs& A = k.A;
   const int b = blockIdx.x, x = b % kXcds, j = b / kXcds;
-  const int w = threadIdx.x >> 6;
   const int m = A.m, L = A.L;
 
   // Region views of this XCD's replicas (sized for this chunk's NPP).
@@ -718,10 +717,11 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
 
 #pragma nounroll
   for (int l = 0; l < L; ++l) {
-    // The thread index, made opaque once per layer: every lane-dependent offset is
-    // computed inside the layer instead of being hoisted out of the loop, where all
-    // phases' offsets would stay live (in registers) at once.
+    // The thread index, made opaque once per layer: every lane- and wave-dependent offset
+    // (and row test) is computed inside the layer instead of being hoisted out of the loop,
+    // where all phases' offsets would stay live (in registers) at once.
     const int tid = opaque((int)threadIdx.x), lane = tid & 63, li = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint8_t* base = k.layers + (size_t)l * k.lay.stride;
     const float* G = reinterpret_cast<const float*>(base + k.lay.gains);
 
@@ -956,8 +956,9 @@ __global__ __launch_bounds__(kPpThreads) void pp_kernel(PpK k) {
     {
       constexpr int kSteps = kIx / 64;  // 6: waves 0..5, one operand step each
       const bool act = w < kSteps;
-      if (act) ld_d(k, l, x, j, w, lane, aD);
+      if (NT < 4 && act) ld_d(k, l, x, j, w, lane, aD);
       if (!wg_wait(k, tid, KG, x, kXcds, kPerXcd, pp_tag(k.tag0, l, KG), &stop, l)) return;
+      if (NT >= 4 && act) ld_d(k, l, x, j, w, lane, aD);
       if (act) {
         f4 acc[2][NT];
 #pragma unroll

@@ -1,7 +1,8 @@
-"""Resource use of the persistent kernel, from the compiler (no GPU needed): every decode
-and prompt kernel, of every body, runs with no scratch memory (no register spilled to
-memory: a reload would wait for every load the wave has in flight, weight streams
-included) and within the 256 registers a wave may hold at two waves per SIMD."""
+"""Resource use of the persistent kernels, from the compiler (no GPU needed): every decode
+and prompt kernel, of every body, and every tile count of the persistent prompt prefill,
+runs with no scratch memory (no register spilled to memory: a reload would wait for
+every load the wave has in flight, weight streams included) and within the 256
+registers a wave may hold at two waves per SIMD."""
 import os
 import re
 import shutil
@@ -20,15 +21,14 @@ def _hipcc():
     return None
 
 
-@pytest.fixture(scope="module")
-def usage(tmp_path_factory):
+def _usage(tmp_path_factory, source):
     hipcc = _hipcc()
     if hipcc is None:
         pytest.skip("hipcc is not installed")
     out = tmp_path_factory.mktemp("res") / "k.o"
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
            "-packed-fp32-ops", "--offload-device-only", "-c", "-Rpass-analysis=kernel-resource-usage",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, "mk_kernel.hip"), "-o", str(out)]
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC, os.path.join(CSRC, source), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     funcs, cur = {}, None
@@ -41,6 +41,26 @@ def usage(tmp_path_factory):
         if m and cur is not None:
             cur[m.group(1).strip()] = int(m.group(2))
     return funcs
+
+
+@pytest.fixture(scope="module")
+def usage(tmp_path_factory):
+    return _usage(tmp_path_factory, "mk_kernel.hip")
+
+
+@pytest.fixture(scope="module")
+def prefill_usage(tmp_path_factory):
+    return _usage(tmp_path_factory, "mk_pprefill.hip")
+
+
+def test_persistent_prefill_kernels_have_no_scratch(prefill_usage):
+    """The persistent prompt prefill, at each of its tile counts (16 to 64 positions)."""
+    kernels = {n: u for n, u in prefill_usage.items() if "pp_kernel" in n}
+    assert len(kernels) == 4, sorted(kernels)
+    for name, u in kernels.items():
+        assert u.get("ScratchSize") == 0, (name, u)
+        assert u.get("VGPRs Spill") == 0, (name, u)
+        assert u.get("VGPRs", 999) <= 256, (name, u)
 
 
 def test_persistent_kernels_have_no_scratch(usage):
