@@ -355,16 +355,20 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       if (grp && r == kPerXcd - 1 && wave == kWorkerWaves - 1) write_kv_entry<B>(P, S, x, l, p, lane);
       // gate/up part 0 (slot A is free): issued after the q/k/v gather rather than ahead of
       // it, where it held back that gather's polls in this CU's memory queue (measured: 1 %
-      // per step); the copy waves' attention shares end by waiting for it
-      dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);
+      // per step).  In the chunked form the copy waves' attention shares end by waiting for
+      // it.  In the whole form it goes after the attention: the compiler cannot count the
+      // copies, so the first use of the prefetched cache rows waits for every load issued
+      // before it, and a copy issued just ahead would hold the attention back.
+      if constexpr (!WHOLE) dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);
       // attention over the chunk (its cache rows were loaded at the start of the layer)
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
+      if constexpr (WHOLE) dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);
       mark(1);
       wsync();
       if constexpr (WHOLE) {
         // the whole attention in this workgroup: the control wave merges the waves' partials
         // into chunk 0 (no exchange), then every wave takes its share of the output
-        if (wave < kDmaWaves) wait_vmem<0>();  // the O tile and gate/up part 0 have landed
+        if (wave < kDmaWaves) wait_vmem_rt(dma_part_count(NI_GU, 4, 0, wave));  // the O tile has landed
         mark(0);
         __syncthreads();
         dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 1, wave, lane);
