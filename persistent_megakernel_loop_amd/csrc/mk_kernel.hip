@@ -373,8 +373,6 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
         // into chunk 0 (no exchange), then every wave takes its share of the output
         if (wave < kDmaWaves) wait_vmem_rt(dma_count(NI_GU, wave));  // the O tile has landed
         mark(0);
-        __syncthreads();
-        if (grp) combine_part<B>(S, 1, wave, lane);
       } else
       // the attention chunks, polled by every wave: no copy in flight (the O tile and gate/up
       // part 0 have landed), then the copy waves issue gate/up parts 1 and 2
@@ -698,7 +696,10 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
       // ------------------------------------------------------------ attention combine
       if (!sync()) return;
       if constexpr (WHOLE) {
-        // every rank ran the whole attention: its waves' partials merged are the result
+        // every rank ran the whole attention: its waves' partials merged are the result.
+        // This wave also finishes it, with no second barrier: the combine of one chunk
+        // (weight exactly 1, sum exactly its L) in the same operations, so the output
+        // equals the chunked form's bit for bit, then the split for the O GEMV.
         float cM[B::QPG], cL[B::QPG], ca[B::QPG][B::DPL];
 #pragma unroll
         for (int h = 0; h < B::QPG; ++h) {
@@ -706,18 +707,18 @@ __device__ __forceinline__ void control_loop(const Params& P, Lds<B>& S, const u
 #pragma unroll
           for (int k = 0; k < B::DPL; ++k) ca[h][k] = 0.f;
         }
-        if (grp) merge_wave_partials<B>(S, lane, cM, cL, ca);
+        if (grp) {
+          merge_wave_partials<B>(S, lane, cM, cL, ca);
 #pragma unroll
-        for (int h = 0; h < B::QPG; ++h) {
+          for (int h = 0; h < B::QPG; ++h) {
+            const float inv = __builtin_amdgcn_rcpf(cL[h]);
 #pragma unroll
-          for (int k = 0; k < B::DPL; ++k) S.part[0][h][2 + lane + 64 * k] = ca[h][k];
-          if (lane == 0) {
-            S.part[0][h][0] = cM[h];
-            S.part[0][h][1] = cL[h];
+            for (int k = 0; k < B::DPL; ++k) S.ov[h * B::D + lane + 64 * k] = fmaf(ca[h][k], 1.f, 0.f) * inv;
           }
+          // (this wave's own LDS writes are seen by its later reads)
+          static_assert(B::OC / 8 <= 64, "a chunk per lane");
+          if (lane < B::OC / 8) split8(S.ov + 8 * lane, S.ov_hi[lane], S.ov_lo[lane]);
         }
-        __syncthreads();
-        if (grp) combine_part<B>(S, 1, kWorkerWaves, lane);
       } else {
         const int nc = n_chunks<B>(p);
         u64* xa = P.xatt + (size_t)x * kPerXcd * B::QPG * (B::D + 2);
