@@ -843,15 +843,30 @@ __device__ __forceinline__ void attention_chunk(const Params& P, Lds<B>& S, int 
     float kp_[DPL], vp_[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) { kp_[e] = S.kp[lane * DPL + e]; vp_[e] = S.vp[lane * DPL + e]; }
+    // bf16 bodies: the current position's k and v as the cache word they will be (the
+    // values are bf16 already, so packing is exact), chosen before widening: one select
+    // per word instead of one per element
+    uint32_t kpw = 0, vpw = 0;
+    if constexpr (B::BF16) {
+      kpw = pack_bf16(kp_[0], kp_[1]);
+      vpw = pack_bf16(vp_[0], vp_[1]);
+    }
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       float kf[DPL];
-      widen(kb.k[u], kf);
-      widen(kb.v[u], vf[u]);
+      if constexpr (B::BF16) {
+        // slots past the range may hold anything, NaN included: their values are zeroed;
+        // their keys need not be, as their scores are replaced by -inf below
+        widen(u == pu ? kpw : kb.k[u], kf);
+        widen(u == pu ? vpw : (u < nb ? kb.v[u] : 0u), vf[u]);
+      } else {
+        widen(kb.k[u], kf);
+        widen(kb.v[u], vf[u]);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {  // slots past the range may hold anything, NaN included: zeroed
-        kf[e] = u == pu ? kp_[e] : (u < nb ? kf[e] : 0.f);
-        vf[u][e] = u == pu ? vp_[e] : (u < nb ? vf[u][e] : 0.f);
+        for (int e = 0; e < DPL; ++e) {  // slots past the range may hold anything, NaN included: zeroed
+          kf[e] = u == pu ? kp_[e] : (u < nb ? kf[e] : 0.f);
+          vf[u][e] = u == pu ? vp_[e] : (u < nb ? vf[u][e] : 0.f);
+        }
       }
 #pragma unroll
       for (int h = 0; h < B::QPG; ++h) {
