@@ -328,7 +328,10 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const bool attn = grp && (WHOLE || r < nc);
       const int c0 = WHOLE ? 0 : r * csz, c1 = WHOLE ? p + 1 : min(p + 1, r * csz + csz);
       KvBatch<B> kb;
-      if (attn) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
+      // (waves 4..6 load theirs after their part of the q/k/v gather: a wave's loads complete
+      // in order, so rows issued here would hold back their first poll round; measured: C2
+      // 0.3785 -> 0.3752 ms/step at 20 steps, 0.4398 -> 0.4362 at 256)
+      if (attn && !poller) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // this layer's O tile, behind the cache rows (slot B has been free since the last
       // down GEMV; layer 0's tile was copied before the position)
       if (l > 0) dma_copy<TO::TOTAL>(A.o(l), slotB, wave, lane);
@@ -346,8 +349,17 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       }
       mark(1);
       wsync();
-      if (gather(grp, std::integral_constant<int, B::RQKV>{}, P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv,
-                 r * B::T_QKV, (r + 1) * B::T_QKV)) {
+      // the q/k/v gather (as gather(), with the pollers' cache rows issued after their part)
+      if (grp && poller) {
+        if (!help_gather<Kp<B::RQKV, kPollWaves>::value>(P.xq + (size_t)x * B::RQKV, B::RQKV, tg0 + 0, S.qkv, r * B::T_QKV,
+                                                        (r + 1) * B::T_QKV, part, lane, P) &&
+            lane == 0)
+          S.abort_ = 1;
+        vmem_drain();
+      }
+      if (attn && poller) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
+      __syncthreads();
+      if (grp && S.abort_ == 0) {
         if constexpr (B::BF16) qk_part<B>(S, S.G[gc & 1] + B::H, S.G[gc & 1] + B::H + B::D, P.rms_eps, P.kv_bf16, wave, lane);
       }
       wsync();  // q rotated, k/v of position p in LDS
