@@ -329,8 +329,9 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       const int c0 = WHOLE ? 0 : r * csz, c1 = WHOLE ? p + 1 : min(p + 1, r * csz + csz);
       KvBatch<B> kb;
       // (waves 4..6 load theirs after their part of the q/k/v gather: a wave's loads complete
-      // in order, so rows issued here would hold back their first poll round; measured: C2
-      // 0.3785 -> 0.3752 ms/step at 20 steps, 0.4398 -> 0.4362 at 256)
+      // in order, so rows issued here would hold back their first poll round; measured on the
+      // 28-layer hidden-1024 talker: 0.3785 -> 0.3752 ms/step over 20 steps, 0.4398 -> 0.4362
+      // over 256)
       if (attn && !poller) attention_prefetch<B>(P, x, l, c0, c1, wave, lane, kb);
       // this layer's O tile, behind the cache rows (slot B has been free since the last
       // down GEMV; layer 0's tile was copied before the position)
@@ -373,7 +374,7 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       // cache rows waits for every load issued before it; and no exchange runs between the
       // attention and the O partials, so the burst sits ahead of no poll, while its issue
       // overlaps the control wave's merge instead of delaying the combine and the O GEMV
-      // (measured: C2 0.3940 -> 0.3843 ms/step at 20 steps).
+      // (measured on the 28-layer hidden-1024 talker: 0.3940 -> 0.3843 ms/step over 20 steps).
       if constexpr (!WHOLE) dma_part<TGU::TOTAL, 4>(A.gu(l), slotA, 0, wave, lane);
       // attention over the chunk (its cache rows were loaded at the start of the layer)
       if (attn) attention_chunk<B, true>(P, S, x, l, p, c0, c1, wave, lane, kb);
@@ -421,8 +422,8 @@ __device__ __forceinline__ void worker_loop_lds(const Params& P, Lds<B>& S, u4* 
       // the down tile (slot B is free) and the next layer's gains (their buffer held those
       // of the layer before this one, last read by this layer's q/k/v GEMV), issued while
       // the copy waves wait out the residual's two exchanges rather than just before the
-      // gate/up GEMV, whose start their issue delayed (measured: C2 0.3972 -> 0.3938
-      // ms/step at 20 steps, 0.4399 -> 0.4385 at 256)
+      // gate/up GEMV, whose start their issue delayed (measured on the 28-layer hidden-1024
+      // talker: 0.3972 -> 0.3938 ms/step over 20 steps, 0.4399 -> 0.4385 over 256)
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 0, wave, lane);
       dma_part<TD::TOTAL, 2>(A.down(l), slotB, 1, wave, lane);
       dma_copy<GCH>(A.gains(ln), S.G[(gc + 1) & 1], wave, lane);
