@@ -105,23 +105,28 @@ def test_full_talker_0p6b():
 
 
 def test_full_text_0p6b():
-    """The Qwen3-0.6B-shaped text decoder (151936-row tied head): 16 prompt ids, one launch of
-    64 greedy steps; every layer at every position and every id (the full head each step),
-    and the oracle's own free run against the GPU's ids up to the first low-margin step."""
-    _, summary = _case(wl.TEXT_0P6B, n_steps=64, free_run=True)
-    assert summary["ids_checked"] == 64
+    """The Qwen3-0.6B-shaped text decoder (151936-row tied head) exactly as the benchmark
+    launches it: 16 prompt ids, one launch of 256 greedy steps; every layer at every position
+    and every id (the full head each step), and the oracle's own free run against the GPU's
+    ids up to the first low-margin step."""
+    _, summary = _case(wl.TEXT_0P6B, n_steps=256, free_run=True)
+    assert summary["ids_checked"] == 256
 
 
 def test_full_talker_long_context():
-    """The talker with 4096 pre-filled positions: one launch of 48 decode steps."""
-    _case(wl.TALKER_0P6B_LONG, n_steps=48)
+    """The talker with 4096 pre-filled positions exactly as the benchmark launches it: one
+    launch of 512 decode steps (positions 4096..4607, all 28 attention chunks), every step's
+    id and every layer's hidden state against the oracle."""
+    _, summary = _case(wl.TALKER_0P6B_LONG, n_steps=512)
+    assert summary["ids_checked"] == 512
 
 
 def test_full_talker_1p7b():
-    """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions: one launch of 64
-    steps, every step's id and every layer's hidden state against the oracle."""
-    _, summary = _case(wl.TALKER_1P7B, n_steps=64)
-    assert summary["ids_checked"] == 64
+    """The 1.7B-scale talker (hidden 2048) with 2048 pre-filled positions exactly as the
+    benchmark launches it: one launch of 512 steps, every step's id and every layer's hidden
+    state against the oracle."""
+    _, summary = _case(wl.TALKER_1P7B, n_steps=512)
+    assert summary["ids_checked"] == 512
 
 
 def _sweep_cases():
